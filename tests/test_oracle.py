@@ -1,0 +1,326 @@
+"""Pins for the CPU oracle (no GPU).
+
+Each test ties the oracle to something other than itself: hand-derived worked
+examples (tests/golden), a library routine that computes the same quantity
+(numpy.flatnonzero, torch's bf16 conversion, torch's fp64 SDPA), closed forms,
+invariants, and brute force written a different way (pure Python, math.fsum,
+no max subtraction).  Chosen so that a dropped term, a wrong sign or index, a
+transposed operand, a missing scale or a cross-image leak fails at least one.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from ragged_attention_token_amd import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _read_golden(name):
+    data = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            key, *vals = line.split()
+            data.setdefault(key, []).append(vals)
+    return data
+
+
+def _f32(a):
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+# ---------------------------------------------------------------- bf16 decode
+def test_bf16_decode_exhaustive_matches_torch():
+    bits = np.arange(65536, dtype=np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    got = np.array([oracle.bf16_to_f64(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert (np.isnan(got) == nan).all()
+    assert (got[~nan] == ref[~nan]).all()
+    # sign bit and exponent bias spot checks
+    assert oracle.bf16_to_f64(0x3F80) == 1.0
+    assert oracle.bf16_to_f64(0xBF80) == -1.0
+    assert oracle.bf16_to_f64(0x4040) == 3.0
+    assert oracle.bf16_to_f64(0x0001) == 2.0 ** -133
+
+
+# ---------------------------------------------------------------------- pack
+def test_pack_golden():
+    g = _read_golden("pack_worked_example.txt")
+    B, N = int(g["B"][0][0]), int(g["N"][0][0])
+    keep = np.array([[int(x) for x in row] for row in g["keep"]], dtype=np.uint8)
+    assert keep.shape == (B, N)
+    src = np.arange(B * N * 4, dtype=np.int32).reshape(B * N, 4)
+    packed, cu, gather = oracle.pack(keep, src)
+    assert cu.tolist() == [int(x) for x in g["cu_seqlens"][0]]
+    assert gather.tolist() == [int(x) for x in g["gather_idx"][0]]
+    assert (packed == src[gather]).all()
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("density", [0.0, 0.05, 0.5, 1.0])
+def test_pack_matches_flatnonzero(seed, density):
+    rng = np.random.default_rng(seed)
+    B, N = 7, 37
+    keep = (rng.random((B, N)) < density).astype(np.uint8) * rng.integers(1, 256, (B, N)).astype(np.uint8)
+    src = rng.integers(0, 2 ** 16, size=(B * N, 24), dtype=np.uint16)
+    packed, cu, gather = oracle.pack(keep, src)
+    ref_gather = np.flatnonzero(keep.reshape(-1))
+    assert (gather == ref_gather).all()
+    ref_cu = np.concatenate([[0], np.cumsum(np.count_nonzero(keep, axis=1))])
+    assert (cu == ref_cu).all()
+    assert (packed == src[ref_gather]).all()
+
+
+@pytest.mark.parametrize("make", [wl.tiny, lambda: wl.deits(4, 800), lambda: wl.deitb_ragged(64)])
+def test_pack_invariants_on_workloads(make):
+    w = make()
+    rows = wl.rows(w)
+    packed, cu, gather = oracle.pack(w.keep, rows)
+    assert cu[0] == 0 and (np.diff(cu) >= 0).all()
+    assert cu[-1] == np.count_nonzero(w.keep) == w.T
+    assert (np.diff(cu) == w.lengths).all()
+    for b in range(w.B):
+        seg = gather[cu[b]:cu[b + 1]]
+        assert (np.diff(seg) > 0).all()
+        assert (seg // w.N == b).all()
+        assert seg[0] == b * w.N  # CLS is always kept
+    assert (packed == rows[gather]).all()
+
+
+def test_unpack_roundtrip_and_sentinel():
+    w = wl.deits(4, 800)
+    rows = wl.rows(w)
+    packed, cu, gather = oracle.pack(w.keep, rows)
+    sentinel = np.full_like(rows, 0xA5A5)
+    out = oracle.unpack(packed, cu, gather, sentinel)
+    kept = w.keep.reshape(-1) != 0
+    assert (out[kept] == rows[kept]).all()
+    assert (out[~kept] == 0xA5A5).all()
+    # golden indices
+    g = _read_golden("pack_worked_example.txt")
+    B, N = int(g["B"][0][0]), int(g["N"][0][0])
+    keep = np.array([[int(x) for x in row] for row in g["keep"]], dtype=np.uint8)
+    src = np.arange(B * N * 2, dtype=np.float32).reshape(B * N, 2)
+    pk, cu2, ga = oracle.pack(keep, src)
+    out2 = oracle.unpack(pk, cu2, ga, np.full_like(src, -1.0))
+    mask = keep.reshape(-1) != 0
+    assert (out2[mask] == src[mask]).all() and (out2[~mask] == -1.0).all()
+
+
+# ----------------------------------------------------------------- attention
+def test_attn_golden_worked_example():
+    g = _read_golden("attn_worked_example.txt")
+    d = int(g["d"][0][0])
+    cu = np.array([int(x) for x in g["cu_seqlens"][0]], dtype=np.int32)
+    q = _f32([[float(x) for x in r] for r in g["q"]])
+    k = _f32([[float(x) for x in r] for r in g["k"]])
+    v = _f32([[float(x) for x in r] for r in g["v"]])
+    want = np.array([[float(x) for x in r] for r in g["o"]])
+    got = oracle.attn(q, k, v, cu, H=1, d=d, scale=math.log(3.0))
+    assert np.abs(got - want).max() < 1e-12
+
+
+def _rand_case(rng, lengths, H, d, dtype="f32"):
+    T = int(sum(lengths))
+    x = rng.standard_normal((T, 3, H * d)).astype(np.float32)
+    if dtype == "bf16":
+        x = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    return x, cu
+
+
+def _decode(a):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    return a.astype(np.float64)
+
+
+def test_attn_length_one_returns_v_row():
+    rng = np.random.default_rng(3)
+    x, cu = _rand_case(rng, [1, 1, 1], H=2, d=8)
+    o = oracle.attn(x[:, 0], x[:, 1], x[:, 2], cu, H=2, d=8, scale=0.35)
+    assert (o == x[:, 2].astype(np.float64)).all()
+
+
+def test_attn_zero_query_or_zero_scale_gives_mean_of_v():
+    rng = np.random.default_rng(4)
+    x, cu = _rand_case(rng, [5, 3], H=2, d=8)
+    for scale, q in ((0.7, np.zeros_like(x[:, 0])), (0.0, x[:, 0])):
+        o = oracle.attn(np.ascontiguousarray(q), x[:, 1], x[:, 2], cu, H=2, d=8, scale=scale)
+        for b in range(2):
+            seg = slice(cu[b], cu[b + 1])
+            mean = x[seg, 2].astype(np.float64).mean(axis=0)
+            assert np.abs(o[seg] - mean).max() < 1e-12
+
+
+def test_attn_constant_v_and_identical_keys():
+    rng = np.random.default_rng(5)
+    x, cu = _rand_case(rng, [6], H=1, d=8)
+    vconst = np.tile(x[:1, 2], (6, 1))
+    o = oracle.attn(x[:, 0], x[:, 1], vconst, cu, H=1, d=8, scale=0.5)
+    assert np.abs(o - vconst[0].astype(np.float64)).max() < 1e-12
+    ksame = np.tile(x[:1, 1], (6, 1))
+    o2 = oracle.attn(x[:, 0], ksame, x[:, 2], cu, H=1, d=8, scale=0.5)
+    assert np.abs(o2 - x[:, 2].astype(np.float64).mean(axis=0)).max() < 1e-12
+
+
+def test_attn_permutation_equivariant_within_image():
+    rng = np.random.default_rng(6)
+    x, cu = _rand_case(rng, [7, 5], H=2, d=8)
+    o = oracle.attn(x[:, 0], x[:, 1], x[:, 2], cu, H=2, d=8, scale=0.3)
+    perm = np.concatenate([rng.permutation(7), 7 + rng.permutation(5)])
+    xp = x[perm]
+    op = oracle.attn(xp[:, 0], xp[:, 1], xp[:, 2], cu, H=2, d=8, scale=0.3)
+    assert np.abs(op - o[perm]).max() < 1e-13
+
+
+def test_attn_bounded_by_v_and_no_leakage():
+    rng = np.random.default_rng(7)
+    x, cu = _rand_case(rng, [4, 9, 3], H=2, d=8)
+    o = oracle.attn(x[:, 0], x[:, 1], x[:, 2], cu, H=2, d=8, scale=1.3)
+    for b in range(3):
+        seg = slice(cu[b], cu[b + 1])
+        v = x[seg, 2].astype(np.float64)
+        assert (o[seg] <= v.max(axis=0) + 1e-12).all() and (o[seg] >= v.min(axis=0) - 1e-12).all()
+    y = x.copy()
+    y[cu[1]:cu[2]] = rng.standard_normal(y[cu[1]:cu[2]].shape).astype(np.float32)
+    o2 = oracle.attn(y[:, 0], y[:, 1], y[:, 2], cu, H=2, d=8, scale=1.3)
+    assert (o2[cu[0]:cu[1]] == o[cu[0]:cu[1]]).all()
+    assert (o2[cu[2]:cu[3]] == o[cu[2]:cu[3]]).all()
+    assert not (o2[cu[1]:cu[2]] == o[cu[1]:cu[2]]).all()
+
+
+def _brute_force(q, k, v, cu, H, d, scale):
+    """Pure-Python loops, exp without max subtraction, math.fsum sums."""
+    T = int(cu[-1])
+    out = [[0.0] * (H * d) for _ in range(T)]
+    for b in range(len(cu) - 1):
+        rows = range(int(cu[b]), int(cu[b + 1]))
+        for h in range(H):
+            cols = range(h * d, h * d + d)
+            for i in rows:
+                w = {j: math.exp(scale * math.fsum(float(q[i][c]) * float(k[j][c]) for c in cols))
+                     for j in rows}
+                z = math.fsum(w.values())
+                for c in cols:
+                    out[i][c] = math.fsum(w[j] * float(v[j][c]) for j in rows) / z
+    return np.array(out)
+
+
+@pytest.mark.parametrize("lengths,H,d", [([1, 2, 3], 1, 4), ([5, 2], 2, 3), ([4, 1, 5], 2, 8)])
+def test_attn_brute_force_tiny(lengths, H, d):
+    rng = np.random.default_rng(sum(lengths) * 10 + H)
+    x, cu = _rand_case(rng, lengths, H=H, d=d)
+    q, k, v = (x[:, i].astype(np.float64).tolist() for i in range(3))
+    want = _brute_force(q, k, v, cu, H, d, 0.4)
+    got = oracle.attn(x[:, 0], x[:, 1], x[:, 2], cu, H=H, d=d, scale=0.4)
+    assert np.abs(got - want).max() < 1e-12
+
+
+def _sdpa_ref(q, k, v, cu, H, d, scale):
+    """torch's fp64 SDPA on the CPU, one image at a time ([1, H, L, d])."""
+    T = int(cu[-1])
+    Q, K, V = (torch.from_numpy(_decode(a).reshape(-1, H * d)[:T]) for a in (q, k, v))
+    out = torch.zeros(T, H * d, dtype=torch.float64)
+    for b in range(len(cu) - 1):
+        s, e = int(cu[b]), int(cu[b + 1])
+        if e == s:
+            continue
+        qh, kh, vh = (X[s:e].reshape(e - s, H, d).transpose(0, 1).unsqueeze(0) for X in (Q, K, V))
+        o = torch.nn.functional.scaled_dot_product_attention(qh, kh, vh, scale=scale)
+        out[s:e] = o[0].transpose(0, 1).reshape(e - s, H * d)
+    return out.numpy()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_attn_matches_torch_sdpa_fp64(dtype):
+    rng = np.random.default_rng(11)
+    lengths = [33, 1, 70, 0, 12]
+    x, cu = _rand_case(rng, lengths, H=3, d=64, dtype=dtype)
+    got = oracle.attn(x[:, 0], x[:, 1], x[:, 2], cu, H=3, d=64, scale=0.125)
+    want = _sdpa_ref(x[:, 0], x[:, 1], x[:, 2], cu, 3, 64, 0.125)
+    assert np.abs(got - want).max() < 1e-12
+
+
+def test_attn_on_tiny_workload_matches_sdpa():
+    w = wl.tiny()
+    rows = wl.rows(w)
+    packed, cu, _ = oracle.pack(w.keep, rows)
+    q, k, v = wl.split_qkv(packed, w.C)
+    got = oracle.attn(q, k, v, cu, w.H, w.d, w.scale)
+    want = _sdpa_ref(q, k, v, cu, w.H, w.d, w.scale)
+    assert np.abs(got - want).max() < 1e-12
+
+
+def test_keep_all_equals_dense_attention():
+    w = wl.custom(B=2, N=23, H=2, lengths=[23, 23], dtype="bf16", seed=9)
+    rows = wl.rows(w)
+    packed, cu, gather = oracle.pack(w.keep, rows)
+    assert (gather == np.arange(2 * 23)).all()
+    q, k, v = wl.split_qkv(packed, w.C)
+    got = oracle.attn(q, k, v, cu, w.H, w.d, w.scale)
+    Q, K, V = (torch.from_numpy(_decode(np.ascontiguousarray(a))) for a in wl.split_qkv(rows, w.C))
+    for b in range(2):
+        for h in range(2):
+            sl = slice(b * 23, (b + 1) * 23)
+            cs = slice(h * 64, (h + 1) * 64)
+            s = w.scale * Q[sl, cs] @ K[sl, cs].T
+            ref = torch.softmax(s, dim=-1) @ V[sl, cs]
+            assert (got[sl, cs] - ref.numpy()).__abs__().max() < 1e-12
+
+
+# ------------------------------------------------------------ padded form
+def test_padded_kept_rows_equal_ragged_and_dropped_rows_match_masked_sdpa():
+    w = wl.custom(B=3, N=19, H=2, lengths=[5, 19, 1], dtype="bf16", seed=12)
+    rows = wl.rows(w)
+    q, k, v = wl.split_qkv(rows, w.C)
+    pad = oracle.attn_padded(q, k, v, w.keep, w.H, w.d, w.scale)
+    packed, cu, gather = oracle.pack(w.keep, rows)
+    pq, pk, pv = wl.split_qkv(packed, w.C)
+    rag = oracle.attn(pq, pk, pv, cu, w.H, w.d, w.scale)
+    assert np.abs(pad[gather] - rag).max() < 1e-13
+    # every query row (kept or dropped) against torch SDPA with a boolean key mask
+    Q, K, V = (torch.from_numpy(_decode(np.ascontiguousarray(a))) for a in (q, k, v))
+    for b in range(w.B):
+        sl = slice(b * w.N, (b + 1) * w.N)
+        mask = torch.from_numpy(w.keep[b] != 0)[None, None, None, :]
+        qh, kh, vh = (X[sl].reshape(w.N, w.H, w.d).transpose(0, 1).unsqueeze(0) for X in (Q, K, V))
+        o = torch.nn.functional.scaled_dot_product_attention(qh, kh, vh, attn_mask=mask, scale=w.scale)
+        ref = o[0].transpose(0, 1).reshape(w.N, w.C).numpy()
+        assert np.abs(pad[sl] - ref).max() < 1e-12
+
+
+def test_padded_empty_image_is_zero():
+    w = wl.custom(B=2, N=8, H=1, lengths=[0, 3], d=16, dtype="f32", seed=13)
+    rows = wl.rows(w)
+    q, k, v = wl.split_qkv(rows, w.C)
+    pad = oracle.attn_padded(q, k, v, w.keep, w.H, w.d, w.scale)
+    assert (pad[:8] == 0).all()
+    assert np.isfinite(pad).all()
+
+
+# -------------------------------------------------------------- workloads
+def test_workload_shapes_and_lengths():
+    t = wl.tiny()
+    assert (t.B, t.N, t.H, t.d, t.dtype) == (2, 197, 3, 64, "f32")
+    assert sorted(t.lengths.tolist()) == [40, 99] and (t.keep[:, 0] == 1).all()
+    s = wl.deits(4, 800)
+    assert (s.lengths == 40).all() and s.C == 384 and s.dtype == "bf16"
+    r = wl.deitb_ragged(64)
+    assert r.lengths.min() >= 20 and r.lengths.max() <= 197 and r.C == 768
+    b384 = wl.deitb384(32)
+    assert b384.N == 577 and b384.lengths.min() >= 231 and b384.lengths.max() <= 347
+    assert [wl.kept_length(197, p) for p in (0, 500, 800, 900)] == [197, 99, 40, 20]
+    # bf16 rounding of the draws is round-to-nearest-even of the fp32 draw
+    x = np.random.default_rng(0).standard_normal(1000, dtype=np.float32)
+    bits = wl._to_bf16_bits(x)
+    back = (bits.astype(np.uint32) << 16).view(np.float32)
+    assert (np.abs(back - x) <= np.abs(x) * 2.0 ** -8).all()

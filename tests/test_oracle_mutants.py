@@ -1,0 +1,80 @@
+"""Plant mistakes in copies of the oracle (on the CPU) and check that the pins
+in test_oracle.py catch every one of them.
+
+Each mutant is a one-token edit of oracle.c of the kind a slip would make: a
+dropped scale, a transposed operand, a wrong sign, an off-by-one, a missing
+normalisation, a head offset forgotten.  The mutant is compiled with gcc into a
+temporary directory and swapped in for the real library while the pins run.
+"""
+import os
+import shutil
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+import test_oracle as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTANTS = {
+    "drop_scale": ("s_buf[j] = scale * dot;", "s_buf[j] = dot;"),
+    "transposed_qk": ("load_elem(kb, dtype, key_rows[j] * k_stride + head_off + c);",
+                      "load_elem(kb, dtype, key_rows[j] * k_stride + head_off + (d - 1 - c));"),
+    "wrong_sign_exp": ("s_buf[j] = exp(s_buf[j] - mx);", "s_buf[j] = exp(mx - s_buf[j]);"),
+    "no_normalise": ("double p = s_buf[j] / denom;", "double p = s_buf[j];"),
+    "no_head_offset_v": ("out[c] += p * load_elem(vb, dtype, key_rows[j] * v_stride + head_off + c);",
+                         "out[c] += p * load_elem(vb, dtype, key_rows[j] * v_stride + c);"),
+    "offset_off_by_one": ("int64_t start = cu_seqlens[b];",
+                          "int64_t start = cu_seqlens[b] - (b > 0);"),
+    "pack_skip_first": ("for (int32_t n = 0; n < N; ++n) {\n            if (keep",
+                        "for (int32_t n = 1; n < N; ++n) {\n            if (keep"),
+    "pack_keep_is_one": ("if (keep[(int64_t)b * N + n] != 0) {", "if (keep[(int64_t)b * N + n] == 1) {"),
+    "unpack_off_by_one": ("for (int64_t t = 0; t < T; ++t)", "for (int64_t t = 1; t < T; ++t)"),
+    "padded_ignores_mask": ("const uint8_t* ok = keep + (int64_t)b * N;", "const uint8_t* ok = NULL;"),
+    "bf16_decode_shift": ("uint32_t w = ((uint32_t)bits) << 16;", "uint32_t w = ((uint32_t)bits) << 15;"),
+}
+
+PINS = [
+    pins.test_bf16_decode_exhaustive_matches_torch,
+    pins.test_pack_golden,
+    lambda: pins.test_pack_matches_flatnonzero(0, 0.5),
+    pins.test_unpack_roundtrip_and_sentinel,
+    pins.test_attn_golden_worked_example,
+    pins.test_attn_length_one_returns_v_row,
+    pins.test_attn_zero_query_or_zero_scale_gives_mean_of_v,
+    pins.test_attn_constant_v_and_identical_keys,
+    pins.test_attn_bounded_by_v_and_no_leakage,
+    lambda: pins.test_attn_brute_force_tiny([4, 1, 5], 2, 8),
+    lambda: pins.test_attn_matches_torch_sdpa_fp64("bf16"),
+    pins.test_padded_kept_rows_equal_ragged_and_dropped_rows_match_masked_sdpa,
+]
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name):
+    old, new = MUTANTS[name]
+    text = open(SRC).read()
+    assert text.count(old) == 1, "mutation site not found: %s" % name
+    tmp = tempfile.mkdtemp(prefix="oracle_mutant_")
+    try:
+        csrc = os.path.join(tmp, "oracle.c")
+        with open(csrc, "w") as f:
+            f.write(text.replace(old, new))
+        lib = os.path.join(tmp, "liboracle_mutant.so")
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", csrc, "-o", lib, "-lm"])
+        saved = oracle._load()
+        oracle._lib = oracle._bind(lib)
+        caught = []
+        try:
+            for pin in PINS:
+                try:
+                    pin()
+                except (AssertionError, ValueError, IndexError):
+                    caught.append(getattr(pin, "__name__", "lambda"))
+        finally:
+            oracle._lib = saved
+        assert caught, "no pin caught mutant %s" % name
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
