@@ -1,0 +1,249 @@
+/*
+ * rag.h -- C ABI of librag.so: ragged pack -> attend -> unpack for token-pruned
+ * Vision Transformers on AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one of "Dispatch-Aware Ragged Attention for Pruned Vision
+ * Transformers" (arXiv 2604.15408):
+ *   [abstract]     the English abstract (paperdance.org card, info.umar.mx
+ *                  record): after token pruning, ViT sequences are short (at
+ *                  most 197 tokens at 224x224) and of different lengths per
+ *                  image; a bidirectional attention kernel runs directly on
+ *                  these ragged sequences, and the pruning savings only show in
+ *                  wall-clock time if the host-side dispatch cost per call is
+ *                  small.  The calls follow the variable-length attention
+ *                  convention: packed tokens, cu_seqlens, max_seqlen.
+ *   [blog-method]  agents-report.net, "Triton Ragged Attention 與
+ *                  pack-attend-unpack", section 方法概覽 (method overview):
+ *                  pack (cu_seqlens + destination indices from the pruning
+ *                  decision, then a vectorised copy of the surviving tokens into
+ *                  one flat buffer), ragged attention on that buffer, unpack
+ *                  (write results back to their batch positions via cu_seqlens).
+ *   [blog-problem] same page, section 問題 (problem): the padded form pads every
+ *                  image to one length and masks, reading and writing the whole
+ *                  padded tensor.
+ *
+ * Conventions for every call:
+ *   - All tensors are device memory owned by the caller.  The library never
+ *     allocates or frees on these paths; it owns only rag_pipeline objects.
+ *   - Every call enqueues its kernel(s) on `stream` (a hipStream_t passed as
+ *     void*; NULL = the null stream) and returns without synchronising.  No
+ *     value travels back to the host: T = cu_seqlens[B] and the longest kept
+ *     length stay on the device, and grids are sized from host-side upper
+ *     bounds (B, N, max_seqlen).
+ *   - Arguments are checked on the host before anything is enqueued; a bad
+ *     argument returns an error status and enqueues nothing.  Device data
+ *     (keep bytes, cu_seqlens, gather_idx) is the caller's contract; kernels
+ *     clamp offsets and indices into the buffers they were given, so bad data
+ *     gives wrong numbers, not out-of-bounds accesses.
+ *   - Nothing throws across the ABI and nothing aborts.  After a non-OK status,
+ *     rag_last_error() returns a message for the calling thread.
+ *   - Buffers passed to one call must not overlap, except q/k/v, which may be
+ *     views into one fused row.
+ */
+#ifndef RAG_H
+#define RAG_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(RAG_BUILDING_LIBRARY)
+#define RAG_API __attribute__((visibility("default")))
+#else
+#define RAG_API
+#endif
+
+/* Status of every call. */
+typedef enum rag_status {
+    RAG_OK = 0,
+    RAG_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, stride too small, ... */
+    RAG_ERR_UNSUPPORTED = 2, /* head_dim != 64, unknown dtype or flag, size over a limit */
+    RAG_ERR_ALIGNMENT = 3,   /* pointer, stride or row size not a multiple of 16 bytes */
+    RAG_ERR_HIP = 4          /* the HIP runtime reported an error (text in rag_last_error) */
+} rag_status;
+
+/* Element types. */
+typedef enum rag_dtype {
+    RAG_DTYPE_F32 = 0,  /* IEEE binary32 */
+    RAG_DTYPE_BF16 = 1  /* bfloat16 (upper half of binary32) */
+} rag_dtype;
+
+/* The only head dimension the attention kernels are built for (DeiT: 64). */
+#define RAG_HEAD_DIM 64
+/* Largest N (tokens per image before pruning) pack/unpack/padded accept. */
+#define RAG_MAX_N 8192
+/* Largest B (images per call). */
+#define RAG_MAX_B 65535
+
+/* rag_unpack flag: also write zeros to the dst rows of dropped tokens. */
+#define RAG_UNPACK_ZERO_DROPPED 1u
+
+/*
+ * rag_pack -- keep mask to cu_seqlens and gather index, then copy the kept
+ * token rows into one flat buffer ([blog-method], fused token packing).
+ *
+ *   keep        [B, N] uint8, row-major (row stride N), 16-byte aligned base.
+ *               A nonzero byte keeps the token.  Position n of image b is the
+ *               source row b*N + n.
+ *   src         token rows; row r starts at src + r*src_row_stride (bytes).
+ *   row_bytes   bytes copied per token row (e.g. a fused q|k|v row of
+ *               3*H*64 elements); multiple of 16.
+ *   packed      output rows, capacity B*N rows (T is known only on the
+ *               device); row t at packed + t*packed_row_stride (bytes).
+ *               Rows t >= T are not written.
+ *   cu_seqlens  out, int32[B+1]: cu[0] = 0, cu[b+1] = cu[b] + L_b, where L_b
+ *               is the number of kept tokens of image b.
+ *   gather_idx  out, int32, capacity B*N: gather_idx[cu[b] + i] = b*N + n_i
+ *               where n_0 < n_1 < ... are image b's kept positions (tokens keep
+ *               their original order).  Entries >= T are not written.
+ *   max_seqlen_dev  out, int32[1], max_b L_b; may be NULL (then not computed).
+ *
+ * Every output is a plain function of keep and src: bit-exact and the same on
+ * every run.  Pointers (keep, src, packed) and strides must be multiples of 16
+ * bytes (RAG_ERR_ALIGNMENT); strides must be >= row_bytes.  1 <= B <= RAG_MAX_B,
+ * 1 <= N <= RAG_MAX_N.
+ */
+RAG_API rag_status rag_pack(const uint8_t* keep, int32_t B, int32_t N, const void* src,
+                            int64_t src_row_stride, int32_t row_bytes, void* packed,
+                            int64_t packed_row_stride, int32_t* cu_seqlens,
+                            int32_t* gather_idx, int32_t* max_seqlen_dev, void* stream);
+
+/*
+ * rag_attn -- bidirectional multi-head attention on packed ragged sequences
+ * ([abstract]; [blog-method], ragged attention kernel).
+ *
+ * Image b owns packed rows cu_seqlens[b] .. cu_seqlens[b+1]-1.  For every head
+ * h and every row i of image b:
+ *     O[i, h] = sum_j softmax_j(scale * Q[i, h] . K[j, h]) V[j, h]
+ * with j over the rows of image b only (no causal mask, no cross-image terms).
+ *
+ *   q, k, v     packed rows; head h of row t is the `head_dim` elements at
+ *               X + t*X_row_stride + h*head_dim (strides in ELEMENTS).  q, k, v
+ *               may be views into one fused row (q | k | v).
+ *   in_dtype    BF16, or F32 (each value is then split exactly enough into a
+ *               bf16 high and low part that the result matches fp32 inputs).
+ *   cu_seqlens  int32[B+1], device; non-decreasing, values in [0, total_rows].
+ *   max_seqlen  host-side upper bound of max_b L_b (e.g. N).  Sizes the grid;
+ *               rows of an image past max_seqlen are not written.
+ *   total_rows  capacity of q/k/v/o in rows; cu values are clamped to it.
+ *   H, head_dim heads; head_dim must be RAG_HEAD_DIM.
+ *   scale       softmax scale (finite), e.g. 1/sqrt(64).
+ *   o           output rows (same row indexing); out_dtype F32, or BF16
+ *               (round to nearest even of the value the F32 mode stores).
+ *
+ * Arithmetic: bf16 MFMA products with fp32 accumulation and an fp32 online
+ * softmax; the softmax weights are split into bf16 high + low parts for the
+ * P.V product.  Deterministic (no atomics).  Max abs error vs exact fp64
+ * attention on the same inputs: <= 2e-3 for F32 output (measured well below).
+ * Pointers must be 16-byte aligned and row strides multiples of 16 bytes.
+ */
+RAG_API rag_status rag_attn(const void* q, const void* k, const void* v, int64_t q_row_stride,
+                            int64_t k_row_stride, int64_t v_row_stride, rag_dtype in_dtype,
+                            const int32_t* cu_seqlens, int32_t B, int32_t max_seqlen,
+                            int32_t total_rows, int32_t H, int32_t head_dim, float scale,
+                            void* o, int64_t o_row_stride, rag_dtype out_dtype, void* stream);
+
+/*
+ * rag_unpack -- scatter packed rows back to their batch positions
+ * ([blog-method], write-back via cu_seqlens).
+ *
+ *   dst row gather_idx[t] = packed row t, for t < cu_seqlens[B].  Rows of
+ *   dropped tokens are left untouched, unless flags has
+ *   RAG_UNPACK_ZERO_DROPPED, in which case they are set to zero bytes.
+ *   cu_seqlens / gather_idx as produced by rag_pack (gather values of image b
+ *   lie in [b*N, (b+1)*N); others are skipped).  Same alignment rules as
+ *   rag_pack.  Bit-exact.
+ */
+RAG_API rag_status rag_unpack(const void* packed, int64_t packed_row_stride, int32_t row_bytes,
+                              const int32_t* cu_seqlens, const int32_t* gather_idx, int32_t B,
+                              int32_t N, void* dst, int64_t dst_row_stride, uint32_t flags,
+                              void* stream);
+
+/*
+ * rag_attn_padded -- the padded comparator ([blog-problem]): the same
+ * attention on the unpacked [B, N] layout, every image padded to N rows, key n
+ * of image b taking part only if keep[b*N + n] != 0.  Every query row (kept or
+ * dropped) is written; kept rows equal rag_attn's result up to rounding.  An
+ * image with no kept token gets zero rows.  Work is B*N*N per head whatever the
+ * prune rate.  q/k/v/o rows are b*N + n; other arguments as in rag_attn.
+ */
+RAG_API rag_status rag_attn_padded(const void* q, const void* k, const void* v,
+                                   int64_t q_row_stride, int64_t k_row_stride,
+                                   int64_t v_row_stride, rag_dtype in_dtype, const uint8_t* keep,
+                                   int32_t B, int32_t N, int32_t H, int32_t head_dim, float scale,
+                                   void* o, int64_t o_row_stride, rag_dtype out_dtype,
+                                   void* stream);
+
+/*
+ * A whole pack -> attend -> unpack pass captured once into a HIP graph, so
+ * that each later pass costs one host call ([abstract]: the per-call host
+ * dispatch cost is what hides the pruning savings).
+ *
+ * The attention reads fused rows of the packed buffer: q at element 0, k at
+ * element H*64, v at element 2*H*64 of each row (src rows are [3, H, 64]).
+ * Buffers are fixed at creation; relaunching reads the current contents.
+ */
+typedef struct rag_pipeline_desc {
+    const uint8_t* keep;     /* [B, N] */
+    int32_t B, N, H, head_dim;
+    rag_dtype in_dtype;      /* element type of src / packed */
+    rag_dtype out_dtype;     /* element type of o_packed / dst */
+    float scale;
+    int32_t max_seqlen;      /* host upper bound, <= N; 0 means N */
+    const void* src;         /* [B*N] fused rows of 3*H*64 elements */
+    int64_t src_row_stride;  /* bytes */
+    void* packed;            /* capacity B*N fused rows */
+    int64_t packed_row_stride; /* bytes */
+    int32_t* cu_seqlens;     /* [B+1] */
+    int32_t* gather_idx;     /* capacity B*N */
+    int32_t* max_seqlen_dev; /* [1] or NULL */
+    void* o_packed;          /* capacity B*N rows of H*64 out_dtype elements */
+    int64_t o_packed_row_stride; /* bytes */
+    void* dst;               /* [B*N] rows of H*64 out_dtype elements */
+    int64_t dst_row_stride;  /* bytes */
+    uint32_t unpack_flags;
+} rag_pipeline_desc;
+
+typedef struct rag_pipeline rag_pipeline;
+
+/* Check the descriptor, capture the three calls into a graph and instantiate
+ * it.  Runs nothing on the device.  *out is NULL on error. */
+RAG_API rag_status rag_pipeline_create(const rag_pipeline_desc* desc, rag_pipeline** out);
+/* Enqueue one pass on `stream`: a single hipGraphLaunch. */
+RAG_API rag_status rag_pipeline_launch(rag_pipeline* p, void* stream);
+/* Enqueue the same pass as three plain launches (no graph) on `stream`. */
+RAG_API rag_status rag_pipeline_launch_eager(rag_pipeline* p, void* stream);
+/* Free the graph; the caller must make sure no launch is still pending. */
+RAG_API void rag_pipeline_destroy(rag_pipeline* p);
+
+/*
+ * Host-side dispatch measurement (the quantity [abstract] is about), taken in
+ * C++ with no Python in the loop.  Times, in microseconds, with
+ * std::chrono::steady_clock over `iters` repetitions after `warmup`:
+ *   [0..2]   empty kernel: launch + hipStreamSynchronize, p10 / p50 / p90
+ *   [3..5]   empty kernel: host enqueue only (launch call return), p10/p50/p90
+ *   [6..8]   rag_attn from the pipeline desc: launch + sync
+ *   [9..11]  rag_attn: host enqueue only
+ *   [12..14] pack + attn + unpack as three launches: launch + sync
+ *   [15..17] the same pass as one hipGraphLaunch: launch + sync
+ *   [18..20] rag_attn_padded on the desc's src/keep (output into dst): launch + sync
+ * `out_us` must hold RAG_FLOOR_N doubles.  Runs work on `stream`.
+ */
+#define RAG_FLOOR_N 21
+RAG_API rag_status rag_measure_dispatch(rag_pipeline* p, int32_t warmup, int32_t iters,
+                                        double* out_us, void* stream);
+
+/* Message for the last non-OK status returned on the calling thread. */
+RAG_API const char* rag_last_error(void);
+/* Static name of a status code. */
+RAG_API const char* rag_status_string(rag_status s);
+/* Library ABI version (major*10000 + minor*100 + patch). */
+RAG_API int32_t rag_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RAG_H */

@@ -1,0 +1,297 @@
+"""Thin ctypes binding of librag.so (argument marshalling only).
+
+Every function here takes torch tensors that live on the GPU, turns them into
+pointers, strides and sizes, and calls the C entry point of the same name on
+torch's current stream.  No arithmetic of the path happens in Python, and there
+is no fallback: if librag.so is missing or a tensor is not on the GPU the call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librag.so")
+
+RAG_OK = 0
+STATUS = {0: "RAG_OK", 1: "RAG_ERR_INVALID_ARG", 2: "RAG_ERR_UNSUPPORTED", 3: "RAG_ERR_ALIGNMENT",
+          4: "RAG_ERR_HIP"}
+RAG_DTYPE_F32 = 0
+RAG_DTYPE_BF16 = 1
+RAG_UNPACK_ZERO_DROPPED = 1
+RAG_HEAD_DIM = 64
+RAG_FLOOR_N = 21
+
+#: Every symbol include/rag.h declares.
+EXPORTS = ("rag_pack", "rag_attn", "rag_unpack", "rag_attn_padded", "rag_pipeline_create",
+           "rag_pipeline_launch", "rag_pipeline_launch_eager", "rag_pipeline_destroy",
+           "rag_measure_dispatch", "rag_last_error", "rag_status_string", "rag_version")
+
+_lib = None
+
+
+class RagError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s: %s" % (STATUS.get(status, status), message))
+        self.status = status
+
+
+class PipelineDesc(ctypes.Structure):
+    _fields_ = [
+        ("keep", ctypes.c_void_p),
+        ("B", ctypes.c_int32), ("N", ctypes.c_int32), ("H", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("max_seqlen", ctypes.c_int32),
+        ("src", ctypes.c_void_p), ("src_row_stride", ctypes.c_int64),
+        ("packed", ctypes.c_void_p), ("packed_row_stride", ctypes.c_int64),
+        ("cu_seqlens", ctypes.c_void_p), ("gather_idx", ctypes.c_void_p),
+        ("max_seqlen_dev", ctypes.c_void_p),
+        ("o_packed", ctypes.c_void_p), ("o_packed_row_stride", ctypes.c_int64),
+        ("dst", ctypes.c_void_p), ("dst_row_stride", ctypes.c_int64),
+        ("unpack_flags", ctypes.c_uint32),
+    ]
+
+
+def load(path: str = LIB_PATH):
+    """Open librag.so and declare its signatures (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError("librag.so is not built (%s); run "
+                           "`python -m ragged_attention_token_amd.build`" % path)
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, u32, f32 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32,
+                              ctypes.c_float)
+    lib.rag_pack.argtypes = [vp, i32, i32, vp, i64, i32, vp, i64, vp, vp, vp, vp]
+    lib.rag_attn.argtypes = [vp, vp, vp, i64, i64, i64, i32, vp, i32, i32, i32, i32, i32, f32, vp,
+                             i64, i32, vp]
+    lib.rag_unpack.argtypes = [vp, i64, i32, vp, vp, i32, i32, vp, i64, u32, vp]
+    lib.rag_attn_padded.argtypes = [vp, vp, vp, i64, i64, i64, i32, vp, i32, i32, i32, i32, f32,
+                                    vp, i64, i32, vp]
+    lib.rag_pipeline_create.argtypes = [ctypes.POINTER(PipelineDesc), ctypes.POINTER(vp)]
+    lib.rag_pipeline_launch.argtypes = [vp, vp]
+    lib.rag_pipeline_launch_eager.argtypes = [vp, vp]
+    lib.rag_pipeline_destroy.argtypes = [vp]
+    lib.rag_pipeline_destroy.restype = None
+    lib.rag_measure_dispatch.argtypes = [vp, i32, i32, ctypes.POINTER(ctypes.c_double), vp]
+    lib.rag_last_error.restype = ctypes.c_char_p
+    lib.rag_status_string.argtypes = [i32]
+    lib.rag_status_string.restype = ctypes.c_char_p
+    lib.rag_version.restype = i32
+    for name in ("rag_pack", "rag_attn", "rag_unpack", "rag_attn_padded", "rag_pipeline_create",
+                 "rag_pipeline_launch", "rag_pipeline_launch_eager", "rag_measure_dispatch"):
+        getattr(lib, name).restype = i32
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load().rag_last_error().decode()
+
+
+def _check(status: int):
+    if status != RAG_OK:
+        raise RagError(status, last_error())
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _gpu(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a torch tensor on the GPU" % name)
+    return t
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return RAG_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return RAG_DTYPE_BF16
+    raise TypeError("dtype must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _rows(t: torch.Tensor, name: str):
+    """(pointer, row stride in elements) of a tensor whose first axis is rows and
+    whose remaining axes are contiguous."""
+    _gpu(t, name)
+    if t.dim() < 2:
+        raise ValueError("%s must have a row axis and a column axis" % name)
+    inner = t[0] if t.shape[0] > 0 else t.new_empty(t.shape[1:])
+    if t.shape[0] > 0 and not inner.is_contiguous():
+        raise ValueError("%s: elements within a row must be contiguous" % name)
+    return t.data_ptr(), t.stride(0)
+
+
+def _row_bytes(t: torch.Tensor) -> int:
+    n = 1
+    for s in t.shape[1:]:
+        n *= s
+    return n * t.element_size()
+
+
+def rag_pack(keep: torch.Tensor, src: torch.Tensor, packed: torch.Tensor, cu_seqlens: torch.Tensor,
+             gather_idx: torch.Tensor, max_seqlen_dev: Optional[torch.Tensor] = None,
+             row_bytes: Optional[int] = None, stream=None) -> None:
+    """keep [B,N] uint8; src rows [B*N, ...]; packed rows [>= B*N, ...];
+    cu_seqlens int32 [B+1]; gather_idx int32 [>= B*N]; max_seqlen_dev int32 [1]."""
+    _gpu(keep, "keep")
+    if keep.dtype != torch.uint8 or keep.dim() != 2 or not keep.is_contiguous():
+        raise ValueError("keep must be a contiguous uint8 [B, N] tensor")
+    B, N = keep.shape
+    sp, ss = _rows(src, "src")
+    pp, ps = _rows(packed, "packed")
+    for t, name in ((cu_seqlens, "cu_seqlens"), (gather_idx, "gather_idx")):
+        _gpu(t, name)
+        if t.dtype != torch.int32:
+            raise TypeError("%s must be int32" % name)
+    if src.shape[0] < B * N or packed.shape[0] < B * N or gather_idx.numel() < B * N \
+            or cu_seqlens.numel() < B + 1:
+        raise ValueError("buffers smaller than the B*N capacity")
+    rb = _row_bytes(src) if row_bytes is None else int(row_bytes)
+    mp = None
+    if max_seqlen_dev is not None:
+        _gpu(max_seqlen_dev, "max_seqlen_dev")
+        mp = max_seqlen_dev.data_ptr()
+    _check(load().rag_pack(keep.data_ptr(), B, N, sp, ss * src.element_size(), rb, pp,
+                           ps * packed.element_size(), cu_seqlens.data_ptr(),
+                           gather_idx.data_ptr(), mp, _stream(stream)))
+
+
+def rag_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
+             max_seqlen: int, o: torch.Tensor, H: int, scale: float, head_dim: int = RAG_HEAD_DIM,
+             total_rows: Optional[int] = None, stream=None) -> None:
+    """q, k, v, o: [rows, >= H*head_dim] (row stride free, rows contiguous inside);
+    cu_seqlens int32 [B+1] on the GPU; max_seqlen a host upper bound."""
+    qp, qs = _rows(q, "q")
+    kp, ks = _rows(k, "k")
+    vp, vs = _rows(v, "v")
+    op, os_ = _rows(o, "o")
+    _gpu(cu_seqlens, "cu_seqlens")
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    rows = min(q.shape[0], k.shape[0], v.shape[0], o.shape[0])
+    tr = rows if total_rows is None else int(total_rows)
+    if tr > rows:
+        raise ValueError("total_rows larger than the buffers")
+    B = cu_seqlens.numel() - 1
+    _check(load().rag_attn(qp, kp, vp, qs, ks, vs, _dtype_code(q), cu_seqlens.data_ptr(), B,
+                           int(max_seqlen), tr, int(H), int(head_dim), float(scale), op, os_,
+                           _dtype_code(o), _stream(stream)))
+
+
+def rag_unpack(packed: torch.Tensor, cu_seqlens: torch.Tensor, gather_idx: torch.Tensor,
+               dst: torch.Tensor, N: int, flags: int = 0, row_bytes: Optional[int] = None,
+               stream=None) -> None:
+    """packed rows [>= B*N, ...] -> dst rows [B*N, ...]."""
+    pp, ps = _rows(packed, "packed")
+    dp, ds = _rows(dst, "dst")
+    for t, name in ((cu_seqlens, "cu_seqlens"), (gather_idx, "gather_idx")):
+        _gpu(t, name)
+        if t.dtype != torch.int32:
+            raise TypeError("%s must be int32" % name)
+    B = cu_seqlens.numel() - 1
+    if dst.shape[0] < B * N or packed.shape[0] < B * N or gather_idx.numel() < B * N:
+        raise ValueError("buffers smaller than the B*N capacity")
+    rb = _row_bytes(dst) if row_bytes is None else int(row_bytes)
+    _check(load().rag_unpack(pp, ps * packed.element_size(), rb, cu_seqlens.data_ptr(),
+                             gather_idx.data_ptr(), B, int(N), dp, ds * dst.element_size(),
+                             int(flags), _stream(stream)))
+
+
+def rag_attn_padded(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, keep: torch.Tensor,
+                    o: torch.Tensor, H: int, scale: float, head_dim: int = RAG_HEAD_DIM,
+                    stream=None) -> None:
+    """Padded comparator: q/k/v/o rows b*N + n of the [B, N] layout."""
+    qp, qs = _rows(q, "q")
+    kp, ks = _rows(k, "k")
+    vp, vs = _rows(v, "v")
+    op, os_ = _rows(o, "o")
+    _gpu(keep, "keep")
+    if keep.dtype != torch.uint8 or keep.dim() != 2 or not keep.is_contiguous():
+        raise ValueError("keep must be a contiguous uint8 [B, N] tensor")
+    B, N = keep.shape
+    if min(q.shape[0], k.shape[0], v.shape[0], o.shape[0]) < B * N:
+        raise ValueError("q/k/v/o need B*N rows")
+    _check(load().rag_attn_padded(qp, kp, vp, qs, ks, vs, _dtype_code(q), keep.data_ptr(), B, N,
+                                  int(H), int(head_dim), float(scale), op, os_, _dtype_code(o),
+                                  _stream(stream)))
+
+
+class Pipeline:
+    """pack -> attend -> unpack captured once into a HIP graph.
+
+    src: fused rows [B*N, 3*H*64] (q | k | v); all buffers are kept alive here
+    and fixed for the pipeline's lifetime."""
+
+    def __init__(self, keep, src, packed, cu_seqlens, gather_idx, o_packed, dst, H, scale,
+                 max_seqlen: int = 0, max_seqlen_dev=None, unpack_flags: int = 0):
+        B, N = keep.shape
+        for t, name in ((keep, "keep"), (src, "src"), (packed, "packed"),
+                        (cu_seqlens, "cu_seqlens"), (gather_idx, "gather_idx"),
+                        (o_packed, "o_packed"), (dst, "dst")):
+            _gpu(t, name)
+        if src.dtype != packed.dtype or o_packed.dtype != dst.dtype:
+            raise TypeError("src/packed and o_packed/dst must share dtypes")
+        if min(src.shape[0], packed.shape[0], o_packed.shape[0], dst.shape[0],
+               gather_idx.numel()) < B * N or cu_seqlens.numel() < B + 1:
+            raise ValueError("buffers smaller than the B*N capacity")
+        self._keep_alive = (keep, src, packed, cu_seqlens, gather_idx, o_packed, dst,
+                            max_seqlen_dev)
+        d = PipelineDesc()
+        d.keep = keep.data_ptr()
+        d.B, d.N, d.H, d.head_dim = B, N, int(H), RAG_HEAD_DIM
+        d.in_dtype, d.out_dtype = _dtype_code(src), _dtype_code(dst)
+        d.scale = float(scale)
+        d.max_seqlen = int(max_seqlen)
+        d.src, d.src_row_stride = src.data_ptr(), src.stride(0) * src.element_size()
+        d.packed, d.packed_row_stride = packed.data_ptr(), packed.stride(0) * packed.element_size()
+        d.cu_seqlens, d.gather_idx = cu_seqlens.data_ptr(), gather_idx.data_ptr()
+        d.max_seqlen_dev = max_seqlen_dev.data_ptr() if max_seqlen_dev is not None else None
+        d.o_packed = o_packed.data_ptr()
+        d.o_packed_row_stride = o_packed.stride(0) * o_packed.element_size()
+        d.dst, d.dst_row_stride = dst.data_ptr(), dst.stride(0) * dst.element_size()
+        d.unpack_flags = int(unpack_flags)
+        self.desc = d
+        handle = ctypes.c_void_p()
+        _check(load().rag_pipeline_create(ctypes.byref(d), ctypes.byref(handle)))
+        self._h = handle
+
+    def launch(self, stream=None) -> None:
+        _check(load().rag_pipeline_launch(self._h, _stream(stream)))
+
+    def launch_eager(self, stream=None) -> None:
+        _check(load().rag_pipeline_launch_eager(self._h, _stream(stream)))
+
+    def measure_dispatch(self, warmup: int = 100, iters: int = 1000, stream=None) -> dict:
+        out = (ctypes.c_double * RAG_FLOOR_N)()
+        _check(load().rag_measure_dispatch(self._h, int(warmup), int(iters), out, _stream(stream)))
+        keys = ["empty_roundtrip", "empty_enqueue", "attn_roundtrip", "attn_enqueue",
+                "eager3_roundtrip", "graph_roundtrip", "padded_roundtrip"]
+        res = {}
+        for i, k in enumerate(keys):
+            res[k] = {"p10": out[3 * i], "p50": out[3 * i + 1], "p90": out[3 * i + 2]}
+        return res
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None and self._h.value:
+            load().rag_pipeline_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,269 @@
+// rag_api.hip -- the extern "C" entry points of librag.so, the graph-captured
+// pipeline and the host dispatch measurement.
+//
+// Host path ("Dispatch-Aware Ragged Attention for Pruned Vision Transformers",
+// abstract: at post-pruning lengths the host-side dispatch of each attention
+// call costs more than the GPU work, so the dispatch floor is what must come
+// down): every entry point checks its arguments on the host, enqueues exactly
+// one kernel on the caller's stream and returns; nothing is read back, nothing
+// waits, nothing is allocated.  The pipeline captures the three launches once
+// into a HIP graph so that a whole pack -> attend -> unpack pass is one host
+// call.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <chrono>
+#include <new>
+#include <vector>
+
+#include "rag_internal.h"
+
+using rag::set_error;
+
+namespace {
+
+rag_status hip_status(int err, const char* what)
+{
+    if (err == (int)hipSuccess) return RAG_OK;
+    return set_error(RAG_ERR_HIP, "%s: %s", what, hipGetErrorString((hipError_t)err));
+}
+
+__global__ void empty_kernel() {}
+
+}  // namespace
+
+extern "C" RAG_API rag_status rag_pack(const uint8_t* keep, int32_t B, int32_t N, const void* src,
+                                       int64_t src_row_stride, int32_t row_bytes, void* packed,
+                                       int64_t packed_row_stride, int32_t* cu_seqlens,
+                                       int32_t* gather_idx, int32_t* max_seqlen_dev, void* stream)
+{
+    rag_status s = rag::validate_pack(keep, B, N, src, src_row_stride, row_bytes, packed,
+                                      packed_row_stride, cu_seqlens, gather_idx);
+    if (s != RAG_OK) return s;
+    return hip_status(rag::launch_pack(keep, B, N, src, src_row_stride, row_bytes, packed,
+                                       packed_row_stride, cu_seqlens, gather_idx, max_seqlen_dev,
+                                       stream),
+                      "rag_pack launch");
+}
+
+extern "C" RAG_API rag_status rag_attn(const void* q, const void* k, const void* v,
+                                       int64_t q_row_stride, int64_t k_row_stride,
+                                       int64_t v_row_stride, rag_dtype in_dtype,
+                                       const int32_t* cu_seqlens, int32_t B, int32_t max_seqlen,
+                                       int32_t total_rows, int32_t H, int32_t head_dim,
+                                       float scale, void* o, int64_t o_row_stride,
+                                       rag_dtype out_dtype, void* stream)
+{
+    rag_status s = rag::validate_attn(q, k, v, q_row_stride, k_row_stride, v_row_stride, in_dtype,
+                                      cu_seqlens, B, max_seqlen, total_rows, H, head_dim, scale, o,
+                                      o_row_stride, out_dtype);
+    if (s != RAG_OK) return s;
+    return hip_status(rag::launch_attn(q, k, v, q_row_stride, k_row_stride, v_row_stride, in_dtype,
+                                       cu_seqlens, nullptr, B, 0, max_seqlen, total_rows, H, scale,
+                                       o, o_row_stride, out_dtype, false, stream),
+                      "rag_attn launch");
+}
+
+extern "C" RAG_API rag_status rag_unpack(const void* packed, int64_t packed_row_stride,
+                                         int32_t row_bytes, const int32_t* cu_seqlens,
+                                         const int32_t* gather_idx, int32_t B, int32_t N,
+                                         void* dst, int64_t dst_row_stride, uint32_t flags,
+                                         void* stream)
+{
+    rag_status s = rag::validate_unpack(packed, packed_row_stride, row_bytes, cu_seqlens,
+                                        gather_idx, B, N, dst, dst_row_stride, flags);
+    if (s != RAG_OK) return s;
+    return hip_status(rag::launch_unpack(packed, packed_row_stride, row_bytes, cu_seqlens,
+                                         gather_idx, B, N, dst, dst_row_stride, flags, stream),
+                      "rag_unpack launch");
+}
+
+extern "C" RAG_API rag_status rag_attn_padded(const void* q, const void* k, const void* v,
+                                              int64_t q_row_stride, int64_t k_row_stride,
+                                              int64_t v_row_stride, rag_dtype in_dtype,
+                                              const uint8_t* keep, int32_t B, int32_t N,
+                                              int32_t H, int32_t head_dim, float scale, void* o,
+                                              int64_t o_row_stride, rag_dtype out_dtype,
+                                              void* stream)
+{
+    rag_status s = rag::validate_attn_padded(q, k, v, q_row_stride, k_row_stride, v_row_stride,
+                                             in_dtype, keep, B, N, H, head_dim, scale, o,
+                                             o_row_stride, out_dtype);
+    if (s != RAG_OK) return s;
+    return hip_status(rag::launch_attn(q, k, v, q_row_stride, k_row_stride, v_row_stride, in_dtype,
+                                       nullptr, keep, B, N, N, B * N, H, scale, o, o_row_stride,
+                                       out_dtype, true, stream),
+                      "rag_attn_padded launch");
+}
+
+// ---------------------------------------------------------------- pipeline
+struct rag_pipeline {
+    rag_pipeline_desc d;
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+};
+
+namespace {
+
+// The three launches of one pass, in order, on `stream`.
+rag_status enqueue_pass(const rag_pipeline_desc& d, void* stream)
+{
+    const int64_t C = (int64_t)d.H * d.head_dim;
+    const int in_es = rag::dtype_bytes(d.in_dtype), out_es = rag::dtype_bytes(d.out_dtype);
+    const int32_t in_row = (int32_t)(3 * C * in_es), out_row = (int32_t)(C * out_es);
+    int e = rag::launch_pack(d.keep, d.B, d.N, d.src, d.src_row_stride, in_row, d.packed,
+                             d.packed_row_stride, d.cu_seqlens, d.gather_idx, d.max_seqlen_dev,
+                             stream);
+    if (e != (int)hipSuccess) return hip_status(e, "pipeline pack");
+    const char* base = static_cast<const char*>(d.packed);
+    const int64_t ps = d.packed_row_stride / in_es;
+    e = rag::launch_attn(base, base + C * in_es, base + 2 * C * in_es, ps, ps, ps, d.in_dtype,
+                         d.cu_seqlens, nullptr, d.B, 0, d.max_seqlen ? d.max_seqlen : d.N,
+                         d.B * d.N, d.H, d.scale, d.o_packed, d.o_packed_row_stride / out_es,
+                         d.out_dtype, false, stream);
+    if (e != (int)hipSuccess) return hip_status(e, "pipeline attn");
+    e = rag::launch_unpack(d.o_packed, d.o_packed_row_stride, out_row, d.cu_seqlens, d.gather_idx,
+                           d.B, d.N, d.dst, d.dst_row_stride, d.unpack_flags, stream);
+    return hip_status(e, "pipeline unpack");
+}
+
+}  // namespace
+
+extern "C" RAG_API rag_status rag_pipeline_create(const rag_pipeline_desc* desc, rag_pipeline** out)
+{
+    if (!out) return set_error(RAG_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    rag_status s = rag::validate_pipeline(desc);
+    if (s != RAG_OK) return s;
+    rag_pipeline* p = new (std::nothrow) rag_pipeline;
+    if (!p) return set_error(RAG_ERR_INVALID_ARG, "out of host memory");
+    p->d = *desc;
+    hipStream_t cs = nullptr;
+    s = hip_status((int)hipStreamCreateWithFlags(&cs, hipStreamNonBlocking), "capture stream");
+    if (s == RAG_OK) {
+        s = hip_status((int)hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal),
+                       "begin capture");
+        if (s == RAG_OK) {
+            rag_status es = enqueue_pass(p->d, cs);
+            rag_status cs_end = hip_status((int)hipStreamEndCapture(cs, &p->graph), "end capture");
+            s = es != RAG_OK ? es : cs_end;
+        }
+        if (s == RAG_OK)
+            s = hip_status((int)hipGraphInstantiate(&p->exec, p->graph, nullptr, nullptr, 0),
+                           "graph instantiate");
+        (void)hipStreamDestroy(cs);
+    }
+    if (s != RAG_OK) {
+        rag_pipeline_destroy(p);
+        return s;
+    }
+    *out = p;
+    return RAG_OK;
+}
+
+extern "C" RAG_API rag_status rag_pipeline_launch(rag_pipeline* p, void* stream)
+{
+    if (!p || !p->exec) return set_error(RAG_ERR_INVALID_ARG, "pipeline is NULL");
+    return hip_status((int)hipGraphLaunch(p->exec, static_cast<hipStream_t>(stream)),
+                      "hipGraphLaunch");
+}
+
+extern "C" RAG_API rag_status rag_pipeline_launch_eager(rag_pipeline* p, void* stream)
+{
+    if (!p) return set_error(RAG_ERR_INVALID_ARG, "pipeline is NULL");
+    return enqueue_pass(p->d, stream);
+}
+
+extern "C" RAG_API void rag_pipeline_destroy(rag_pipeline* p)
+{
+    if (!p) return;
+    if (p->exec) (void)hipGraphExecDestroy(p->exec);
+    if (p->graph) (void)hipGraphDestroy(p->graph);
+    delete p;
+}
+
+// ------------------------------------------------------- dispatch measurement
+namespace {
+
+typedef std::chrono::steady_clock Clock;
+
+void percentiles(std::vector<double>& v, double* out3)
+{
+    std::sort(v.begin(), v.end());
+    const size_t n = v.size();
+    const double qs[3] = {0.10, 0.50, 0.90};
+    for (int i = 0; i < 3; ++i) out3[i] = n ? v[std::min(n - 1, (size_t)(qs[i] * (n - 1) + 0.5))] : 0.0;
+}
+
+double us_since(Clock::time_point t0, Clock::time_point t1)
+{
+    return std::chrono::duration<double, std::micro>(t1 - t0).count();
+}
+
+// Times `launch` (returning a rag_status) `iters` times: round trip with
+// hipStreamSynchronize into rt[3], host enqueue time into enq[3] (if non-NULL).
+template <typename F>
+rag_status time_calls(F launch, hipStream_t st, int warmup, int iters, double* rt, double* enq)
+{
+    std::vector<double> a, b;
+    a.reserve(iters);
+    b.reserve(iters);
+    for (int i = 0; i < warmup + iters; ++i) {
+        const Clock::time_point t0 = Clock::now();
+        rag_status s = launch();
+        const Clock::time_point t1 = Clock::now();
+        if (s != RAG_OK) return s;
+        rag_status ss = hip_status((int)hipStreamSynchronize(st), "hipStreamSynchronize");
+        const Clock::time_point t2 = Clock::now();
+        if (ss != RAG_OK) return ss;
+        if (i >= warmup) {
+            a.push_back(us_since(t0, t2));
+            b.push_back(us_since(t0, t1));
+        }
+    }
+    percentiles(a, rt);
+    if (enq) percentiles(b, enq);
+    return RAG_OK;
+}
+
+}  // namespace
+
+extern "C" RAG_API rag_status rag_measure_dispatch(rag_pipeline* p, int32_t warmup, int32_t iters,
+                                                   double* out_us, void* stream)
+{
+    if (!p || !out_us || warmup < 0 || iters < 1)
+        return set_error(RAG_ERR_INVALID_ARG, "bad arguments to rag_measure_dispatch");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const rag_pipeline_desc& d = p->d;
+    const int64_t C = (int64_t)d.H * d.head_dim;
+    const int in_es = rag::dtype_bytes(d.in_dtype), out_es = rag::dtype_bytes(d.out_dtype);
+    const char* pk = static_cast<const char*>(d.packed);
+    const int64_t ps = d.packed_row_stride / in_es;
+    const char* sr = static_cast<const char*>(d.src);
+    const int64_t ss = d.src_row_stride / in_es;
+    const int32_t maxlen = d.max_seqlen ? d.max_seqlen : d.N;
+
+    auto empty = [&]() {
+        hipLaunchKernelGGL(empty_kernel, dim3(1), dim3(64), 0, st);
+        return hip_status((int)hipGetLastError(), "empty kernel");
+    };
+    auto attn = [&]() {
+        return rag_attn(pk, pk + C * in_es, pk + 2 * C * in_es, ps, ps, ps, d.in_dtype,
+                        d.cu_seqlens, d.B, maxlen, d.B * d.N, d.H, d.head_dim, d.scale, d.o_packed,
+                        d.o_packed_row_stride / out_es, d.out_dtype, st);
+    };
+    auto eager = [&]() { return enqueue_pass(d, st); };
+    auto graph = [&]() { return rag_pipeline_launch(p, st); };
+    auto padded = [&]() {
+        return rag_attn_padded(sr, sr + C * in_es, sr + 2 * C * in_es, ss, ss, ss, d.in_dtype,
+                               d.keep, d.B, d.N, d.H, d.head_dim, d.scale, d.dst,
+                               d.dst_row_stride / out_es, d.out_dtype, st);
+    };
+    rag_status s;
+    if ((s = time_calls(empty, st, warmup, iters, out_us + 0, out_us + 3)) != RAG_OK) return s;
+    if ((s = time_calls(attn, st, warmup, iters, out_us + 6, out_us + 9)) != RAG_OK) return s;
+    if ((s = time_calls(eager, st, warmup, iters, out_us + 12, nullptr)) != RAG_OK) return s;
+    if ((s = time_calls(graph, st, warmup, iters, out_us + 15, nullptr)) != RAG_OK) return s;
+    if ((s = time_calls(padded, st, warmup, iters, out_us + 18, nullptr)) != RAG_OK) return s;
+    return RAG_OK;
+}

@@ -1,0 +1,58 @@
+// rag_internal.h -- declarations shared by the translation units of librag.so.
+// HIP-free on purpose: rag_validate.cpp includes it and builds with any C++17
+// compiler, so argument checking can be tested without a GPU.
+#pragma once
+
+#include <cstdint>
+
+#include "rag.h"
+
+namespace rag {
+
+// Record a message for rag_last_error() on this thread and return `s`.
+rag_status set_error(rag_status s, const char* fmt, ...)
+    __attribute__((format(printf, 2, 3)));
+void clear_error();
+
+// ---- argument checks (host only, run before anything is enqueued) ----
+rag_status validate_pack(const uint8_t* keep, int32_t B, int32_t N, const void* src,
+                         int64_t src_row_stride, int32_t row_bytes, const void* packed,
+                         int64_t packed_row_stride, const int32_t* cu_seqlens,
+                         const int32_t* gather_idx);
+rag_status validate_unpack(const void* packed, int64_t packed_row_stride, int32_t row_bytes,
+                           const int32_t* cu_seqlens, const int32_t* gather_idx, int32_t B,
+                           int32_t N, const void* dst, int64_t dst_row_stride, uint32_t flags);
+rag_status validate_attn(const void* q, const void* k, const void* v, int64_t q_row_stride,
+                         int64_t k_row_stride, int64_t v_row_stride, int32_t in_dtype,
+                         const int32_t* cu_seqlens, int32_t B, int32_t max_seqlen,
+                         int32_t total_rows, int32_t H, int32_t head_dim, float scale,
+                         const void* o, int64_t o_row_stride, int32_t out_dtype);
+rag_status validate_attn_padded(const void* q, const void* k, const void* v,
+                                int64_t q_row_stride, int64_t k_row_stride, int64_t v_row_stride,
+                                int32_t in_dtype, const uint8_t* keep, int32_t B, int32_t N,
+                                int32_t H, int32_t head_dim, float scale, const void* o,
+                                int64_t o_row_stride, int32_t out_dtype);
+rag_status validate_pipeline(const rag_pipeline_desc* d);
+
+inline int dtype_bytes(int32_t dt) { return dt == RAG_DTYPE_F32 ? 4 : 2; }
+
+// ---- work split of the row-copy kernels (pack / unpack) ----
+// Rows of one image handled by one workgroup, chosen so that a workgroup moves
+// a few tens of KiB; the grid is ceil(N / rows) x B.
+int rows_per_chunk(int32_t row_bytes);
+
+// ---- launchers (defined in the .hip files; return a hipError_t value) ----
+int launch_pack(const uint8_t* keep, int32_t B, int32_t N, const void* src,
+                int64_t src_row_stride, int32_t row_bytes, void* packed,
+                int64_t packed_row_stride, int32_t* cu_seqlens, int32_t* gather_idx,
+                int32_t* max_seqlen_dev, void* stream);
+int launch_unpack(const void* packed, int64_t packed_row_stride, int32_t row_bytes,
+                  const int32_t* cu_seqlens, const int32_t* gather_idx, int32_t B, int32_t N,
+                  void* dst, int64_t dst_row_stride, uint32_t flags, void* stream);
+int launch_attn(const void* q, const void* k, const void* v, int64_t q_row_stride,
+                int64_t k_row_stride, int64_t v_row_stride, int32_t in_dtype,
+                const int32_t* cu_seqlens, const uint8_t* keep, int32_t B, int32_t N,
+                int32_t max_seqlen, int32_t total_rows, int32_t H, float scale, void* o,
+                int64_t o_row_stride, int32_t out_dtype, bool padded, void* stream);
+
+}  // namespace rag

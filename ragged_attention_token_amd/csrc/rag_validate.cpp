@@ -1,0 +1,211 @@
+// rag_validate.cpp -- host-side argument checks and the per-thread error text.
+// No HIP call lives here: every check runs before anything is enqueued, and the
+// unit tests exercise each error path on a machine without a GPU.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "rag_internal.h"
+
+namespace rag {
+
+namespace {
+thread_local char g_error[512] = "";
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool valid_dtype(int32_t dt) { return dt == RAG_DTYPE_F32 || dt == RAG_DTYPE_BF16; }
+}  // namespace
+
+rag_status set_error(rag_status s, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_error, sizeof g_error, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+void clear_error() { g_error[0] = '\0'; }
+
+int rows_per_chunk(int32_t row_bytes)
+{
+    int r = 24576 / (row_bytes > 0 ? row_bytes : 1);
+    if (r < 1) r = 1;
+    if (r > 64) r = 64;
+    return r;
+}
+
+static rag_status check_rows(const char* what, const void* base, int64_t stride, int32_t row_bytes)
+{
+    if (!base) return set_error(RAG_ERR_INVALID_ARG, "%s is NULL", what);
+    if (stride < row_bytes)
+        return set_error(RAG_ERR_INVALID_ARG, "%s row stride %lld is smaller than row_bytes %d",
+                         what, (long long)stride, row_bytes);
+    if (!aligned16(base) || (stride & 15))
+        return set_error(RAG_ERR_ALIGNMENT, "%s base and row stride must be multiples of 16 bytes",
+                         what);
+    return RAG_OK;
+}
+
+static rag_status check_batch(int32_t B, int32_t N)
+{
+    if (B < 1 || N < 1) return set_error(RAG_ERR_INVALID_ARG, "B=%d and N=%d must be >= 1", B, N);
+    if (B > RAG_MAX_B || N > RAG_MAX_N)
+        return set_error(RAG_ERR_UNSUPPORTED, "B=%d N=%d exceed the limits B<=%d N<=%d", B, N,
+                         RAG_MAX_B, RAG_MAX_N);
+    if ((int64_t)B * N > INT32_MAX)
+        return set_error(RAG_ERR_UNSUPPORTED, "B*N must fit in int32");
+    return RAG_OK;
+}
+
+rag_status validate_pack(const uint8_t* keep, int32_t B, int32_t N, const void* src,
+                         int64_t src_row_stride, int32_t row_bytes, const void* packed,
+                         int64_t packed_row_stride, const int32_t* cu_seqlens,
+                         const int32_t* gather_idx)
+{
+    rag_status s = check_batch(B, N);
+    if (s != RAG_OK) return s;
+    if (!keep) return set_error(RAG_ERR_INVALID_ARG, "keep is NULL");
+    if (!aligned16(keep)) return set_error(RAG_ERR_ALIGNMENT, "keep must be 16-byte aligned");
+    if (row_bytes < 16) return set_error(RAG_ERR_INVALID_ARG, "row_bytes=%d must be >= 16", row_bytes);
+    if (row_bytes & 15) return set_error(RAG_ERR_ALIGNMENT, "row_bytes=%d must be a multiple of 16", row_bytes);
+    if ((s = check_rows("src", src, src_row_stride, row_bytes)) != RAG_OK) return s;
+    if ((s = check_rows("packed", packed, packed_row_stride, row_bytes)) != RAG_OK) return s;
+    if (!cu_seqlens || !gather_idx)
+        return set_error(RAG_ERR_INVALID_ARG, "cu_seqlens and gather_idx must not be NULL");
+    return RAG_OK;
+}
+
+rag_status validate_unpack(const void* packed, int64_t packed_row_stride, int32_t row_bytes,
+                           const int32_t* cu_seqlens, const int32_t* gather_idx, int32_t B,
+                           int32_t N, const void* dst, int64_t dst_row_stride, uint32_t flags)
+{
+    rag_status s = check_batch(B, N);
+    if (s != RAG_OK) return s;
+    if (flags & ~RAG_UNPACK_ZERO_DROPPED)
+        return set_error(RAG_ERR_UNSUPPORTED, "unknown unpack flags 0x%x", flags);
+    if (row_bytes < 16) return set_error(RAG_ERR_INVALID_ARG, "row_bytes=%d must be >= 16", row_bytes);
+    if (row_bytes & 15) return set_error(RAG_ERR_ALIGNMENT, "row_bytes=%d must be a multiple of 16", row_bytes);
+    if ((s = check_rows("packed", packed, packed_row_stride, row_bytes)) != RAG_OK) return s;
+    if ((s = check_rows("dst", dst, dst_row_stride, row_bytes)) != RAG_OK) return s;
+    if (!cu_seqlens || !gather_idx)
+        return set_error(RAG_ERR_INVALID_ARG, "cu_seqlens and gather_idx must not be NULL");
+    return RAG_OK;
+}
+
+static rag_status check_attn_common(const void* q, const void* k, const void* v, int64_t qs,
+                                    int64_t ks, int64_t vs, int32_t in_dtype, int32_t H,
+                                    int32_t head_dim, float scale, const void* o, int64_t os,
+                                    int32_t out_dtype)
+{
+    if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+        return set_error(RAG_ERR_UNSUPPORTED, "dtype must be RAG_DTYPE_F32 or RAG_DTYPE_BF16");
+    if (head_dim != RAG_HEAD_DIM)
+        return set_error(RAG_ERR_UNSUPPORTED, "head_dim=%d; only %d is built", head_dim,
+                         RAG_HEAD_DIM);
+    if (H < 1) return set_error(RAG_ERR_INVALID_ARG, "H=%d must be >= 1", H);
+    if (!std::isfinite(scale)) return set_error(RAG_ERR_INVALID_ARG, "scale must be finite");
+    const int64_t C = (int64_t)H * head_dim;
+    const void* ptrs[4] = {q, k, v, o};
+    const int64_t strides[4] = {qs, ks, vs, os};
+    const int32_t dts[4] = {in_dtype, in_dtype, in_dtype, out_dtype};
+    const char* names[4] = {"q", "k", "v", "o"};
+    for (int i = 0; i < 4; ++i) {
+        if (!ptrs[i]) return set_error(RAG_ERR_INVALID_ARG, "%s is NULL", names[i]);
+        if (strides[i] < C)
+            return set_error(RAG_ERR_INVALID_ARG, "%s row stride %lld < H*head_dim %lld", names[i],
+                             (long long)strides[i], (long long)C);
+        if (!aligned16(ptrs[i]) || ((strides[i] * dtype_bytes(dts[i])) & 15))
+            return set_error(RAG_ERR_ALIGNMENT,
+                             "%s base and row stride must be multiples of 16 bytes", names[i]);
+    }
+    return RAG_OK;
+}
+
+rag_status validate_attn(const void* q, const void* k, const void* v, int64_t q_row_stride,
+                         int64_t k_row_stride, int64_t v_row_stride, int32_t in_dtype,
+                         const int32_t* cu_seqlens, int32_t B, int32_t max_seqlen,
+                         int32_t total_rows, int32_t H, int32_t head_dim, float scale,
+                         const void* o, int64_t o_row_stride, int32_t out_dtype)
+{
+    if (B < 1 || B > RAG_MAX_B) return set_error(RAG_ERR_INVALID_ARG, "B=%d out of [1, %d]", B, RAG_MAX_B);
+    if (max_seqlen < 1) return set_error(RAG_ERR_INVALID_ARG, "max_seqlen=%d must be >= 1", max_seqlen);
+    if (total_rows < 0) return set_error(RAG_ERR_INVALID_ARG, "total_rows=%d must be >= 0", total_rows);
+    if (!cu_seqlens) return set_error(RAG_ERR_INVALID_ARG, "cu_seqlens is NULL");
+    rag_status s = check_attn_common(q, k, v, q_row_stride, k_row_stride, v_row_stride, in_dtype,
+                                     H, head_dim, scale, o, o_row_stride, out_dtype);
+    if (s != RAG_OK) return s;
+    const int64_t qtiles = (max_seqlen + 63) / 64;
+    if (qtiles * H * B > INT32_MAX)
+        return set_error(RAG_ERR_UNSUPPORTED, "grid ceil(max_seqlen/64)*H*B exceeds int32");
+    return RAG_OK;
+}
+
+rag_status validate_attn_padded(const void* q, const void* k, const void* v,
+                                int64_t q_row_stride, int64_t k_row_stride, int64_t v_row_stride,
+                                int32_t in_dtype, const uint8_t* keep, int32_t B, int32_t N,
+                                int32_t H, int32_t head_dim, float scale, const void* o,
+                                int64_t o_row_stride, int32_t out_dtype)
+{
+    rag_status s = check_batch(B, N);
+    if (s != RAG_OK) return s;
+    if (!keep) return set_error(RAG_ERR_INVALID_ARG, "keep is NULL");
+    s = check_attn_common(q, k, v, q_row_stride, k_row_stride, v_row_stride, in_dtype, H, head_dim,
+                          scale, o, o_row_stride, out_dtype);
+    if (s != RAG_OK) return s;
+    const int64_t qtiles = (N + 63) / 64;
+    if (qtiles * H * B > INT32_MAX)
+        return set_error(RAG_ERR_UNSUPPORTED, "grid ceil(N/64)*H*B exceeds int32");
+    return RAG_OK;
+}
+
+rag_status validate_pipeline(const rag_pipeline_desc* d)
+{
+    if (!d) return set_error(RAG_ERR_INVALID_ARG, "desc is NULL");
+    if (d->head_dim != RAG_HEAD_DIM)
+        return set_error(RAG_ERR_UNSUPPORTED, "head_dim=%d; only %d is built", d->head_dim,
+                         RAG_HEAD_DIM);
+    if (!valid_dtype(d->in_dtype) || !valid_dtype(d->out_dtype))
+        return set_error(RAG_ERR_UNSUPPORTED, "dtype must be RAG_DTYPE_F32 or RAG_DTYPE_BF16");
+    if (d->H < 1) return set_error(RAG_ERR_INVALID_ARG, "H=%d must be >= 1", d->H);
+    if (d->max_seqlen < 0 || d->max_seqlen > d->N)
+        return set_error(RAG_ERR_INVALID_ARG, "max_seqlen=%d must lie in [0, N]", d->max_seqlen);
+    const int64_t C = (int64_t)d->H * d->head_dim;
+    const int64_t in_row = 3 * C * dtype_bytes(d->in_dtype);
+    const int64_t out_row = C * dtype_bytes(d->out_dtype);
+    if (in_row > INT32_MAX || out_row > INT32_MAX)
+        return set_error(RAG_ERR_UNSUPPORTED, "row too large");
+    rag_status s = validate_pack(d->keep, d->B, d->N, d->src, d->src_row_stride, (int32_t)in_row,
+                                 d->packed, d->packed_row_stride, d->cu_seqlens, d->gather_idx);
+    if (s != RAG_OK) return s;
+    const int64_t in_es = dtype_bytes(d->in_dtype), out_es = dtype_bytes(d->out_dtype);
+    if (d->packed_row_stride % in_es || d->o_packed_row_stride % out_es)
+        return set_error(RAG_ERR_ALIGNMENT, "row strides must be whole elements");
+    s = validate_attn(d->packed, d->packed, d->packed, d->packed_row_stride / in_es,
+                      d->packed_row_stride / in_es, d->packed_row_stride / in_es, d->in_dtype,
+                      d->cu_seqlens, d->B, d->max_seqlen ? d->max_seqlen : d->N, d->B * d->N,
+                      d->H, d->head_dim, d->scale, d->o_packed, d->o_packed_row_stride / out_es,
+                      d->out_dtype);
+    if (s != RAG_OK) return s;
+    return validate_unpack(d->o_packed, d->o_packed_row_stride, (int32_t)out_row, d->cu_seqlens,
+                           d->gather_idx, d->B, d->N, d->dst, d->dst_row_stride, d->unpack_flags);
+}
+
+}  // namespace rag
+
+extern "C" RAG_API const char* rag_last_error(void) { return rag::g_error; }
+
+extern "C" RAG_API const char* rag_status_string(rag_status s)
+{
+    switch (s) {
+    case RAG_OK: return "RAG_OK";
+    case RAG_ERR_INVALID_ARG: return "RAG_ERR_INVALID_ARG";
+    case RAG_ERR_UNSUPPORTED: return "RAG_ERR_UNSUPPORTED";
+    case RAG_ERR_ALIGNMENT: return "RAG_ERR_ALIGNMENT";
+    case RAG_ERR_HIP: return "RAG_ERR_HIP";
+    }
+    return "RAG_ERR_UNKNOWN";
+}
+
+extern "C" RAG_API int32_t rag_version(void) { return 100; }

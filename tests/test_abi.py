@@ -1,0 +1,147 @@
+"""The C ABI on a machine without a GPU: the library loads, exports every symbol
+include/rag.h declares, and rejects every kind of bad argument on the host with
+the documented status before anything is enqueued (no call here reaches HIP).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from ragged_attention_token_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rag.h")
+
+OK, INVALID, UNSUPPORTED, ALIGN = 0, 1, 2, 3
+F32, BF16 = 0, 1
+A = 0x100000  # a 16-byte aligned fake device address; never dereferenced here
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from ragged_attention_token_amd import build
+        build.build()
+    return binding.load()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"RAG_API\s+[\w\s\*]+?\b(rag_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    syms = declared_symbols()
+    for name in ("rag_pack", "rag_attn", "rag_unpack", "rag_attn_padded", "rag_pipeline_create",
+                 "rag_pipeline_launch", "rag_pipeline_destroy", "rag_last_error"):
+        assert name in syms
+    assert sorted(binding.EXPORTS) == syms
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    assert lib.rag_version() >= 100
+    assert lib.rag_status_string(3) == b"RAG_ERR_ALIGNMENT"
+
+
+def pack(lib, keep=A, B=2, N=197, src=A, ss=2304, rb=2304, packed=A, ps=2304, cu=A, g=A, m=None):
+    return lib.rag_pack(keep, B, N, src, ss, rb, packed, ps, cu, g, m, None)
+
+
+@pytest.mark.parametrize("kwargs,status,needle", [
+    (dict(B=0), INVALID, "B=0"),
+    (dict(N=0), INVALID, "N=0"),
+    (dict(B=70000), UNSUPPORTED, "limits"),
+    (dict(N=9000), UNSUPPORTED, "limits"),
+    (dict(keep=None), INVALID, "keep"),
+    (dict(keep=A + 3), ALIGN, "keep"),
+    (dict(rb=8), INVALID, "row_bytes"),
+    (dict(rb=2308), ALIGN, "row_bytes"),
+    (dict(src=None), INVALID, "src"),
+    (dict(src=A + 8), ALIGN, "src"),
+    (dict(ss=2000), INVALID, "src row stride"),
+    (dict(ps=2320 + 8), ALIGN, "packed"),
+    (dict(cu=None), INVALID, "cu_seqlens"),
+    (dict(g=None), INVALID, "gather_idx"),
+])
+def test_pack_rejects(lib, kwargs, status, needle):
+    assert pack(lib, **kwargs) == status
+    assert needle in binding.last_error()
+
+
+def attn(lib, q=A, k=A, v=A, qs=1152, ks=1152, vs=1152, dt=BF16, cu=A, B=4, maxlen=197, tr=788,
+         H=6, hd=64, scale=0.125, o=A, os_=384, odt=F32):
+    return lib.rag_attn(q, k, v, qs, ks, vs, dt, cu, B, maxlen, tr, H, hd, scale, o, os_, odt, None)
+
+
+@pytest.mark.parametrize("kwargs,status,needle", [
+    (dict(hd=32), UNSUPPORTED, "head_dim"),
+    (dict(dt=7), UNSUPPORTED, "dtype"),
+    (dict(odt=2), UNSUPPORTED, "dtype"),
+    (dict(H=0), INVALID, "H=0"),
+    (dict(B=0), INVALID, "B=0"),
+    (dict(maxlen=0), INVALID, "max_seqlen"),
+    (dict(tr=-1), INVALID, "total_rows"),
+    (dict(cu=None), INVALID, "cu_seqlens"),
+    (dict(q=None), INVALID, "q is NULL"),
+    (dict(v=A + 2), ALIGN, "v base"),
+    (dict(qs=100), INVALID, "q row stride"),
+    (dict(ks=388), ALIGN, "k base"),          # 388 bf16 = 776 B, not a multiple of 16
+    (dict(os_=386), ALIGN, "o base"),         # 386 fp32 = 1544 B, not a multiple of 16
+    (dict(scale=float("inf")), INVALID, "scale"),
+    (dict(scale=float("nan")), INVALID, "scale"),
+    (dict(B=65535, H=3000, maxlen=8192, qs=192000, ks=192000, vs=192000, os_=192000),
+     UNSUPPORTED, "grid"),
+])
+def test_attn_rejects(lib, kwargs, status, needle):
+    assert attn(lib, **kwargs) == status
+    assert needle in binding.last_error()
+
+
+def test_unpack_and_padded_reject(lib):
+    assert lib.rag_unpack(A, 768, 768, A, A, 4, 197, A, 768, 2, None) == UNSUPPORTED
+    assert "flags" in binding.last_error()
+    assert lib.rag_unpack(A, 768, 768, None, A, 4, 197, A, 768, 0, None) == INVALID
+    assert lib.rag_unpack(A, 768, 768, A, A, 4, 197, A + 4, 768, 0, None) == ALIGN
+    assert lib.rag_unpack(A, 768, 768, A, A, 0, 197, A, 768, 0, None) == INVALID
+    assert lib.rag_attn_padded(A, A, A, 1152, 1152, 1152, BF16, None, 4, 197, 6, 64, 0.125, A, 384,
+                               F32, None) == INVALID
+    assert lib.rag_attn_padded(A, A, A, 1152, 1152, 1152, BF16, A, 4, 197, 6, 48, 0.125, A, 384,
+                               F32, None) == UNSUPPORTED
+    assert lib.rag_attn_padded(A, A, A, 1152, 1152, 1152, BF16, A, 4, 0, 6, 64, 0.125, A, 384,
+                               F32, None) == INVALID
+
+
+def test_pipeline_rejects(lib):
+    h = ctypes.c_void_p()
+    assert lib.rag_pipeline_create(None, ctypes.byref(h)) == INVALID
+    d = binding.PipelineDesc()
+    d.keep, d.B, d.N, d.H, d.head_dim = A, 4, 197, 6, 64
+    d.in_dtype, d.out_dtype, d.scale = BF16, BF16, 0.125
+    d.src, d.src_row_stride = A, 2304
+    d.packed, d.packed_row_stride = A, 2304
+    d.cu_seqlens, d.gather_idx = A, A
+    d.o_packed, d.o_packed_row_stride = A, 768
+    d.dst, d.dst_row_stride = A, 768
+    for field, value, status in (("head_dim", 80, UNSUPPORTED), ("max_seqlen", 500, INVALID),
+                                 ("src_row_stride", 2000, INVALID), ("dst", A + 8, ALIGN),
+                                 ("unpack_flags", 4, UNSUPPORTED), ("in_dtype", 5, UNSUPPORTED)):
+        saved = getattr(d, field)
+        setattr(d, field, value)
+        assert lib.rag_pipeline_create(ctypes.byref(d), ctypes.byref(h)) == status, field
+        assert h.value is None
+        setattr(d, field, saved)
+    assert lib.rag_pipeline_launch(None, None) == INVALID
+    assert lib.rag_pipeline_launch_eager(None, None) == INVALID
+    lib.rag_pipeline_destroy(None)  # a no-op
+    out = (ctypes.c_double * binding.RAG_FLOOR_N)()
+    assert lib.rag_measure_dispatch(None, 1, 1, out, None) == INVALID
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    keep = torch.zeros(2, 4, dtype=torch.uint8)
+    with pytest.raises(TypeError):
+        binding.rag_pack(keep, keep, keep, keep, keep)

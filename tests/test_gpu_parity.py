@@ -1,0 +1,290 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.
+
+Bar: pack / unpack bit-exact (indices and bytes, capacity tails untouched);
+attention within 2e-3 max abs error of fp64 attention for fp32 output; bf16
+output is the round-to-nearest-even of the fp32 output, bit for bit, and so lies
+within 2e-3 + 2^-8 |o| of the oracle.  The oracle always computes from the
+workload's own inputs (its own packing), never from a GPU result.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import (SENTINEL_BYTE, as_numpy_rows, bf16_bits_to_f64, gpu_attn, gpu_pack,
+                         sentinel_like, to_gpu_rows, torch_dtype)
+from ragged_attention_token_amd import binding
+from ragged_attention_token_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+ATOL = 2e-3
+
+FULL = {  # workloads the oracle finishes in seconds: compared on every output
+    "tiny": wl.tiny,
+    "deits_b4_p800": lambda: wl.deits(4, 800),
+    "deitb_ragged_b64": lambda: wl.deitb_ragged(64),
+    "deits_b1_p000": lambda: wl.deits(1, 0),
+    "deits_b2_p500": lambda: wl.deits(2, 500),
+    "deits_b4_p900": lambda: wl.deits(4, 900),
+    "deits_b1_p800": lambda: wl.deits(1, 800),
+    "empty_and_full": lambda: wl.custom(B=5, N=197, H=6, lengths=[0, 197, 1, 0, 64], seed=3),
+    "n5_golden_like": lambda: wl.custom(B=3, N=5, H=2, lengths=[3, 0, 3], keep_kind="uniform",
+                                        seed=4),
+    "n1": lambda: wl.custom(B=5, N=1, H=1, lengths=[1, 0, 1, 1, 0], seed=5),
+    "tile_edges": lambda: wl.custom(B=6, N=129, H=3, lengths=[63, 64, 65, 128, 129, 16], seed=6),
+    "n577_two": lambda: wl.custom(B=2, N=577, H=2, lengths=[577, 2], seed=7),
+    "f32_odd": lambda: wl.custom(B=3, N=70, H=2, lengths=[70, 33, 5], dtype="f32", seed=8),
+}
+SAMPLED = {  # full-size workloads: pack/unpack compared whole, attention on sampled images
+    "deitb384_b32": (lambda: wl.deitb384(32), 6),
+    "deits_b256_p000": (lambda: wl.deits(256, 0), 4),
+    "deits_b256_p500": (lambda: wl.deits(256, 500), 6),
+    "deits_b256_p800": (lambda: wl.deits(256, 800), 8),
+    "deits_b256_p900": (lambda: wl.deits(256, 900), 8),
+}
+
+
+def _oracle_pack(w):
+    return oracle.pack(w.keep, wl.rows(w))
+
+
+def _check_pack(w, g, ref):
+    packed_ref, cu_ref, gather_ref = ref
+    T = int(cu_ref[-1])
+    cu = g["cu"].cpu().numpy()
+    assert (cu == cu_ref).all(), "cu_seqlens differ"
+    gather = g["gather"].cpu().numpy()
+    assert (gather[:T] == gather_ref).all(), "gather_idx differs"
+    assert (gather[T:].view(np.uint32) == np.uint32(0xA5A5A5A5)).all(), "gather tail written"
+    packed = as_numpy_rows(g["packed"])
+    assert (packed[:T].view(np.uint8) == packed_ref.view(np.uint8)).all(), "packed bytes differ"
+    assert (packed[T:].view(np.uint8) == SENTINEL_BYTE).all(), "packed tail written"
+    assert int(g["max"].item()) == int(w.lengths.max())
+
+
+def _oracle_attn_images(w, ref, images):
+    """Oracle attention for the listed images only, from the oracle's own packing."""
+    packed_ref, cu_ref, _ = ref
+    out = {}
+    for b in images:
+        s, e = int(cu_ref[b]), int(cu_ref[b + 1])
+        if e == s:
+            continue
+        q, k, v = wl.split_qkv(packed_ref[s:e], w.C)
+        out[b] = oracle.attn(q, k, v, np.array([0, e - s], np.int32), w.H, w.d, w.scale)
+    return out
+
+
+def _check_attn(w, ref, o_f32, o_bf16, images):
+    cu_ref = ref[1]
+    o32 = o_f32.cpu().numpy().astype(np.float64)
+    o16 = as_numpy_rows(o_bf16)
+    # bf16 output is RNE of the fp32 output (same kernel, epilogue rounding only)
+    rne = o_f32.cpu().to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    T = int(cu_ref[-1])
+    assert (o16[:T] == rne[:T]).all(), "bf16 output is not RNE(fp32 output)"
+    worst = 0.0
+    for b, want in _oracle_attn_images(w, ref, images).items():
+        s, e = int(cu_ref[b]), int(cu_ref[b + 1])
+        err = np.abs(o32[s:e] - want).max()
+        worst = max(worst, err)
+        assert err <= ATOL, "image %d: max abs err %.3g" % (b, err)
+        err16 = np.abs(bf16_bits_to_f64(o16[s:e]) - want) - (ATOL + np.abs(want) * 2.0 ** -8)
+        assert (err16 <= 0).all(), "image %d: bf16 output outside its bound" % b
+    return worst
+
+
+@pytest.mark.parametrize("name", sorted(FULL))
+def test_pack_and_attention_full(name):
+    w = FULL[name]()
+    print("case", name, "B", w.B, "N", w.N, "H", w.H, "T", w.T, flush=True)
+    ref = _oracle_pack(w)
+    g = gpu_pack(w)
+    _check_pack(w, g, ref)
+    o32 = gpu_attn(g["packed"], g["cu"], w, torch.float32)
+    o16 = gpu_attn(g["packed"], g["cu"], w, torch.bfloat16)
+    worst = _check_attn(w, ref, o32, o16, range(w.B))
+    print("max abs err", worst, flush=True)
+    # rows past T are never written
+    T = w.T
+    assert (as_numpy_rows(o32)[T:].view(np.uint8) == SENTINEL_BYTE).all()
+
+
+@pytest.mark.parametrize("name", sorted(SAMPLED))
+def test_pack_and_attention_full_size_sampled(name):
+    make, nsample = SAMPLED[name]
+    w = make()
+    print("case", name, "B", w.B, "N", w.N, "H", w.H, "T", w.T, flush=True)
+    ref = _oracle_pack(w)
+    g = gpu_pack(w)
+    _check_pack(w, g, ref)
+    o32 = gpu_attn(g["packed"], g["cu"], w, torch.float32)
+    o16 = gpu_attn(g["packed"], g["cu"], w, torch.bfloat16)
+    rng = np.random.default_rng(0)
+    images = sorted(set(rng.choice(w.B, size=min(nsample, w.B), replace=False).tolist())
+                    | {0, w.B - 1})
+    worst = _check_attn(w, ref, o32, o16, images)
+    print("max abs err over", images, worst, flush=True)
+    o = o32.cpu().numpy()
+    assert np.isfinite(o[:w.T]).all()
+
+
+def test_keep_bytes_other_than_one_count_as_kept():
+    w = wl.custom(B=4, N=197, H=6, lengths=[40, 100, 1, 197], seed=10)
+    rng = np.random.default_rng(1)
+    w.keep = (w.keep * rng.integers(1, 256, w.keep.shape)).astype(np.uint8)
+    ref = _oracle_pack(w)
+    _check_pack(w, gpu_pack(w), ref)
+
+
+def test_length_one_returns_v_row_exactly():
+    w = wl.custom(B=7, N=33, H=6, lengths=[1] * 7, seed=11)
+    g = gpu_pack(w)
+    o = gpu_attn(g["packed"], g["cu"], w, torch.float32).cpu().numpy()
+    packed_ref, cu_ref, _ = _oracle_pack(w)
+    v = bf16_bits_to_f64(packed_ref[:, 2 * w.C:3 * w.C])
+    assert (o[:w.T].astype(np.float64) == v).all()
+
+
+def test_attention_is_deterministic():
+    w = wl.deitb_ragged(64)
+    g = gpu_pack(w)
+    a = gpu_attn(g["packed"], g["cu"], w, torch.float32)
+    b = gpu_attn(g["packed"], g["cu"], w, torch.float32)
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+def test_max_seqlen_larger_than_needed_changes_nothing():
+    w = wl.deits(4, 800)
+    g = gpu_pack(w)
+    a = gpu_attn(g["packed"], g["cu"], w, torch.float32, max_seqlen=40)
+    b = gpu_attn(g["packed"], g["cu"], w, torch.float32, max_seqlen=197)
+    assert torch.equal(a[:w.T].view(torch.int32), b[:w.T].view(torch.int32))
+
+
+@pytest.mark.parametrize("flags", [0, binding.RAG_UNPACK_ZERO_DROPPED])
+def test_unpack_bit_exact(flags):
+    w = wl.deitb_ragged(64)
+    _, cu_ref, gather_ref = _oracle_pack(w)
+    T = int(cu_ref[-1])
+    rng = np.random.default_rng(12)
+    packed = rng.integers(0, 2 ** 16, size=(w.B * w.N, w.C), dtype=np.uint16)
+    dst0 = np.full((w.B * w.N, w.C), 0xA5A5, dtype=np.uint16)
+    want = oracle.unpack(packed[:T], cu_ref, gather_ref, dst0)
+    if flags:
+        want[w.keep.reshape(-1) == 0] = 0
+    gather_full = np.zeros(w.B * w.N, np.int32)
+    gather_full[:T] = gather_ref
+    dev = lambda a: torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda()
+    dst = dev(dst0.copy())
+    binding.rag_unpack(dev(packed), dev(cu_ref), dev(gather_full), dst, N=w.N, flags=flags)
+    torch.cuda.synchronize()
+    got = dst.cpu().numpy().view(np.uint16)
+    assert (got == want).all()
+
+
+def test_padded_comparator():
+    for w in (wl.deits(4, 800), wl.custom(B=3, N=70, H=2, lengths=[70, 0, 9], dtype="f32", seed=13),
+              wl.deitb384(2)):
+        print("padded case", w.name, flush=True)
+        src = to_gpu_rows(w)
+        keep = torch.from_numpy(w.keep).cuda()
+        C = w.C
+        o = sentinel_like((w.B * w.N, C), torch.float32)
+        binding.rag_attn_padded(src[:, :C], src[:, C:2 * C], src[:, 2 * C:], keep, o, H=w.H,
+                                scale=w.scale)
+        torch.cuda.synchronize()
+        rows = wl.rows(w)
+        q, k, v = wl.split_qkv(rows, C)
+        want = oracle.attn_padded(q, k, v, w.keep, w.H, w.d, w.scale)
+        got = o.cpu().numpy().astype(np.float64)
+        err = np.abs(got - want).max()
+        print("padded max abs err", err, flush=True)
+        assert err <= ATOL
+
+
+def _pipeline_buffers(w, out_dtype):
+    B, N, C = w.B, w.N, w.C
+    bufs = dict(
+        keep=torch.from_numpy(w.keep).cuda(), src=to_gpu_rows(w),
+        packed=sentinel_like((B * N, 3 * C), torch_dtype(w)),
+        cu=sentinel_like((B + 1,), torch.int32), gather=sentinel_like((B * N,), torch.int32),
+        o_packed=sentinel_like((B * N, C), out_dtype), dst=sentinel_like((B * N, C), out_dtype),
+        mx=sentinel_like((1,), torch.int32))
+    return bufs
+
+
+def _make_pipeline(w, bufs, flags=0):
+    return binding.Pipeline(bufs["keep"], bufs["src"], bufs["packed"], bufs["cu"], bufs["gather"],
+                            bufs["o_packed"], bufs["dst"], H=w.H, scale=w.scale,
+                            max_seqlen_dev=bufs["mx"], unpack_flags=flags)
+
+
+@pytest.mark.parametrize("name,out_dtype", [("deits_b256_p800", torch.bfloat16),
+                                            ("tiny", torch.float32),
+                                            ("deitb_ragged_b64", torch.float32)])
+def test_pipeline_graph_replays_match_eager_and_oracle(name, out_dtype):
+    w = {"deits_b256_p800": lambda: wl.deits(256, 800), "tiny": wl.tiny,
+         "deitb_ragged_b64": lambda: wl.deitb_ragged(64)}[name]()
+    print("pipeline case", name, flush=True)
+    bufs = _pipeline_buffers(w, out_dtype)
+    pipe = _make_pipeline(w, bufs)
+    pipe.launch_eager()
+    torch.cuda.synchronize()
+    eager = {k: bufs[k].clone() for k in ("packed", "cu", "gather", "o_packed", "dst", "mx")}
+    for rep in range(3):
+        for k in ("packed", "cu", "gather", "o_packed", "dst"):
+            bufs[k].view(torch.uint8).fill_(SENTINEL_BYTE)
+        torch.cuda.synchronize()
+        pipe.launch()
+        torch.cuda.synchronize()
+        for k, t in eager.items():
+            assert torch.equal(bufs[k].view(torch.uint8), t.view(torch.uint8)), (rep, k)
+        scratch = torch.randn(1 << 20, device="cuda").sum()  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        del scratch
+    # against the oracle
+    ref = _oracle_pack(w)
+    g = dict(cu=bufs["cu"], gather=bufs["gather"], packed=bufs["packed"], max=bufs["mx"])
+    _check_pack(w, g, ref)
+    images = range(w.B) if w.B <= 64 else [0, 1, 77, 128, 255]
+    want = _oracle_attn_images(w, ref, images)
+    dst = as_numpy_rows(bufs["dst"])
+    o_packed = as_numpy_rows(bufs["o_packed"])
+    _, cu_ref, gather_ref = ref
+    T = int(cu_ref[-1])
+    # unpack is a byte copy of the attention output to the kept rows
+    assert (dst[gather_ref].view(np.uint8) == o_packed[:T].view(np.uint8)).all()
+    dropped = np.setdiff1d(np.arange(w.B * w.N), gather_ref)
+    assert (dst[dropped].view(np.uint8) == SENTINEL_BYTE).all()
+    for b, ref_o in want.items():
+        s, e = int(cu_ref[b]), int(cu_ref[b + 1])
+        got = dst[gather_ref[s:e]]
+        got = bf16_bits_to_f64(got) if out_dtype == torch.bfloat16 else got.astype(np.float64)
+        tol = ATOL + (np.abs(ref_o) * 2.0 ** -8 if out_dtype == torch.bfloat16 else 0.0)
+        assert (np.abs(got - ref_o) <= tol).all(), b
+    pipe.close()
+
+
+def test_pipeline_zero_dropped_flag():
+    w = wl.deits(4, 800)
+    bufs = _pipeline_buffers(w, torch.float32)
+    pipe = _make_pipeline(w, bufs, flags=binding.RAG_UNPACK_ZERO_DROPPED)
+    pipe.launch()
+    torch.cuda.synchronize()
+    dst = bufs["dst"].cpu().numpy()
+    assert (dst[w.keep.reshape(-1) == 0] == 0).all()
+    assert np.isfinite(dst).all()
+    pipe.close()
+
+
+def test_dispatch_measurement_runs():
+    w = wl.deits(1, 800)
+    bufs = _pipeline_buffers(w, torch.bfloat16)
+    pipe = _make_pipeline(w, bufs)
+    res = pipe.measure_dispatch(warmup=5, iters=20)
+    for k, v in res.items():
+        assert 0 < v["p10"] <= v["p50"] <= v["p90"] < 1e6, (k, v)
+    pipe.close()
