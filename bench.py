@@ -1,0 +1,365 @@
+#!/usr/bin/env python3
+"""Benchmark of the ragged pack -> attend -> unpack path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step = one whole pass of the path (pack: keep mask -> cu_seqlens, gather
+index, packed rows; ragged attention; unpack) over one batch of synthetic DeiT-S
+tokens (N = 197, H = 6, head dim 64, bf16), launched as one captured HIP graph.
+The headline workload is 80 % token pruning (40 kept tokens per image, CLS
+included) at batch 256, the top of the 1-256 batch range the metric covers.
+
+Printed: one JSON line with packed tokens/s over the timed steps, the attention
+kernel latency, per-kernel HIP-event durations and their HBM roofline
+fractions, the padded comparator, the prune-rate sweep at B in {1, 2, 4, 256},
+the host dispatch floor (measured in C++), and the CPU oracle's throughput on the
+host cores.
+
+Other modes (used under rocprofv3, see profiles/):
+    --kernels-only   run only the timed pipeline steps (no sweep, no oracle)
+    --pmc-calib      run a plain device copy of a known size (counter scale)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+METRIC = "rag_attn latency us + packed tokens/s, DeiT-S 80% prune BS=1-256; HBM/MFMA %"
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--batch", type=int, default=256)
+    ap.add_argument("--prune", type=int, default=800, help="prune rate in thousandths")
+    ap.add_argument("--kernels-only", action="store_true")
+    ap.add_argument("--pmc-calib", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="bound on the oracle's CPU time for cpu_baseline")
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------- buffers
+class Bufs:
+    """Device buffers of one workload, sized to the B*N capacity."""
+
+    def __init__(self, w, out_dtype=None):
+        import torch
+        from ragged_attention_token_amd import binding
+
+        self.w = w
+        B, N, C = w.B, w.N, w.C
+        rows = np.ascontiguousarray(w.qkv.reshape(B * N, 3 * C))
+        if w.dtype == "f32":
+            self.src = torch.from_numpy(rows).cuda()
+        else:
+            self.src = torch.from_numpy(rows.view(np.int16)).view(torch.bfloat16).cuda()
+        out_dtype = out_dtype or self.src.dtype
+        self.keep = torch.from_numpy(w.keep).cuda()
+        self.packed = torch.empty(B * N, 3 * C, dtype=self.src.dtype, device="cuda")
+        self.cu = torch.zeros(B + 1, dtype=torch.int32, device="cuda")
+        self.gather = torch.zeros(B * N, dtype=torch.int32, device="cuda")
+        self.mx = torch.zeros(1, dtype=torch.int32, device="cuda")
+        self.o_packed = torch.empty(B * N, C, dtype=out_dtype, device="cuda")
+        self.dst = torch.zeros(B * N, C, dtype=out_dtype, device="cuda")
+        self.o_pad = torch.empty(B * N, C, dtype=out_dtype, device="cuda")
+        self.pipe = binding.Pipeline(self.keep, self.src, self.packed, self.cu, self.gather,
+                                     self.o_packed, self.dst, H=w.H, scale=w.scale,
+                                     max_seqlen_dev=self.mx)
+        self.binding = binding
+
+    # the three stages and the comparator, each one launch on the current stream
+    def pack(self):
+        self.binding.rag_pack(self.keep, self.src, self.packed, self.cu, self.gather, self.mx)
+
+    def attn(self):
+        C = self.w.C
+        p = self.packed
+        self.binding.rag_attn(p[:, :C], p[:, C:2 * C], p[:, 2 * C:], self.cu, self.w.N,
+                              self.o_packed, H=self.w.H, scale=self.w.scale)
+
+    def unpack(self):
+        self.binding.rag_unpack(self.o_packed, self.cu, self.gather, self.dst, N=self.w.N)
+
+    def padded(self):
+        C = self.w.C
+        s = self.src
+        self.binding.rag_attn_padded(s[:, :C], s[:, C:2 * C], s[:, 2 * C:], self.keep, self.o_pad,
+                                     H=self.w.H, scale=self.w.scale)
+
+
+def event_time_us(fn, iters, per_launch=True):
+    """Average duration of fn() in microseconds from HIP events on the current
+    stream (the stream every launch here goes to).  per_launch: an event pair
+    around each launch; otherwise one pair around `iters` back-to-back launches."""
+    import torch
+
+    st = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    if per_launch:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(iters)]
+        for a, b in evs:
+            a.record(st)
+            fn()
+            b.record(st)
+        torch.cuda.synchronize()
+        times = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+        return {"mean": float(np.mean(times)), "p50": times[len(times) // 2],
+                "p10": times[len(times) // 10], "p90": times[(9 * len(times)) // 10]}
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(st)
+    for _ in range(iters):
+        fn()
+    b.record(st)
+    torch.cuda.synchronize()
+    return {"mean": a.elapsed_time(b) * 1e3 / iters}
+
+
+# ------------------------------------------------------------ algorithmic work
+def algorithmic(w, out_bytes):
+    """Algorithmic bytes per launch of each kernel and attention flops."""
+    T, B, N, C, H, d = w.T, w.B, w.N, w.C, w.H, w.d
+    s_in = w.elem_bytes
+    L = w.lengths.astype(np.int64)
+    attn_flops = int(4 * (L * L).sum() * d * H)
+    return {
+        # keep mask + (read + write) of each kept fused row + gather index + offsets
+        "pack": B * N + T * (2 * 3 * C * s_in + 4) + 4 * (B + 1),
+        # q, k, v rows read once, o rows written once
+        "attn": T * (3 * C * s_in + C * out_bytes),
+        # read + write of each kept output row + gather index + offsets
+        "unpack": T * (2 * C * out_bytes + 4) + 4 * (B + 1),
+        # padded: every position read and written, whatever the prune rate
+        "padded": B * N * (3 * C * s_in + C * out_bytes) + B * N,
+        "attn_flops": attn_flops,
+        "padded_flops": int(4 * B * N * N * d * H),
+    }
+
+
+def source_sha(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic(kernel, workload):
+    """HBM bytes per launch from a committed rocprofv3 PMC summary, or None when
+    none exists or the kernel source changed since the counters were taken."""
+    path = os.path.join(PROFILES, "pmc_%s_%s.txt" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    try:
+        src = os.path.join(ROOT, "ragged_attention_token_amd", "csrc", kv["source_file"])
+        if source_sha(src) != kv["source_sha256"]:
+            return None
+        calib_bytes = float(kv["calib_bytes"])
+        fetch = float(kv["fetch_kib_per_dispatch"]) * calib_bytes / float(kv["calib_fetch_kib"])
+        write = float(kv["write_kib_per_dispatch"]) * calib_bytes / float(kv["calib_write_kib"])
+        return int(round(fetch + write))
+    except (KeyError, ValueError, OSError):
+        return None
+
+
+# ------------------------------------------------------------------- modes
+def pmc_calib():
+    """A plain device-to-device copy of 1 GiB, five times: the known-size
+    reference that scales the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+
+    nbytes = 1 << 30
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calib_copy_bytes_read": nbytes, "calib_copy_bytes_written": nbytes,
+                      "launches": 5}))
+
+
+def cpu_baseline(w, seconds):
+    """The oracle (plain C, fp64, one thread) on the same workload: pack,
+    attention, unpack, repeated until `seconds` of CPU time (at least once)."""
+    import oracle
+    from ragged_attention_token_amd import workloads as wl
+
+    rows = wl.rows(w)
+    dst0 = np.zeros((w.B * w.N, w.C), dtype=np.float64)
+    reps, t_total = 0, 0.0
+    while reps == 0 or (t_total < seconds and reps < 50):
+        t0 = time.perf_counter()
+        packed, cu, gather = oracle.pack(w.keep, rows)
+        q, k, v = wl.split_qkv(packed, w.C)
+        o = oracle.attn(q, k, v, cu, w.H, w.d, w.scale)
+        oracle.unpack(o, cu, gather, dst0)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    return {"value": w.T * reps / t_total, "unit": "packed tokens/s", "cores": 1, "kind": "oracle",
+            "sample": "whole workload (%s, T=%d), %d pass(es) of fp64 pack+attention+unpack in "
+                      "%.1f s on one host thread" % (w.name, w.T, reps, t_total),
+            "seconds_per_pass": t_total / reps,
+            "host_cpu": _cpu_model(), "host_threads_available": len(os.sched_getaffinity(0))}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def sweep(steps):
+    """Prune-rate sweep on the DeiT-S shape: kernel latencies and pipeline time."""
+    import torch
+    from ragged_attention_token_amd import workloads as wl
+
+    out = {}
+    for B in wl.SWEEP_BATCHES:
+        for p in wl.SWEEP_PRUNE_PERMILLE:
+            w = wl.deits(B, p)
+            bf = Bufs(w)
+            bf.pipe.launch()
+            torch.cuda.synchronize()
+            it = max(50, min(steps, 400))
+            rec = {
+                "T": w.T,
+                "pack_us": event_time_us(bf.pack, it)["p50"],
+                "attn_us": event_time_us(bf.attn, it)["p50"],
+                "unpack_us": event_time_us(bf.unpack, it)["p50"],
+                "padded_attn_us": event_time_us(bf.padded, it)["p50"],
+                "graph_pipeline_us": event_time_us(bf.pipe.launch, it, per_launch=False)["mean"],
+            }
+            rec["ragged_pipeline_vs_padded_attn"] = rec["padded_attn_us"] / rec["graph_pipeline_us"]
+            out["B%d_p%03d" % (B, p)] = rec
+            print("sweep B=%d p=%03d: attn %.2f us, graph pipeline %.2f us" %
+                  (B, p, rec["attn_us"], rec["graph_pipeline_us"]), file=sys.stderr, flush=True)
+            del bf
+    return out
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this path has no multi-GPU step (images shard "
+              "across GPUs with no exchange); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    if args.pmc_calib:
+        pmc_calib()
+        return
+    from ragged_attention_token_amd import workloads as wl
+
+    w = wl.deits(args.batch, args.prune)
+    bf = Bufs(w)
+    print("workload %s B=%d N=%d H=%d T=%d" % (w.name, w.B, w.N, w.H, w.T), file=sys.stderr,
+          flush=True)
+
+    # ---- timed region: K whole passes, one graph launch each ------------------
+    for _ in range(args.warmup):
+        bf.pipe.launch()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        bf.pipe.launch()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    tokens_per_s = w.T * args.steps / wall
+    print("timed %d steps: %.3f ms/step" % (args.steps, ms_per_step), file=sys.stderr, flush=True)
+    if args.kernels_only:
+        print(json.dumps({"metric": METRIC, "value": tokens_per_s, "unit": "packed tokens/s",
+                          "ms_per_step": ms_per_step, "steps": args.steps}))
+        return
+
+    # ---- per-kernel durations, HIP events on the launch stream ---------------
+    it = max(100, min(args.steps, 2000))
+    kern = {name: event_time_us(getattr(bf, name), it)
+            for name in ("pack", "attn", "unpack", "padded")}
+    kern_b2b = {name: event_time_us(getattr(bf, name), it, per_launch=False)["mean"]
+                for name in ("pack", "attn", "unpack", "padded")}
+    eager = event_time_us(bf.pipe.launch_eager, it, per_launch=False)["mean"]
+    graph = event_time_us(bf.pipe.launch, it, per_launch=False)["mean"]
+    out_bytes = 2
+    alg = algorithmic(w, out_bytes)
+    per_kernel = {}
+    for name in ("pack", "attn", "unpack", "padded"):
+        us = kern[name]["mean"]
+        per_kernel[name] = {
+            "event_us_mean": us, "event_us_p50": kern[name]["p50"],
+            "back_to_back_us": kern_b2b[name], "alg_bytes": alg[name],
+            "achieved_GBs": alg[name] / us * 1e-3, "hbm_frac": alg[name] / us * 1e-3 / HBM_PEAK_GBS,
+        }
+    per_kernel["attn"]["alg_flops"] = alg["attn_flops"]
+    per_kernel["attn"]["mfma_frac"] = alg["attn_flops"] / kern["attn"]["mean"] * 1e-6 / BF16_PEAK_TFLOPS
+    per_kernel["padded"]["alg_flops"] = alg["padded_flops"]
+    per_kernel["padded"]["mfma_frac"] = alg["padded_flops"] / kern["padded"]["mean"] * 1e-6 / BF16_PEAK_TFLOPS
+    dominant = max(("pack", "attn", "unpack"), key=lambda n: kern[n]["mean"])
+    dk = per_kernel[dominant]
+    roofline = {"bound": "hbm", "kernel": dominant, "achieved": dk["achieved_GBs"],
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dk["achieved_GBs"] / HBM_PEAK_GBS,
+                "traffic": read_traffic(dominant, w.name),
+                "alg_bytes_per_launch": alg[dominant], "event_us": dk["event_us_mean"]}
+
+    # ---- host dispatch floor, measured in C++ (minimal work: one image) -------
+    floor = {}
+    for lab, wf in (("B1_L1", wl.custom(B=1, N=197, H=6, lengths=[1], seed=0, name="floor_l1")),
+                    ("B1_p800", wl.deits(1, 800))):
+        fb = Bufs(wf)
+        floor[lab] = fb.pipe.measure_dispatch(warmup=100, iters=1000)
+        del fb
+
+    res = {
+        "metric": METRIC, "value": tokens_per_s, "unit": "packed tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "%s: DeiT-S layer (N=197, H=6, d=64), 80%% prune (40 kept incl. "
+                               "CLS), B=%d, bf16 in/out, graph-captured pack+attn+unpack" %
+                               (w.name, w.B),
+                   "B": w.B, "N": w.N, "H": w.H, "head_dim": w.d, "kept_per_image": int(w.lengths[0]),
+                   "T": w.T, "seed": w.seed, "generator": "numpy PCG64; " + w.recipe},
+        "rag_attn_latency_us": kern["attn"]["mean"],
+        "roofline": roofline,
+        "kernels": per_kernel,
+        "pipeline_us": {"graph": graph, "eager_3_launches": eager,
+                        "padded_attn_only": kern["padded"]["mean"]},
+        "dispatch_floor_us": floor,
+    }
+    if not args.no_sweep:
+        res["sweep"] = sweep(args.steps)
+    if not args.no_cpu:
+        print("timing the CPU oracle (<= %.0f s)" % args.cpu_seconds, file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()
