@@ -102,7 +102,8 @@ typedef enum rag_dtype {
  *
  * Every output is a plain function of keep and src: bit-exact and the same on
  * every run.  Pointers (keep, src, packed) and strides must be multiples of 16
- * bytes (RAG_ERR_ALIGNMENT); strides must be >= row_bytes.  1 <= B <= RAG_MAX_B,
+ * bytes (RAG_ERR_ALIGNMENT); strides must be >= row_bytes, and max(N, 64) rows
+ * of either stride must span less than 2^31 bytes.  1 <= B <= RAG_MAX_B,
  * 1 <= N <= RAG_MAX_N.
  */
 RAG_API rag_status rag_pack(const uint8_t* keep, int32_t B, int32_t N, const void* src,
@@ -126,7 +127,8 @@ RAG_API rag_status rag_pack(const uint8_t* keep, int32_t B, int32_t N, const voi
  *               bf16 high and low part that the result matches fp32 inputs).
  *   cu_seqlens  int32[B+1], device; non-decreasing, values in [0, total_rows].
  *   max_seqlen  host-side upper bound of max_b L_b (e.g. N).  Sizes the grid;
- *               rows of an image past max_seqlen are not written.
+ *               an image longer than max_seqlen is treated as its first
+ *               max_seqlen rows (later rows are neither attended nor written).
  *   total_rows  capacity of q/k/v/o in rows; cu values are clamped to it.
  *   H, head_dim heads; head_dim must be RAG_HEAD_DIM.
  *   scale       softmax scale (finite), e.g. 1/sqrt(64).
@@ -137,7 +139,8 @@ RAG_API rag_status rag_pack(const uint8_t* keep, int32_t B, int32_t N, const voi
  * softmax; the softmax weights are split into bf16 high + low parts for the
  * P.V product.  Deterministic (no atomics).  Max abs error vs exact fp64
  * attention on the same inputs: <= 2e-3 for F32 output (measured well below).
- * Pointers must be 16-byte aligned and row strides multiples of 16 bytes.
+ * Pointers must be 16-byte aligned and row strides multiples of 16 bytes;
+ * max_seqlen times the widest row stride must stay below 2^31 bytes.
  */
 RAG_API rag_status rag_attn(const void* q, const void* k, const void* v, int64_t q_row_stride,
                             int64_t k_row_stride, int64_t v_row_stride, rag_dtype in_dtype,
@@ -153,8 +156,8 @@ RAG_API rag_status rag_attn(const void* q, const void* k, const void* v, int64_t
  *   dropped tokens are left untouched, unless flags has
  *   RAG_UNPACK_ZERO_DROPPED, in which case they are set to zero bytes.
  *   cu_seqlens / gather_idx as produced by rag_pack (gather values of image b
- *   lie in [b*N, (b+1)*N); others are skipped).  Same alignment rules as
- *   rag_pack.  Bit-exact.
+ *   lie in [b*N, (b+1)*N); others are skipped).  Same alignment and span
+ *   rules as rag_pack.  Bit-exact.
  */
 RAG_API rag_status rag_unpack(const void* packed, int64_t packed_row_stride, int32_t row_bytes,
                               const int32_t* cu_seqlens, const int32_t* gather_idx, int32_t B,

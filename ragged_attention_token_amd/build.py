@@ -3,7 +3,8 @@
     python -m ragged_attention_token_amd.build
 
 Every HIP source is compiled for gfx950 only, with packed-fp32 instruction
-selection switched off (-Xclang -target-feature -Xclang -packed-fp32-ops); the
+selection switched off (-Xclang -target-feature -Xclang -packed-fp32-ops) and
+MFMA operands kept in VGPRs (-mllvm -amdgpu-mfma-vgpr-form); the
 HIP-free validation unit is compiled as plain C++17.  The result lands next to
 this file, where the binding loads it.
 """
@@ -25,6 +26,9 @@ ARCH = "gfx950"
 HIP_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in ordinary VGPRs (no AGPR <-> VGPR copies around
+    # the fp32 softmax updates of the accumulator)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-fvisibility=hidden", "-DRAG_BUILDING_LIBRARY", "-I" + INCLUDE, "-I" + CSRC,
     "-Wall", "-Werror", "-Wno-unused-command-line-argument",
 ]

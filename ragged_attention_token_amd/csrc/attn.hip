@@ -14,19 +14,25 @@
 //     owning 16 query rows.  A 1-D grid is remapped so that consecutive tiles
 //     of one (image, head) land on the same XCD (shared K/V in that L2).
 //     Tiles past an image's length exit at once (grid sized from max_seqlen).
+//   * all global traffic goes through buffer resources whose range ends at the
+//     image's last row: loads past the sequence end return zeros and stores
+//     past it are dropped by the hardware, so no per-lane predicate is needed
+//     and no uninitialised value can reach an MFMA.
 //   * K and V are staged through LDS 64 keys at a time: K row-major, V
-//     transposed (d-major), both zero-filled past the sequence end so that no
-//     uninitialised value can reach an MFMA.
-//   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (fp32 accumulate), so that each
-//     lane holds the scores of ONE query row (lane & 15) for 4 keys per 16-key
-//     block; the row max / row sum need only two cross-lane exchanges.
-//   * online softmax in fp32 with exp2 (scale * log2 e folded into the scores);
-//     the probabilities are split into bf16 high + low parts and
-//     O^T += V^T P^T runs both through the same MFMA, so P is carried to about
-//     16 mantissa bits.  fp32 inputs are split the same way (hi/lo for Q, K, V).
+//     transposed (d-major) so that each lane's MFMA operand is contiguous.
+//   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (fp32 accumulate): each lane
+//     holds the scores of ONE query row (lane & 15) for 4 keys per 16-key
+//     block, so the row max / row sum take two v_permlane{16,32}_swap steps.
+//   * online softmax in fp32 with exp2; masking only in a sequence's last,
+//     partial tile; no rescale on the first tile.  The probabilities are split
+//     into bf16 high + low parts and O^T += V^T P^T runs both through the same
+//     MFMA, so P is carried to about 16 mantissa bits.  fp32 inputs are split
+//     the same way (hi/lo for Q, K, V).
 //   * the probabilities never leave registers: the MFMA result layout of S^T is
 //     used directly as the B operand of the P.V product (keys are a summation
 //     index, so the k-order only has to agree between the two operands).
+//   * the output goes through LDS so that each row segment is written by
+//     consecutive lanes with 16-byte stores.
 #include <hip/hip_runtime.h>
 
 #include "rag_internal.h"
@@ -37,13 +43,15 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kD = 64;        // head dimension
-constexpr int kBM = 64;       // query rows per workgroup
-constexpr int kBN = 64;       // keys per LDS tile
-constexpr int kThreads = 256; // 4 waves x 16 query rows
-constexpr int kKS = 72;       // LDS row stride of the K tile (bf16): 144 B
-constexpr int kVS = 68;       // LDS row stride of the V^T tile (bf16): 136 B
+constexpr int kD = 64;         // head dimension
+constexpr int kBM = 64;        // query rows per workgroup
+constexpr int kBN = 64;        // keys per LDS tile
+constexpr int kThreads = 256;  // 4 waves x 16 query rows
+constexpr int kKS = 72;        // LDS row stride of the K tile (bf16): 144 B
+constexpr int kVS = 68;        // LDS row stride of the V^T tile (bf16): 136 B
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw 32-bit buffer, gfx9 family
 
 struct AttnParams {
     const void* q;
@@ -53,7 +61,7 @@ struct AttnParams {
     int64_t qs, ks, vs, os;  // row strides, elements
     const int32_t* cu;       // ragged
     const uint8_t* keep;     // padded
-    int32_t B, N, H, total_rows, n_qtiles, total_wgs;
+    int32_t B, N, H, total_rows, max_len, n_qtiles, total_wgs;
     float scale_log2;        // scale * log2(e)
 };
 
@@ -62,43 +70,56 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo)
-{
-    hi = static_cast<__bf16>(x);
-    lo = static_cast<__bf16>(x - static_cast<float>(hi));
-}
-
-__device__ __forceinline__ uint32_t pack2(__bf16 a, __bf16 b)
-{
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
-}
-
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Eight consecutive input elements as bf16 (hi) and, for fp32 input, the bf16
-// remainder (lo).  `ok` false gives zeros.
+// Combine a per-lane value over the four 16-lane rows of the wave (lanes l,
+// l^16, l^32, l^48), which hold the same query row.
+__device__ __forceinline__ float row_max(float x)
+{
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float row_sum(float x)
+{
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+__device__ __forceinline__ uint32_t bits(__bf16 x) { return __builtin_bit_cast(uint16_t, x); }
+
+// A buffer resource over [base, base + bytes); accesses outside read zeros /
+// are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
+}
+
+__device__ __forceinline__ u32x4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+// Eight consecutive input elements at byte offset `off` as bf16 (hi) and, for
+// fp32 input, the bf16 remainder x - hi (lo).
 template <bool IN_F32>
-__device__ __forceinline__ void load8(const void* base, int64_t off, bool ok, bf16x8& hi,
-                                      bf16x8& lo)
+__device__ __forceinline__ void load8(__amdgpu_buffer_rsrc_t r, uint32_t off, bf16x8& hi, bf16x8& lo)
 {
     if constexpr (!IN_F32) {
-        if (ok) hi = *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(base) + off);
-        else hi = bf16x8{};
-        lo = bf16x8{};
+        hi = __builtin_bit_cast(bf16x8, ld16(r, off));
     } else {
-        float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-        if (ok) {
-            const float* f = static_cast<const float*>(base) + off;
-            a = *reinterpret_cast<const float4*>(f);
-            b = *reinterpret_cast<const float4*>(f + 4);
-        }
-        const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        const f32x4 a = __builtin_bit_cast(f32x4, ld16(r, off));
+        const f32x4 b = __builtin_bit_cast(f32x4, ld16(r, off + 16));
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            __bf16 h, l;
-            split_bf16(x[e], h, l);
+            const float x = e < 4 ? a[e] : b[e - 4];
+            const __bf16 h = static_cast<__bf16>(x);
             hi[e] = h;
-            lo[e] = l;
+            lo[e] = static_cast<__bf16>(x - static_cast<float>(h));
         }
     }
 }
@@ -107,8 +128,16 @@ template <bool IN_F32, bool OUT_F32, bool PADDED>
 __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
 {
     constexpr int NP = IN_F32 ? 2 : 1;  // bf16 planes: hi (and lo)
-    __shared__ __attribute__((aligned(16))) __bf16 sK[NP][kBN * kKS];
-    __shared__ __attribute__((aligned(16))) __bf16 sVt[NP][kD * kVS];
+    constexpr int ES = IN_F32 ? 4 : 2;  // input element bytes
+    constexpr int OES = OUT_F32 ? 4 : 2;
+    constexpr int K_PLANE = kBN * kKS;   // bf16 elements
+    constexpr int V_PLANE = kD * kVS;
+    constexpr int OUT_ROW = kD * OES + 16;                   // bytes, padded
+    constexpr int SMEM = 2 * (NP * K_PLANE + NP * V_PLANE);  // bytes
+    static_assert(4 * 16 * OUT_ROW <= SMEM, "output staging must fit the tile buffers");
+    __shared__ __attribute__((aligned(16))) char smem[SMEM];
+    __bf16* sK = reinterpret_cast<__bf16*>(smem);
+    __bf16* sVt = sK + NP * K_PLANE;
     __shared__ uint8_t sKeep[kBN];
 
     // ---- which (q-tile, head, image): XCD-aware remap of the 1-D grid -------
@@ -133,58 +162,66 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
         const int s = min(max(p.cu[b], 0), p.total_rows);
         const int e = min(max(p.cu[b + 1], s), p.total_rows);
         row0 = s;
-        L = e - s;
+        L = min(e - s, p.max_len);
     }
     const int q0 = qt * kBM;
     if (q0 >= L) return;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r16 = lane & 15, g = lane >> 4;
-    const int qrow = q0 + wave * 16 + r16;  // query row inside the image
     const bool wave_active = q0 + wave * 16 < L;
     const int64_t hoff = (int64_t)h * kD;
+
+    // Buffer resources covering rows row0 .. row0+L-1 of this head.
+    const uint32_t qsb = (uint32_t)(p.qs * ES), ksb = (uint32_t)(p.ks * ES),
+                   vsb = (uint32_t)(p.vs * ES), osb = (uint32_t)(p.os * OES);
+    const auto rq = make_rsrc(static_cast<const char*>(p.q) + (row0 * p.qs + hoff) * ES,
+                              (uint32_t)(L - 1) * qsb + kD * ES);
+    const auto rk = make_rsrc(static_cast<const char*>(p.k) + (row0 * p.ks + hoff) * ES,
+                              (uint32_t)(L - 1) * ksb + kD * ES);
+    const auto rv = make_rsrc(static_cast<const char*>(p.v) + (row0 * p.vs + hoff) * ES,
+                              (uint32_t)(L - 1) * vsb + kD * ES);
 
     // Q^T as the B operand: lane holds query row r16, d = 8g..8g+7 and 32+8g..
     bf16x8 qh0, qh1, ql0, ql1;
     {
-        const int64_t off = (row0 + qrow) * p.qs + hoff + 8 * g;
-        const bool ok = qrow < L;
-        load8<IN_F32>(p.q, off, ok, qh0, ql0);
-        load8<IN_F32>(p.q, off + 32, ok, qh1, ql1);
+        const uint32_t off = (uint32_t)(q0 + wave * 16 + r16) * qsb + 8 * g * ES;
+        load8<IN_F32>(rq, off, qh0, ql0);
+        load8<IN_F32>(rq, off + 32 * ES, qh1, ql1);
     }
 
     f32x4 acc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
+    const float c = p.scale_log2;
 
     for (int kt = 0; kt < L; kt += kBN) {
         const int nk = min(kBN, L - kt);
-        __syncthreads();  // the previous tile is no longer read
+        if (kt > 0) __syncthreads();  // the previous tile is no longer read
         // ---- stage K (row-major) -------------------------------------------
 #pragma unroll
         for (int j = 0; j < (kBN * kD / 8) / kThreads; ++j) {
             const int ci = tid + j * kThreads;
             const int key = ci >> 3, dg = ci & 7;
             bf16x8 hi, lo;
-            load8<IN_F32>(p.k, (row0 + kt + key) * p.ks + hoff + 8 * dg, key < nk, hi, lo);
-            *reinterpret_cast<bf16x8*>(&sK[0][key * kKS + 8 * dg]) = hi;
-            if constexpr (IN_F32) *reinterpret_cast<bf16x8*>(&sK[NP - 1][key * kKS + 8 * dg]) = lo;
+            load8<IN_F32>(rk, (uint32_t)(kt + key) * ksb + 8 * dg * ES, hi, lo);
+            *reinterpret_cast<bf16x8*>(&sK[key * kKS + 8 * dg]) = hi;
+            if constexpr (IN_F32) *reinterpret_cast<bf16x8*>(&sK[K_PLANE + key * kKS + 8 * dg]) = lo;
         }
         // ---- stage V transposed: thread owns keys 2kp, 2kp+1 and d 8dg..8dg+7
         {
             const int kp = tid >> 3, dg = tid & 7;
-            const int k0 = 2 * kp, k1 = 2 * kp + 1;
+            const uint32_t off = (uint32_t)(kt + 2 * kp) * vsb + 8 * dg * ES;
             bf16x8 h0, l0, h1, l1;
-            load8<IN_F32>(p.v, (row0 + kt + k0) * p.vs + hoff + 8 * dg, k0 < nk, h0, l0);
-            load8<IN_F32>(p.v, (row0 + kt + k1) * p.vs + hoff + 8 * dg, k1 < nk, h1, l1);
+            load8<IN_F32>(rv, off, h0, l0);
+            load8<IN_F32>(rv, off + vsb, h1, l1);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                // keys k0, k1 side by side: one 32-bit LDS store per (d, key pair)
-                const int off = (8 * dg + i) * kVS + k0;
-                *reinterpret_cast<uint32_t*>(&sVt[0][off]) = pack2(h0[i], h1[i]);
+                const int o = (8 * dg + i) * kVS + 2 * kp;
+                *reinterpret_cast<uint32_t*>(&sVt[o]) = bits(h0[i]) | (bits(h1[i]) << 16);
                 if constexpr (IN_F32)
-                    *reinterpret_cast<uint32_t*>(&sVt[NP - 1][off]) = pack2(l0[i], l1[i]);
+                    *reinterpret_cast<uint32_t*>(&sVt[V_PLANE + o]) = bits(l0[i]) | (bits(l1[i]) << 16);
             }
         }
         if constexpr (PADDED) {
@@ -194,50 +231,59 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
         if (!wave_active) continue;
 
         // ---- S^T = K Q^T: block kb holds keys kt+16kb+4g+i (i<4), query r16 --
+        const int nblk = (nk + 15) >> 4;
         f32x4 s[4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-            if (kb * 16 < nk) {
-                const __bf16* kr = &sK[0][(kb * 16 + r16) * kKS + 8 * g];
+            s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (kb < nblk) {
+                const __bf16* kr = &sK[(kb * 16 + r16) * kKS + 8 * g];
                 const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kr);
                 const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kr + 32);
-                f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
-                t = mfma(a0, qh0, t);
-                t = mfma(a1, qh1, t);
+                s[kb] = mfma(a0, qh0, s[kb]);
+                s[kb] = mfma(a1, qh1, s[kb]);
                 if constexpr (IN_F32) {
-                    const __bf16* kl = &sK[NP - 1][(kb * 16 + r16) * kKS + 8 * g];
-                    const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(kl);
-                    const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(kl + 32);
-                    t = mfma(b0, qh0, t);
-                    t = mfma(b1, qh1, t);
-                    t = mfma(a0, ql0, t);
-                    t = mfma(a1, ql1, t);
+                    const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(kr + K_PLANE);
+                    const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(kr + K_PLANE + 32);
+                    s[kb] = mfma(b0, qh0, s[kb]);
+                    s[kb] = mfma(b1, qh1, s[kb]);
+                    s[kb] = mfma(a0, ql0, s[kb]);
+                    s[kb] = mfma(a1, ql1, s[kb]);
                 }
-                s[kb] = t;
-            } else {
-                s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
         }
 
         // ---- online softmax (fp32, base 2) ----------------------------------
-        float mloc = -INFINITY;
+        // x = scale*log2(e)*s; keys past the tile (or dropped, padded) -> -inf.
+        if (PADDED || nk < kBN) {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
+            for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int key = kb * 16 + 4 * g + i;
-                bool ok = key < nk;
-                if constexpr (PADDED) ok = ok && sKeep[key] != 0;
-                const float x = ok ? s[kb][i] * p.scale_log2 : -INFINITY;
-                s[kb][i] = x;
-                mloc = fmaxf(mloc, x);
+                for (int i = 0; i < 4; ++i) {
+                    const int key = kb * 16 + 4 * g + i;
+                    bool ok = key < nk;
+                    if constexpr (PADDED) ok = ok && sKeep[key] != 0;
+                    s[kb][i] = ok ? s[kb][i] * c : -INFINITY;
+                }
             }
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) s[kb] *= c;
         }
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+        float mloc = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                           fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+        mloc = fmaxf(mloc, fmaxf(fmaxf(fmaxf(s[2][0], s[2][1]), fmaxf(s[2][2], s[2][3])),
+                                 fmaxf(fmaxf(s[3][0], s[3][1]), fmaxf(s[3][2], s[3][3]))));
+        mloc = row_max(mloc);
         const float m_new = fmaxf(m_run, mloc);
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run - m_use);
+        if (kt > 0) {
+            const float alpha = fast_exp2(m_run - m_use);
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < 4; ++db) acc[db] *= alpha;
+        }
+        m_run = m_new;
         float psum = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
@@ -248,39 +294,33 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
                 psum += e;
             }
         }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) acc[db] *= alpha;
+        l_run += psum;
 
         // ---- O^T += V^T P^T, 32 keys per MFMA ---------------------------------
         // k-slot e of lane group g: e<4 -> key 32c+4g+e, e>=4 -> key 32c+16+4g+e-4;
         // these are exactly the keys of s[2c][e] and s[2c+1][e-4].
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            if (c * 32 < nk) {
+        for (int cc = 0; cc < 2; ++cc) {
+            if (cc * 32 < nk) {
                 bf16x8 ph, pl;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    __bf16 hh, ll;
-                    split_bf16(s[2 * c][e], hh, ll);
+                for (int e = 0; e < 8; ++e) {
+                    const float x = e < 4 ? s[2 * cc][e] : s[2 * cc + 1][e - 4];
+                    const __bf16 hh = static_cast<__bf16>(x);
                     ph[e] = hh;
-                    pl[e] = ll;
-                    split_bf16(s[2 * c + 1][e], hh, ll);
-                    ph[e + 4] = hh;
-                    pl[e + 4] = ll;
+                    pl[e] = static_cast<__bf16>(x - static_cast<float>(hh));
                 }
 #pragma unroll
                 for (int db = 0; db < 4; ++db) {
-                    const int vo = (db * 16 + r16) * kVS + 32 * c + 4 * g;
-                    const bf16x4 v0 = *reinterpret_cast<const bf16x4*>(&sVt[0][vo]);
-                    const bf16x4 v1 = *reinterpret_cast<const bf16x4*>(&sVt[0][vo + 16]);
+                    const int vo = (db * 16 + r16) * kVS + 32 * cc + 4 * g;
+                    const bf16x4 v0 = *reinterpret_cast<const bf16x4*>(&sVt[vo]);
+                    const bf16x4 v1 = *reinterpret_cast<const bf16x4*>(&sVt[vo + 16]);
                     const bf16x8 av = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
                     acc[db] = mfma(av, ph, acc[db]);
                     acc[db] = mfma(av, pl, acc[db]);
                     if constexpr (IN_F32) {
-                        const bf16x4 w0 = *reinterpret_cast<const bf16x4*>(&sVt[NP - 1][vo]);
-                        const bf16x4 w1 = *reinterpret_cast<const bf16x4*>(&sVt[NP - 1][vo + 16]);
+                        const bf16x4 w0 = *reinterpret_cast<const bf16x4*>(&sVt[V_PLANE + vo]);
+                        const bf16x4 w1 = *reinterpret_cast<const bf16x4*>(&sVt[V_PLANE + vo + 16]);
                         const bf16x8 al = __builtin_shufflevector(w0, w1, 0, 1, 2, 3, 4, 5, 6, 7);
                         acc[db] = mfma(al, ph, acc[db]);
                     }
@@ -289,27 +329,37 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
         }
     }
 
+    // ---- epilogue: O = acc / l, staged through LDS for row-contiguous stores --
+    __syncthreads();  // every wave is done with the K / V tiles
     if (!wave_active) return;
-    // ---- epilogue: O = acc / l; lane holds O[r16][16db + 4g + i] --------------
-    float lt = l_run + __shfl_xor(l_run, 16);
-    lt += __shfl_xor(lt, 32);
+    const float lt = row_sum(l_run);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    if (qrow >= L) return;
-    const int64_t ooff = (row0 + qrow) * p.os + hoff + 4 * g;
+    char* so = smem + wave * 16 * OUT_ROW;
+    // lane holds O[r16][16db + 4g + i]
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
         const f32x4 r = acc[db] * inv;
+        char* dst = so + r16 * OUT_ROW + (16 * db + 4 * g) * OES;
         if constexpr (OUT_F32) {
-            *reinterpret_cast<float4*>(static_cast<float*>(p.o) + ooff + 16 * db) =
-                make_float4(r[0], r[1], r[2], r[3]);
+            *reinterpret_cast<f32x4*>(dst) = r;
         } else {
             bf16x4 o4;
-            o4[0] = static_cast<__bf16>(r[0]);
-            o4[1] = static_cast<__bf16>(r[1]);
-            o4[2] = static_cast<__bf16>(r[2]);
-            o4[3] = static_cast<__bf16>(r[3]);
-            *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(p.o) + ooff + 16 * db) = o4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o4[i] = static_cast<__bf16>(r[i]);
+            *reinterpret_cast<bf16x4*>(dst) = o4;
         }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+    __builtin_amdgcn_wave_barrier();
+    const auto ro = make_rsrc(static_cast<char*>(p.o) + (row0 * p.os + hoff) * OES,
+                              (uint32_t)(L - 1) * osb + kD * OES);
+    constexpr int CHUNKS = kD * OES / 16;  // 16-byte pieces per row: 8 (bf16) or 16 (fp32)
+#pragma unroll
+    for (int j = 0; j < 16 * CHUNKS / 64; ++j) {
+        const int piece = lane + 64 * j;
+        const int r = piece / CHUNKS, cix = piece % CHUNKS;
+        const u32x4 val = *reinterpret_cast<const u32x4*>(so + r * OUT_ROW + 16 * cix);
+        __builtin_amdgcn_raw_buffer_store_b128(val, ro, (uint32_t)(q0 + wave * 16 + r) * osb + 16 * cix, 0, 0);
     }
 }
 
@@ -346,7 +396,8 @@ int launch_attn(const void* q, const void* k, const void* v, int64_t q_row_strid
     p.N = N;
     p.H = H;
     p.total_rows = total_rows;
-    p.n_qtiles = ((padded ? N : max_seqlen) + kBM - 1) / kBM;
+    p.max_len = padded ? N : max_seqlen;
+    p.n_qtiles = (p.max_len + kBM - 1) / kBM;
     p.total_wgs = p.n_qtiles * H * B;
     p.scale_log2 = scale * 1.4426950408889634f;
     hipStream_t st = static_cast<hipStream_t>(stream);

@@ -10,11 +10,16 @@
 //   1. ranks inside image b: the image's N keep bytes are read once; a 64-lane
 //      ballot + popcount gives each kept position its rank, and the kept
 //      positions are listed by rank in LDS;
-//   2. offset of image b = number of kept tokens in images 0..b-1, counted from
-//      16-byte words of the keep mask (each workgroup recounts the prefix, which
-//      is at most B*N bytes and stays in L2; no atomics, no inter-workgroup
-//      waits, so the result is deterministic);
-//   3. copy: 16-byte vector loads and stores, several in flight per lane.
+//   2. the chunk's source rows are requested (four 16-byte loads per lane in
+//      flight), and while they travel:
+//   3. offset of image b = number of kept tokens in images 0..b-1, counted from
+//      16-byte words of the keep mask (each workgroup recounts the prefix, at
+//      most B*N bytes that stay in L2; no atomics and no inter-workgroup waits,
+//      so the result is deterministic);
+//   4. the rows are stored.
+// All row traffic goes through buffer resources: a lane past the chunk's end
+// gets an offset outside the resource, so its load reads zero and its store is
+// dropped by the hardware; no predicated register arrays are needed.
 // An extra workgroup row (b == B) computes max_b L_b when asked for.
 #include <hip/hip_runtime.h>
 
@@ -25,7 +30,12 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 4;                           // 16-byte vectors per lane per batch
+constexpr int kBatch = kThreads * kUnroll;           // vectors per workgroup per batch
+constexpr uint32_t kRsrcWord3 = 0x00020000u;        // raw 32-bit buffer, gfx9 family
+constexpr uint32_t kDropOffset = 0xFFFFFFF0u;       // outside every resource below
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct PackParams {
     const uint8_t* keep;
@@ -49,6 +59,21 @@ struct UnpackParams {
     int32_t B, N, row_vecs, rows, zero_dropped;
 };
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
+}
+
+__device__ __forceinline__ u32x4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+__device__ __forceinline__ void st16(u32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+}
+
 // Number of nonzero bytes in a 32-bit word: bit 7 of each byte of
 // ((w & 0x7f..) + 0x7f..) | w is set exactly when that byte is nonzero, and the
 // addition cannot carry across bytes.
@@ -56,11 +81,6 @@ __device__ __forceinline__ int nonzero_bytes(uint32_t w)
 {
     const uint32_t y = ((w & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | w;
     return __popc(y & 0x80808080u);
-}
-
-__device__ __forceinline__ int nonzero_bytes(uint4 x)
-{
-    return nonzero_bytes(x.x) + nonzero_bytes(x.y) + nonzero_bytes(x.z) + nonzero_bytes(x.w);
 }
 
 __device__ __forceinline__ int wave_sum(int v)
@@ -91,24 +111,24 @@ __device__ __forceinline__ int block_sum(int v, int* red)
     return t;
 }
 
-// Kept tokens in keep[0, nbytes): 16-byte words, kUnroll loads in flight per lane.
+// Kept tokens in keep[0, nbytes): 16-byte words through a buffer resource
+// (words past the range read as zero), eight loads in flight per lane.
 __device__ int count_kept_prefix(const uint8_t* keep, int64_t nbytes, int* red)
 {
     const int tid = threadIdx.x;
-    const int64_t nwords = nbytes >> 4;
-    const uint4* kw = reinterpret_cast<const uint4*>(keep);
+    const uint32_t nwords = (uint32_t)(nbytes >> 4);
+    const auto rk = make_rsrc(keep, nwords << 4);
     int cnt = 0;
-    for (int64_t w0 = tid; w0 < nwords; w0 += (int64_t)kThreads * kUnroll) {
-        uint4 x[kUnroll];
+    for (uint32_t w0 = 0; w0 < nwords; w0 += kThreads * 8) {
+        u32x4 x[8];
 #pragma unroll
-        for (int j = 0; j < kUnroll; ++j) {
-            const int64_t w = w0 + (int64_t)j * kThreads;
-            x[j] = (w < nwords) ? kw[w] : make_uint4(0u, 0u, 0u, 0u);
-        }
+        for (int j = 0; j < 8; ++j) x[j] = ld16(rk, (w0 + tid + j * kThreads) << 4);
 #pragma unroll
-        for (int j = 0; j < kUnroll; ++j) cnt += nonzero_bytes(x[j]);
+        for (int j = 0; j < 8; ++j)
+            cnt += nonzero_bytes(x[j][0]) + nonzero_bytes(x[j][1]) + nonzero_bytes(x[j][2]) +
+                   nonzero_bytes(x[j][3]);
     }
-    const int64_t tail0 = nwords << 4;
+    const uint32_t tail0 = nwords << 4;
     if (tid < nbytes - tail0) cnt += keep[tail0 + tid] != 0;
     return block_sum(cnt, red);
 }
@@ -194,6 +214,25 @@ __device__ void max_length_pass(const PackParams& p, int* cnt, int window, int* 
     }
 }
 
+// Byte offset, inside image b's source rows, of 16-byte vector v of the chunk;
+// a vector past the chunk re-reads the chunk's first row (its store is dropped).
+__device__ __forceinline__ uint32_t pack_src_off(const PackParams& p, const int* pos, int r0,
+                                                 int total, int v)
+{
+    const int vv = v < total ? v : 0;
+    const int r = vv / p.row_vecs;
+    const int col = vv - r * p.row_vecs;
+    return (uint32_t)pos[r0 + r] * (uint32_t)p.src_stride + 16u * col;
+}
+
+__device__ __forceinline__ uint32_t pack_dst_off(const PackParams& p, int total, int v)
+{
+    if (v >= total) return kDropOffset;
+    const int r = v / p.row_vecs;
+    const int col = v - r * p.row_vecs;
+    return (uint32_t)r * (uint32_t)p.packed_stride + 16u * col;
+}
+
 __global__ __launch_bounds__(kThreads) void pack_kernel(PackParams p)
 {
     extern __shared__ int s_pos[];  // max(N, 256) ints
@@ -204,40 +243,40 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(PackParams p)
         if (c == 0) max_length_pass(p, s_pos, max(p.N, kThreads), s_red);
         return;
     }
-    const int L = rank_image(p.keep + (int64_t)b * p.N, p.N, s_pos, s_red);
+    const int64_t img_row0 = (int64_t)b * p.N;
+    const int L = rank_image(p.keep + img_row0, p.N, s_pos, s_red);
     const int r0 = c * p.rows;
     if (c > 0 && r0 >= L) return;  // nothing to copy; chunk 0 still writes cu
-    const int offset = count_kept_prefix(p.keep, (int64_t)b * p.N, s_red);
+    const int nr = max(0, min(p.rows, L - r0));
+    const int total = nr * p.row_vecs;
+
+    // source rows of image b; destination rows are placed once the offset is known
+    const auto rs = make_rsrc(p.src + img_row0 * p.src_stride, (uint32_t)(p.N * p.src_stride));
+    int v = tid;
+    u32x4 x0 = ld16(rs, pack_src_off(p, s_pos, r0, total, v));
+    u32x4 x1 = ld16(rs, pack_src_off(p, s_pos, r0, total, v + kThreads));
+    u32x4 x2 = ld16(rs, pack_src_off(p, s_pos, r0, total, v + 2 * kThreads));
+    u32x4 x3 = ld16(rs, pack_src_off(p, s_pos, r0, total, v + 3 * kThreads));
+
+    const int offset = count_kept_prefix(p.keep, img_row0, s_red);
     if (c == 0 && tid == 0) {
         p.cu[b + 1] = offset + L;
         if (b == 0) p.cu[0] = 0;
     }
-    const int nr = min(p.rows, L - r0);
-    if (nr <= 0) return;
-    const int64_t img_row0 = (int64_t)b * p.N;
     if (tid < nr) p.gather[offset + r0 + tid] = (int32_t)(img_row0 + s_pos[r0 + tid]);
-
-    const int total = nr * p.row_vecs;
-    const int64_t dst_row0 = (int64_t)offset + r0;
-    for (int v0 = tid; v0 < total; v0 += kThreads * kUnroll) {
-        uint4 x[kUnroll];
-        int64_t dst_off[kUnroll];
-#pragma unroll
-        for (int j = 0; j < kUnroll; ++j) {
-            const int v = v0 + j * kThreads;
-            if (v < total) {
-                const int r = v / p.row_vecs;
-                const int col = v - r * p.row_vecs;
-                const int64_t srow = img_row0 + s_pos[r0 + r];
-                x[j] = *reinterpret_cast<const uint4*>(p.src + srow * p.src_stride + col * 16);
-                dst_off[j] = (dst_row0 + r) * p.packed_stride + col * 16;
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < kUnroll; ++j) {
-            if (v0 + j * kThreads < total)
-                *reinterpret_cast<uint4*>(p.packed + dst_off[j]) = x[j];
-        }
+    const auto rd = make_rsrc(p.packed + ((int64_t)offset + r0) * p.packed_stride,
+                              (uint32_t)(nr * p.packed_stride));
+    for (;;) {
+        st16(x0, rd, pack_dst_off(p, total, v));
+        st16(x1, rd, pack_dst_off(p, total, v + kThreads));
+        st16(x2, rd, pack_dst_off(p, total, v + 2 * kThreads));
+        st16(x3, rd, pack_dst_off(p, total, v + 3 * kThreads));
+        v += kBatch;
+        if (v - tid >= total) break;  // uniform: every lane sees the same v - tid
+        x0 = ld16(rs, pack_src_off(p, s_pos, r0, total, v));
+        x1 = ld16(rs, pack_src_off(p, s_pos, r0, total, v + kThreads));
+        x2 = ld16(rs, pack_src_off(p, s_pos, r0, total, v + 2 * kThreads));
+        x3 = ld16(rs, pack_src_off(p, s_pos, r0, total, v + 3 * kThreads));
     }
 }
 
@@ -251,6 +290,7 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackParams p)
     const int64_t end = min(max((int64_t)p.cu[b + 1], start), cap);
     const int L = (int)min(end - start, (int64_t)p.N);
     const int64_t img_row0 = (int64_t)b * p.N;
+    const auto rdst = make_rsrc(p.dst + img_row0 * p.dst_stride, (uint32_t)(p.N * p.dst_stride));
 
     if (p.zero_dropped) {
         const int nwords = (p.N + 31) >> 5;
@@ -264,13 +304,13 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackParams p)
         // this chunk zeroes the dropped positions in [c*rows, c*rows + rows)
         const int n0 = c * p.rows, n1 = min(n0 + p.rows, p.N);
         const int total = (n1 > n0 ? n1 - n0 : 0) * p.row_vecs;
+        const u32x4 zero = {0u, 0u, 0u, 0u};
         for (int v = tid; v < total; v += kThreads) {
             const int r = v / p.row_vecs;
             const int col = v - r * p.row_vecs;
             const int n = n0 + r;
-            if (!((s_kept[n >> 5] >> (n & 31)) & 1u))
-                *reinterpret_cast<uint4*>(p.dst + (img_row0 + n) * p.dst_stride + col * 16) =
-                    make_uint4(0u, 0u, 0u, 0u);
+            const bool dropped = !((s_kept[n >> 5] >> (n & 31)) & 1u);
+            st16(zero, rdst, dropped ? (uint32_t)n * (uint32_t)p.dst_stride + 16u * col : kDropOffset);
         }
     }
 
@@ -278,25 +318,39 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackParams p)
     const int nr = min(p.rows, L - r0);
     if (nr <= 0) return;
     const int total = nr * p.row_vecs;
-    for (int v0 = tid; v0 < total; v0 += kThreads * kUnroll) {
-        uint4 x[kUnroll];
-        int64_t dst_off[kUnroll];
+    const auto rsrc = make_rsrc(p.packed + (start + r0) * p.packed_stride,
+                                (uint32_t)(nr * p.packed_stride));
+    const auto rg = make_rsrc(p.gather + start + r0, (uint32_t)nr * 4u);
+    const uint32_t img0 = (uint32_t)img_row0;
+    // vector v: its packed row r, column col; past the chunk, r >= nr and the
+    // loads through rsrc / rg read zeros while the store gets a dropped offset
+    for (int v = tid; v - tid < total; v += kBatch) {
+        int r[kUnroll], col[kUnroll];
 #pragma unroll
         for (int j = 0; j < kUnroll; ++j) {
-            const int v = v0 + j * kThreads;
-            dst_off[j] = -1;
-            if (v < total) {
-                const int r = v / p.row_vecs;
-                const int col = v - r * p.row_vecs;
-                const int64_t t = start + r0 + r;
-                const int64_t g = (int64_t)p.gather[t] - img_row0;
-                x[j] = *reinterpret_cast<const uint4*>(p.packed + t * p.packed_stride + col * 16);
-                if (g >= 0 && g < p.N) dst_off[j] = (img_row0 + g) * p.dst_stride + col * 16;
-            }
+            r[j] = (v + j * kThreads) / p.row_vecs;
+            col[j] = (v + j * kThreads) - r[j] * p.row_vecs;
         }
+        // all loads first (gather indices, then rows), then the offsets
+        const uint32_t g0 = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rg, 4u * r[0], 0, 0);
+        const uint32_t g1 = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rg, 4u * r[1], 0, 0);
+        const uint32_t g2 = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rg, 4u * r[2], 0, 0);
+        const uint32_t g3 = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rg, 4u * r[3], 0, 0);
+        const u32x4 x0 = ld16(rsrc, (uint32_t)r[0] * (uint32_t)p.packed_stride + 16u * col[0]);
+        const u32x4 x1 = ld16(rsrc, (uint32_t)r[1] * (uint32_t)p.packed_stride + 16u * col[1]);
+        const u32x4 x2 = ld16(rsrc, (uint32_t)r[2] * (uint32_t)p.packed_stride + 16u * col[2]);
+        const u32x4 x3 = ld16(rsrc, (uint32_t)r[3] * (uint32_t)p.packed_stride + 16u * col[3]);
+        const uint32_t gg[kUnroll] = {g0 - img0, g1 - img0, g2 - img0, g3 - img0};
+        uint32_t d[kUnroll];
 #pragma unroll
-        for (int j = 0; j < kUnroll; ++j)
-            if (dst_off[j] >= 0) *reinterpret_cast<uint4*>(p.dst + dst_off[j]) = x[j];
+        for (int j = 0; j < kUnroll; ++j) {
+            const bool ok = v + j * kThreads < total && gg[j] < (uint32_t)p.N;
+            d[j] = ok ? gg[j] * (uint32_t)p.dst_stride + 16u * col[j] : kDropOffset;
+        }
+        st16(x0, rdst, d[0]);
+        st16(x1, rdst, d[1]);
+        st16(x2, rdst, d[2]);
+        st16(x3, rdst, d[3]);
     }
 }
 

@@ -1,6 +1,7 @@
 // rag_validate.cpp -- host-side argument checks and the per-thread error text.
 // No HIP call lives here: every check runs before anything is enqueued, and the
 // unit tests exercise each error path on a machine without a GPU.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -30,10 +31,21 @@ void clear_error() { g_error[0] = '\0'; }
 
 int rows_per_chunk(int32_t row_bytes)
 {
-    int r = 24576 / (row_bytes > 0 ? row_bytes : 1);
+    // one batch of four 16-byte vectors per lane of a 256-lane workgroup
+    int r = 16384 / (row_bytes > 0 ? row_bytes : 1);
     if (r < 1) r = 1;
     if (r > 64) r = 64;
     return r;
+}
+
+// The copy kernels address one image's rows (and one chunk of packed rows)
+// through 32-bit byte offsets.
+static rag_status check_image_span(const char* what, int32_t N, int64_t stride)
+{
+    if ((int64_t)std::max(N, 64) * stride >= ((int64_t)1 << 31))
+        return set_error(RAG_ERR_UNSUPPORTED, "%s: max(N, 64) rows x %lld-byte stride >= 2^31 bytes",
+                         what, (long long)stride);
+    return RAG_OK;
 }
 
 static rag_status check_rows(const char* what, const void* base, int64_t stride, int32_t row_bytes)
@@ -74,7 +86,8 @@ rag_status validate_pack(const uint8_t* keep, int32_t B, int32_t N, const void* 
     if ((s = check_rows("packed", packed, packed_row_stride, row_bytes)) != RAG_OK) return s;
     if (!cu_seqlens || !gather_idx)
         return set_error(RAG_ERR_INVALID_ARG, "cu_seqlens and gather_idx must not be NULL");
-    return RAG_OK;
+    if ((s = check_image_span("src", N, src_row_stride)) != RAG_OK) return s;
+    return check_image_span("packed", N, packed_row_stride);
 }
 
 rag_status validate_unpack(const void* packed, int64_t packed_row_stride, int32_t row_bytes,
@@ -91,7 +104,8 @@ rag_status validate_unpack(const void* packed, int64_t packed_row_stride, int32_
     if ((s = check_rows("dst", dst, dst_row_stride, row_bytes)) != RAG_OK) return s;
     if (!cu_seqlens || !gather_idx)
         return set_error(RAG_ERR_INVALID_ARG, "cu_seqlens and gather_idx must not be NULL");
-    return RAG_OK;
+    if ((s = check_image_span("dst", N, dst_row_stride)) != RAG_OK) return s;
+    return check_image_span("packed", N, packed_row_stride);
 }
 
 static rag_status check_attn_common(const void* q, const void* k, const void* v, int64_t qs,
@@ -123,6 +137,20 @@ static rag_status check_attn_common(const void* q, const void* k, const void* v,
     return RAG_OK;
 }
 
+// The kernels address one image's rows through 32-bit byte offsets: the span
+// of `rows` rows must stay below 2^31 bytes for every operand.
+static rag_status check_span(int64_t rows, int64_t qs, int64_t ks, int64_t vs, int32_t in_dtype,
+                             int64_t os, int32_t out_dtype)
+{
+    const int64_t ie = dtype_bytes(in_dtype), oe = dtype_bytes(out_dtype);
+    const int64_t widest = std::max(std::max(qs, ks) * ie, std::max(vs * ie, os * oe));
+    if (rows * widest >= ((int64_t)1 << 31))
+        return set_error(RAG_ERR_UNSUPPORTED,
+                         "one image spans >= 2^31 bytes (%lld rows x %lld-byte stride)",
+                         (long long)rows, (long long)widest);
+    return RAG_OK;
+}
+
 rag_status validate_attn(const void* q, const void* k, const void* v, int64_t q_row_stride,
                          int64_t k_row_stride, int64_t v_row_stride, int32_t in_dtype,
                          const int32_t* cu_seqlens, int32_t B, int32_t max_seqlen,
@@ -139,7 +167,8 @@ rag_status validate_attn(const void* q, const void* k, const void* v, int64_t q_
     const int64_t qtiles = (max_seqlen + 63) / 64;
     if (qtiles * H * B > INT32_MAX)
         return set_error(RAG_ERR_UNSUPPORTED, "grid ceil(max_seqlen/64)*H*B exceeds int32");
-    return RAG_OK;
+    return check_span(max_seqlen, q_row_stride, k_row_stride, v_row_stride, in_dtype, o_row_stride,
+                      out_dtype);
 }
 
 rag_status validate_attn_padded(const void* q, const void* k, const void* v,
@@ -157,7 +186,8 @@ rag_status validate_attn_padded(const void* q, const void* k, const void* v,
     const int64_t qtiles = (N + 63) / 64;
     if (qtiles * H * B > INT32_MAX)
         return set_error(RAG_ERR_UNSUPPORTED, "grid ceil(N/64)*H*B exceeds int32");
-    return RAG_OK;
+    return check_span(N, q_row_stride, k_row_stride, v_row_stride, in_dtype, o_row_stride,
+                      out_dtype);
 }
 
 rag_status validate_pipeline(const rag_pipeline_desc* d)
