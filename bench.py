@@ -5,7 +5,8 @@
 
 One step = one whole pass of the path (pack: keep mask -> cu_seqlens, gather
 index, packed rows; ragged attention; unpack) over one batch of synthetic DeiT-S
-tokens (N = 197, H = 6, head dim 64, bf16), launched as one captured HIP graph.
+tokens (N = 197, H = 6, head dim 64, bf16), enqueued by one host call (three
+kernel launches from C++; --graph times the captured HIP graph instead).
 The headline workload is 80 % token pruning (40 kept tokens per image, CLS
 included) at batch 256, the top of the 1-256 batch range the metric covers.
 
@@ -24,7 +25,6 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -48,6 +48,7 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--batch", type=int, default=256)
     ap.add_argument("--prune", type=int, default=800, help="prune rate in thousandths")
+    ap.add_argument("--graph", action="store_true", help="time steps as hipGraphLaunch")
     ap.add_argument("--kernels-only", action="store_true")
     ap.add_argument("--pmc-calib", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
@@ -104,34 +105,6 @@ class Bufs:
         s = self.src
         self.binding.rag_attn_padded(s[:, :C], s[:, C:2 * C], s[:, 2 * C:], self.keep, self.o_pad,
                                      H=self.w.H, scale=self.w.scale)
-
-
-def event_time_us(fn, iters, per_launch=True):
-    """Average duration of fn() in microseconds from HIP events on the current
-    stream (the stream every launch here goes to).  per_launch: an event pair
-    around each launch; otherwise one pair around `iters` back-to-back launches."""
-    import torch
-
-    st = torch.cuda.current_stream()
-    torch.cuda.synchronize()
-    if per_launch:
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(iters)]
-        for a, b in evs:
-            a.record(st)
-            fn()
-            b.record(st)
-        torch.cuda.synchronize()
-        times = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
-        return {"mean": float(np.mean(times)), "p50": times[len(times) // 2],
-                "p10": times[len(times) // 10], "p90": times[(9 * len(times)) // 10]}
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(st)
-    for _ in range(iters):
-        fn()
-    b.record(st)
-    torch.cuda.synchronize()
-    return {"mean": a.elapsed_time(b) * 1e3 / iters}
 
 
 # ------------------------------------------------------------ algorithmic work
@@ -233,7 +206,8 @@ def _cpu_model():
 
 
 def sweep(steps):
-    """Prune-rate sweep on the DeiT-S shape: kernel latencies and pipeline time."""
+    """Prune-rate sweep on the DeiT-S shape: per-launch device time of each kernel
+    and of a whole pass (three launches, and one graph launch)."""
     import torch
     from ragged_attention_token_amd import workloads as wl
 
@@ -245,18 +219,14 @@ def sweep(steps):
             bf.pipe.launch()
             torch.cuda.synchronize()
             it = max(50, min(steps, 400))
-            rec = {
-                "T": w.T,
-                "pack_us": event_time_us(bf.pack, it)["p50"],
-                "attn_us": event_time_us(bf.attn, it)["p50"],
-                "unpack_us": event_time_us(bf.unpack, it)["p50"],
-                "padded_attn_us": event_time_us(bf.padded, it)["p50"],
-                "graph_pipeline_us": event_time_us(bf.pipe.launch, it, per_launch=False)["mean"],
-            }
-            rec["ragged_pipeline_vs_padded_attn"] = rec["padded_attn_us"] / rec["graph_pipeline_us"]
+            m = bf.pipe.measure_stages(it)
+            rec = {"T": w.T, "pack_us": m["pack"], "attn_us": m["attn"], "unpack_us": m["unpack"],
+                   "padded_attn_us": m["padded"], "pipeline_us": m["eager_pass"],
+                   "graph_pipeline_us": m["graph_pass"]}
+            rec["ragged_pipeline_vs_padded_attn"] = rec["padded_attn_us"] / rec["pipeline_us"]
             out["B%d_p%03d" % (B, p)] = rec
-            print("sweep B=%d p=%03d: attn %.2f us, graph pipeline %.2f us" %
-                  (B, p, rec["attn_us"], rec["graph_pipeline_us"]), file=sys.stderr, flush=True)
+            print("sweep B=%d p=%03d: attn %.2f us, pipeline %.2f us" %
+                  (B, p, rec["attn_us"], rec["pipeline_us"]), file=sys.stderr, flush=True)
             del bf
     return out
 
@@ -282,13 +252,16 @@ def main():
     print("workload %s B=%d N=%d H=%d T=%d" % (w.name, w.B, w.N, w.H, w.T), file=sys.stderr,
           flush=True)
 
-    # ---- timed region: K whole passes, one graph launch each ------------------
+    # ---- timed region: K whole passes ------------------------------------------
+    # One host call per pass: the three launches from C++ (on ROCm 7.2 this beats
+    # one hipGraphLaunch of the captured pass, which is reported beside it).
+    step = bf.pipe.launch if args.graph else bf.pipe.launch_eager
     for _ in range(args.warmup):
-        bf.pipe.launch()
+        step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        bf.pipe.launch()
+        step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
@@ -299,34 +272,27 @@ def main():
                           "ms_per_step": ms_per_step, "steps": args.steps}))
         return
 
-    # ---- per-kernel durations, HIP events on the launch stream ---------------
-    it = max(100, min(args.steps, 2000))
-    kern = {name: event_time_us(getattr(bf, name), it)
-            for name in ("pack", "attn", "unpack", "padded")}
-    kern_b2b = {name: event_time_us(getattr(bf, name), it, per_launch=False)["mean"]
-                for name in ("pack", "attn", "unpack", "padded")}
-    eager = event_time_us(bf.pipe.launch_eager, it, per_launch=False)["mean"]
-    graph = event_time_us(bf.pipe.launch, it, per_launch=False)["mean"]
+    # ---- per-kernel durations: HIP events on the launch stream around
+    # back-to-back launches issued from C++ (no Python between launches) --------
+    it = max(200, min(args.steps, 2000))
+    st = bf.pipe.measure_stages(it)
     out_bytes = 2
     alg = algorithmic(w, out_bytes)
     per_kernel = {}
     for name in ("pack", "attn", "unpack", "padded"):
-        us = kern[name]["mean"]
-        per_kernel[name] = {
-            "event_us_mean": us, "event_us_p50": kern[name]["p50"],
-            "back_to_back_us": kern_b2b[name], "alg_bytes": alg[name],
-            "achieved_GBs": alg[name] / us * 1e-3, "hbm_frac": alg[name] / us * 1e-3 / HBM_PEAK_GBS,
-        }
+        us = st[name]
+        per_kernel[name] = {"us": us, "alg_bytes": alg[name], "achieved_GBs": alg[name] / us * 1e-3,
+                            "hbm_frac": alg[name] / us * 1e-3 / HBM_PEAK_GBS}
     per_kernel["attn"]["alg_flops"] = alg["attn_flops"]
-    per_kernel["attn"]["mfma_frac"] = alg["attn_flops"] / kern["attn"]["mean"] * 1e-6 / BF16_PEAK_TFLOPS
+    per_kernel["attn"]["mfma_frac"] = alg["attn_flops"] / st["attn"] * 1e-6 / BF16_PEAK_TFLOPS
     per_kernel["padded"]["alg_flops"] = alg["padded_flops"]
-    per_kernel["padded"]["mfma_frac"] = alg["padded_flops"] / kern["padded"]["mean"] * 1e-6 / BF16_PEAK_TFLOPS
-    dominant = max(("pack", "attn", "unpack"), key=lambda n: kern[n]["mean"])
+    per_kernel["padded"]["mfma_frac"] = alg["padded_flops"] / st["padded"] * 1e-6 / BF16_PEAK_TFLOPS
+    dominant = max(("pack", "attn", "unpack"), key=lambda n: st[n])
     dk = per_kernel[dominant]
     roofline = {"bound": "hbm", "kernel": dominant, "achieved": dk["achieved_GBs"],
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dk["achieved_GBs"] / HBM_PEAK_GBS,
                 "traffic": read_traffic(dominant, w.name),
-                "alg_bytes_per_launch": alg[dominant], "event_us": dk["event_us_mean"]}
+                "alg_bytes_per_launch": alg[dominant], "launch_us": dk["us"]}
 
     # ---- host dispatch floor, measured in C++ (minimal work: one image) -------
     floor = {}
@@ -342,15 +308,16 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "%s: DeiT-S layer (N=197, H=6, d=64), 80%% prune (40 kept incl. "
-                               "CLS), B=%d, bf16 in/out, graph-captured pack+attn+unpack" %
+                               "CLS), B=%d, bf16 in/out, pack+attn+unpack" %
                                (w.name, w.B),
                    "B": w.B, "N": w.N, "H": w.H, "head_dim": w.d, "kept_per_image": int(w.lengths[0]),
                    "T": w.T, "seed": w.seed, "generator": "numpy PCG64; " + w.recipe},
-        "rag_attn_latency_us": kern["attn"]["mean"],
+        "rag_attn_latency_us": st["attn"],
         "roofline": roofline,
         "kernels": per_kernel,
-        "pipeline_us": {"graph": graph, "eager_3_launches": eager,
-                        "padded_attn_only": kern["padded"]["mean"]},
+        "pipeline_us": {"eager_3_launches": st["eager_pass"], "graph": st["graph_pass"],
+                        "padded_attn_only": st["padded"],
+                        "ragged_pass_vs_padded_attn": st["padded"] / st["eager_pass"]},
         "dispatch_floor_us": floor,
     }
     if not args.no_sweep:

@@ -238,6 +238,20 @@ RAG_API void rag_pipeline_destroy(rag_pipeline* p);
 RAG_API rag_status rag_measure_dispatch(rag_pipeline* p, int32_t warmup, int32_t iters,
                                         double* out_us, void* stream);
 
+/*
+ * Device time per launch, in microseconds, of each stage of the pipeline's
+ * workload: HIP events on `stream` around `iters` back-to-back launches (after
+ * iters/10 unmeasured ones), divided by `iters`.  Launches come from C++, so the
+ * figure is the kernel's duration plus the hardware's launch-to-launch gap,
+ * with no host overhead when the kernel outlasts its own enqueue.
+ *   [0] rag_pack  [1] rag_attn  [2] rag_unpack  [3] rag_attn_padded (on the
+ *   desc's src / keep, output into dst)  [4] pack + attn + unpack as three
+ *   launches  [5] the same pass as one hipGraphLaunch
+ * `out_us` must hold RAG_STAGES_N doubles.  Overwrites the desc's buffers.
+ */
+#define RAG_STAGES_N 6
+RAG_API rag_status rag_measure_stages(rag_pipeline* p, int32_t iters, double* out_us, void* stream);
+
 /* Message for the last non-OK status returned on the calling thread. */
 RAG_API const char* rag_last_error(void);
 /* Static name of a status code. */

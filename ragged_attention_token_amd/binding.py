@@ -25,11 +25,13 @@ RAG_DTYPE_BF16 = 1
 RAG_UNPACK_ZERO_DROPPED = 1
 RAG_HEAD_DIM = 64
 RAG_FLOOR_N = 21
+RAG_STAGES_N = 6
 
 #: Every symbol include/rag.h declares.
 EXPORTS = ("rag_pack", "rag_attn", "rag_unpack", "rag_attn_padded", "rag_pipeline_create",
            "rag_pipeline_launch", "rag_pipeline_launch_eager", "rag_pipeline_destroy",
-           "rag_measure_dispatch", "rag_last_error", "rag_status_string", "rag_version")
+           "rag_measure_dispatch", "rag_measure_stages", "rag_last_error", "rag_status_string",
+           "rag_version")
 
 _lib = None
 
@@ -81,12 +83,14 @@ def load(path: str = LIB_PATH):
     lib.rag_pipeline_destroy.argtypes = [vp]
     lib.rag_pipeline_destroy.restype = None
     lib.rag_measure_dispatch.argtypes = [vp, i32, i32, ctypes.POINTER(ctypes.c_double), vp]
+    lib.rag_measure_stages.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_double), vp]
     lib.rag_last_error.restype = ctypes.c_char_p
     lib.rag_status_string.argtypes = [i32]
     lib.rag_status_string.restype = ctypes.c_char_p
     lib.rag_version.restype = i32
     for name in ("rag_pack", "rag_attn", "rag_unpack", "rag_attn_padded", "rag_pipeline_create",
-                 "rag_pipeline_launch", "rag_pipeline_launch_eager", "rag_measure_dispatch"):
+                 "rag_pipeline_launch", "rag_pipeline_launch_eager", "rag_measure_dispatch",
+                 "rag_measure_stages"):
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -284,6 +288,12 @@ class Pipeline:
         for i, k in enumerate(keys):
             res[k] = {"p10": out[3 * i], "p50": out[3 * i + 1], "p90": out[3 * i + 2]}
         return res
+
+    def measure_stages(self, iters: int = 500, stream=None) -> dict:
+        """Device microseconds per launch of each stage (see rag_measure_stages)."""
+        out = (ctypes.c_double * RAG_STAGES_N)()
+        _check(load().rag_measure_stages(self._h, int(iters), out, _stream(stream)))
+        return dict(zip(("pack", "attn", "unpack", "padded", "eager_pass", "graph_pass"), list(out)))
 
     def close(self) -> None:
         if getattr(self, "_h", None) is not None and self._h.value:

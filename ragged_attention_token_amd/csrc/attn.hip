@@ -10,16 +10,19 @@
 // dropped keys masked out.
 //
 // Kernel design (ours, for gfx950; the pages' Triton kernel is not followed):
-//   * one workgroup = one (q-tile of 64 rows, head, image); 4 wave64s, each
-//     owning 16 query rows.  A 1-D grid is remapped so that consecutive tiles
-//     of one (image, head) land on the same XCD (shared K/V in that L2).
-//     Tiles past an image's length exit at once (grid sized from max_seqlen).
+//   * one workgroup = one (head, image, q-tile of 64 rows); 4 wave64s, each
+//     owning 16 query rows.  The q-tile is the slowest grid dimension, so the
+//     first tile of every (image, head) is dispatched before the later tiles,
+//     most of which exit at once for pruned sequences (the grid is sized from
+//     the host-side max_seqlen, never from device data).
 //   * all global traffic goes through buffer resources whose range ends at the
 //     image's last row: loads past the sequence end return zeros and stores
 //     past it are dropped by the hardware, so no per-lane predicate is needed
 //     and no uninitialised value can reach an MFMA.
 //   * K and V are staged through LDS 64 keys at a time: K row-major, V
-//     transposed (d-major) so that each lane's MFMA operand is contiguous.
+//     transposed (d-major) so that each lane's MFMA operand is contiguous.  The
+//     next tile's loads are issued into registers before the current tile is
+//     computed, so a long sequence costs one memory round trip, not one per tile.
 //   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (fp32 accumulate): each lane
 //     holds the scores of ONE query row (lane & 15) for 4 keys per 16-key
 //     block, so the row max / row sum take two v_permlane{16,32}_swap steps.
@@ -61,7 +64,7 @@ struct AttnParams {
     int64_t qs, ks, vs, os;  // row strides, elements
     const int32_t* cu;       // ragged
     const uint8_t* keep;     // padded
-    int32_t B, N, H, total_rows, max_len, n_qtiles, total_wgs;
+    int32_t B, N, H, total_rows, max_len, n_qtiles;
     float scale_log2;        // scale * log2(e)
 };
 
@@ -140,18 +143,12 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
     __bf16* sVt = sK + NP * K_PLANE;
     __shared__ uint8_t sKeep[kBN];
 
-    // ---- which (q-tile, head, image): XCD-aware remap of the 1-D grid -------
-    // Workgroup ids are dealt round-robin to the 8 XCDs; give each XCD a
-    // contiguous run of work items so one (image, head)'s tiles share an L2.
-    const int id = blockIdx.x;
-    const int total = p.total_wgs;
-    const int xcd = id & 7, slot = id >> 3;
-    const int per = total >> 3, extra = total & 7;
-    const int w = (xcd < extra ? xcd * (per + 1) : extra * (per + 1) + (xcd - extra) * per) + slot;
-    const int qt = w % p.n_qtiles;
-    const int bh = w / p.n_qtiles;
-    const int h = bh % p.H;
-    const int b = bh / p.H;
+    // ---- which (head, image, q-tile): a 3-D grid with the q-tile slowest, so
+    // that the first q-tile of every (image, head) -- the only one most pruned
+    // sequences have -- is dispatched before any tile that will exit at once.
+    const int h = blockIdx.x;
+    const int b = blockIdx.y;
+    const int qt = blockIdx.z;
 
     int64_t row0;
     int L;
@@ -196,34 +193,42 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
     float m_run = -INFINITY, l_run = 0.f;
     const float c = p.scale_log2;
 
+    // Registers carrying one K/V tile from global memory to LDS: this thread's
+    // two 16-byte K pieces and its V key pair (hi and, for fp32 input, lo).
+    bf16x8 kh0, kl0, kh1, kl1, vh0, vl0, vh1, vl1;
+    const int k_key0 = tid >> 3, k_key1 = (tid + kThreads) >> 3, k_dg = tid & 7;
+    const int v_kp = tid >> 3, v_dg = tid & 7;
+    auto fetch = [&](int kt) {
+        load8<IN_F32>(rk, (uint32_t)(kt + k_key0) * ksb + 8 * k_dg * ES, kh0, kl0);
+        load8<IN_F32>(rk, (uint32_t)(kt + k_key1) * ksb + 8 * k_dg * ES, kh1, kl1);
+        const uint32_t off = (uint32_t)(kt + 2 * v_kp) * vsb + 8 * v_dg * ES;
+        load8<IN_F32>(rv, off, vh0, vl0);
+        load8<IN_F32>(rv, off + vsb, vh1, vl1);
+    };
+    auto stash = [&]() {
+        // K row-major; V transposed with keys 2kp, 2kp+1 side by side (one
+        // 32-bit LDS store per (d, key pair))
+        *reinterpret_cast<bf16x8*>(&sK[k_key0 * kKS + 8 * k_dg]) = kh0;
+        *reinterpret_cast<bf16x8*>(&sK[k_key1 * kKS + 8 * k_dg]) = kh1;
+        if constexpr (IN_F32) {
+            *reinterpret_cast<bf16x8*>(&sK[K_PLANE + k_key0 * kKS + 8 * k_dg]) = kl0;
+            *reinterpret_cast<bf16x8*>(&sK[K_PLANE + k_key1 * kKS + 8 * k_dg]) = kl1;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int o = (8 * v_dg + i) * kVS + 2 * v_kp;
+            *reinterpret_cast<uint32_t*>(&sVt[o]) = bits(vh0[i]) | (bits(vh1[i]) << 16);
+            if constexpr (IN_F32)
+                *reinterpret_cast<uint32_t*>(&sVt[V_PLANE + o]) = bits(vl0[i]) | (bits(vl1[i]) << 16);
+        }
+    };
+    fetch(0);
+
     for (int kt = 0; kt < L; kt += kBN) {
         const int nk = min(kBN, L - kt);
         if (kt > 0) __syncthreads();  // the previous tile is no longer read
-        // ---- stage K (row-major) -------------------------------------------
-#pragma unroll
-        for (int j = 0; j < (kBN * kD / 8) / kThreads; ++j) {
-            const int ci = tid + j * kThreads;
-            const int key = ci >> 3, dg = ci & 7;
-            bf16x8 hi, lo;
-            load8<IN_F32>(rk, (uint32_t)(kt + key) * ksb + 8 * dg * ES, hi, lo);
-            *reinterpret_cast<bf16x8*>(&sK[key * kKS + 8 * dg]) = hi;
-            if constexpr (IN_F32) *reinterpret_cast<bf16x8*>(&sK[K_PLANE + key * kKS + 8 * dg]) = lo;
-        }
-        // ---- stage V transposed: thread owns keys 2kp, 2kp+1 and d 8dg..8dg+7
-        {
-            const int kp = tid >> 3, dg = tid & 7;
-            const uint32_t off = (uint32_t)(kt + 2 * kp) * vsb + 8 * dg * ES;
-            bf16x8 h0, l0, h1, l1;
-            load8<IN_F32>(rv, off, h0, l0);
-            load8<IN_F32>(rv, off + vsb, h1, l1);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int o = (8 * dg + i) * kVS + 2 * kp;
-                *reinterpret_cast<uint32_t*>(&sVt[o]) = bits(h0[i]) | (bits(h1[i]) << 16);
-                if constexpr (IN_F32)
-                    *reinterpret_cast<uint32_t*>(&sVt[V_PLANE + o]) = bits(l0[i]) | (bits(l1[i]) << 16);
-            }
-        }
+        stash();
+        if (kt + kBN < L) fetch(kt + kBN);  // in flight while this tile is computed
         if constexpr (PADDED) {
             if (tid < kBN) sKeep[tid] = (tid < nk) ? p.keep[row0 + kt + tid] : 0;
         }
@@ -366,7 +371,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
 template <bool IN_F32, bool OUT_F32>
 void launch_variant(const AttnParams& p, bool padded, hipStream_t st)
 {
-    const dim3 grid(p.total_wgs), block(kThreads);
+    const dim3 grid(p.H, p.B, p.n_qtiles), block(kThreads);
     if (padded)
         hipLaunchKernelGGL((attn_kernel<IN_F32, OUT_F32, true>), grid, block, 0, st, p);
     else
@@ -398,7 +403,6 @@ int launch_attn(const void* q, const void* k, const void* v, int64_t q_row_strid
     p.total_rows = total_rows;
     p.max_len = padded ? N : max_seqlen;
     p.n_qtiles = (p.max_len + kBM - 1) / kBM;
-    p.total_wgs = p.n_qtiles * H * B;
     p.scale_log2 = scale * 1.4426950408889634f;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool in_f32 = in_dtype == RAG_DTYPE_F32, out_f32 = out_dtype == RAG_DTYPE_F32;

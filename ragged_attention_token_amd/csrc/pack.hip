@@ -6,7 +6,9 @@
 // token rows into one flat buffer.  Unpack (same section, write-back): copy each
 // packed row back to its batch position.
 //
-// One launch each.  Workgroup (c, b) serves rows [c*R, c*R + R) of image b:
+// One launch each.  Workgroup (b, c) serves rows [c*R, c*R + R) of image b; the
+// chunk index is the slowest grid dimension, so the first chunk of every image
+// is dispatched before the later chunks, which pruned images mostly lack.
 //   1. ranks inside image b: the image's N keep bytes are read once; a 64-lane
 //      ballot + popcount gives each kept position its rank, and the kept
 //      positions are listed by rank in LDS;
@@ -238,7 +240,7 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(PackParams p)
     extern __shared__ int s_pos[];  // max(N, 256) ints
     __shared__ int s_red[kWaves];
     const int tid = threadIdx.x;
-    const int b = blockIdx.y, c = blockIdx.x;
+    const int b = blockIdx.x, c = blockIdx.y;  // chunk slowest: chunk 0 of every image first
     if (b == p.B) {
         if (c == 0) max_length_pass(p, s_pos, max(p.N, kThreads), s_red);
         return;
@@ -284,7 +286,7 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackParams p)
 {
     __shared__ uint32_t s_kept[RAG_MAX_N / 32];
     const int tid = threadIdx.x;
-    const int b = blockIdx.y, c = blockIdx.x;
+    const int b = blockIdx.x, c = blockIdx.y;  // chunk slowest: chunk 0 of every image first
     const int64_t cap = (int64_t)p.B * p.N;
     const int64_t start = min(max((int64_t)p.cu[b], (int64_t)0), cap);
     const int64_t end = min(max((int64_t)p.cu[b + 1], start), cap);
@@ -374,7 +376,7 @@ int launch_pack(const uint8_t* keep, int32_t B, int32_t N, const void* src,
     p.N = N;
     p.row_vecs = row_bytes / 16;
     p.rows = rows_per_chunk(row_bytes);
-    const dim3 grid((N + p.rows - 1) / p.rows, B + (max_seqlen_dev ? 1 : 0));
+    const dim3 grid(B + (max_seqlen_dev ? 1 : 0), (N + p.rows - 1) / p.rows);
     const size_t lds = sizeof(int) * (size_t)max(N, kThreads);
     hipLaunchKernelGGL(pack_kernel, grid, dim3(kThreads), lds, static_cast<hipStream_t>(stream), p);
     return (int)hipGetLastError();
@@ -396,7 +398,7 @@ int launch_unpack(const void* packed, int64_t packed_row_stride, int32_t row_byt
     p.row_vecs = row_bytes / 16;
     p.rows = rows_per_chunk(row_bytes);
     p.zero_dropped = (flags & RAG_UNPACK_ZERO_DROPPED) ? 1 : 0;
-    const dim3 grid((N + p.rows - 1) / p.rows, B);
+    const dim3 grid(B, (N + p.rows - 1) / p.rows);
     hipLaunchKernelGGL(unpack_kernel, grid, dim3(kThreads), 0, static_cast<hipStream_t>(stream), p);
     return (int)hipGetLastError();
 }

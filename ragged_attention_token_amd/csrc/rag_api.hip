@@ -267,3 +267,80 @@ extern "C" RAG_API rag_status rag_measure_dispatch(rag_pipeline* p, int32_t warm
     if ((s = time_calls(padded, st, warmup, iters, out_us + 18, nullptr)) != RAG_OK) return s;
     return RAG_OK;
 }
+
+extern "C" RAG_API rag_status rag_measure_stages(rag_pipeline* p, int32_t iters, double* out_us,
+                                                 void* stream)
+{
+    if (!p || !out_us || iters < 1)
+        return set_error(RAG_ERR_INVALID_ARG, "bad arguments to rag_measure_stages");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const rag_pipeline_desc& d = p->d;
+    const int64_t C = (int64_t)d.H * d.head_dim;
+    const int in_es = rag::dtype_bytes(d.in_dtype), out_es = rag::dtype_bytes(d.out_dtype);
+    const int32_t in_row = (int32_t)(3 * C * in_es), out_row = (int32_t)(C * out_es);
+    const char* pk = static_cast<const char*>(d.packed);
+    const int64_t ps = d.packed_row_stride / in_es;
+    const char* sr = static_cast<const char*>(d.src);
+    const int64_t ss = d.src_row_stride / in_es;
+    const int32_t maxlen = d.max_seqlen ? d.max_seqlen : d.N;
+    auto pack = [&]() {
+        return hip_status(rag::launch_pack(d.keep, d.B, d.N, d.src, d.src_row_stride, in_row,
+                                           d.packed, d.packed_row_stride, d.cu_seqlens,
+                                           d.gather_idx, d.max_seqlen_dev, st),
+                          "pack");
+    };
+    auto attn = [&]() {
+        return hip_status(rag::launch_attn(pk, pk + C * in_es, pk + 2 * C * in_es, ps, ps, ps,
+                                           d.in_dtype, d.cu_seqlens, nullptr, d.B, 0, maxlen,
+                                           d.B * d.N, d.H, d.scale, d.o_packed,
+                                           d.o_packed_row_stride / out_es, d.out_dtype, false, st),
+                          "attn");
+    };
+    auto unpack = [&]() {
+        return hip_status(rag::launch_unpack(d.o_packed, d.o_packed_row_stride, out_row,
+                                             d.cu_seqlens, d.gather_idx, d.B, d.N, d.dst,
+                                             d.dst_row_stride, d.unpack_flags, st),
+                          "unpack");
+    };
+    auto padded = [&]() {
+        return hip_status(rag::launch_attn(sr, sr + C * in_es, sr + 2 * C * in_es, ss, ss, ss,
+                                           d.in_dtype, nullptr, d.keep, d.B, d.N, d.N, d.B * d.N,
+                                           d.H, d.scale, d.dst, d.dst_row_stride / out_es,
+                                           d.out_dtype, true, st),
+                          "padded");
+    };
+    auto eager = [&]() { return enqueue_pass(d, st); };
+    auto graph = [&]() { return rag_pipeline_launch(p, st); };
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    rag_status s = hip_status((int)hipEventCreate(&e0), "hipEventCreate");
+    if (s == RAG_OK) s = hip_status((int)hipEventCreate(&e1), "hipEventCreate");
+    auto timed = [&](auto fn, double* out) -> rag_status {
+        const int warm = std::max(1, iters / 10);
+        for (int i = 0; i < warm; ++i)
+            if (rag_status r = fn(); r != RAG_OK) return r;
+        if (rag_status r = hip_status((int)hipEventRecord(e0, st), "hipEventRecord"); r != RAG_OK)
+            return r;
+        for (int i = 0; i < iters; ++i)
+            if (rag_status r = fn(); r != RAG_OK) return r;
+        if (rag_status r = hip_status((int)hipEventRecord(e1, st), "hipEventRecord"); r != RAG_OK)
+            return r;
+        if (rag_status r = hip_status((int)hipEventSynchronize(e1), "hipEventSynchronize");
+            r != RAG_OK)
+            return r;
+        float ms = 0.f;
+        if (rag_status r = hip_status((int)hipEventElapsedTime(&ms, e0, e1), "hipEventElapsedTime");
+            r != RAG_OK)
+            return r;
+        *out = (double)ms * 1e3 / iters;
+        return RAG_OK;
+    };
+    if (s == RAG_OK) s = timed(pack, out_us + 0);
+    if (s == RAG_OK) s = timed(attn, out_us + 1);
+    if (s == RAG_OK) s = timed(unpack, out_us + 2);
+    if (s == RAG_OK) s = timed(padded, out_us + 3);
+    if (s == RAG_OK) s = timed(eager, out_us + 4);
+    if (s == RAG_OK) s = timed(graph, out_us + 5);
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    return s;
+}

@@ -159,14 +159,13 @@ rag_status validate_attn(const void* q, const void* k, const void* v, int64_t q_
 {
     if (B < 1 || B > RAG_MAX_B) return set_error(RAG_ERR_INVALID_ARG, "B=%d out of [1, %d]", B, RAG_MAX_B);
     if (max_seqlen < 1) return set_error(RAG_ERR_INVALID_ARG, "max_seqlen=%d must be >= 1", max_seqlen);
+    if (max_seqlen > 65535 * 64)
+        return set_error(RAG_ERR_UNSUPPORTED, "max_seqlen=%d exceeds %d", max_seqlen, 65535 * 64);
     if (total_rows < 0) return set_error(RAG_ERR_INVALID_ARG, "total_rows=%d must be >= 0", total_rows);
     if (!cu_seqlens) return set_error(RAG_ERR_INVALID_ARG, "cu_seqlens is NULL");
     rag_status s = check_attn_common(q, k, v, q_row_stride, k_row_stride, v_row_stride, in_dtype,
                                      H, head_dim, scale, o, o_row_stride, out_dtype);
     if (s != RAG_OK) return s;
-    const int64_t qtiles = (max_seqlen + 63) / 64;
-    if (qtiles * H * B > INT32_MAX)
-        return set_error(RAG_ERR_UNSUPPORTED, "grid ceil(max_seqlen/64)*H*B exceeds int32");
     return check_span(max_seqlen, q_row_stride, k_row_stride, v_row_stride, in_dtype, o_row_stride,
                       out_dtype);
 }
@@ -183,9 +182,6 @@ rag_status validate_attn_padded(const void* q, const void* k, const void* v,
     s = check_attn_common(q, k, v, q_row_stride, k_row_stride, v_row_stride, in_dtype, H, head_dim,
                           scale, o, o_row_stride, out_dtype);
     if (s != RAG_OK) return s;
-    const int64_t qtiles = (N + 63) / 64;
-    if (qtiles * H * B > INT32_MAX)
-        return set_error(RAG_ERR_UNSUPPORTED, "grid ceil(N/64)*H*B exceeds int32");
     return check_span(N, q_row_stride, k_row_stride, v_row_stride, in_dtype, o_row_stride,
                       out_dtype);
 }

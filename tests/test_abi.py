@@ -92,8 +92,8 @@ def attn(lib, q=A, k=A, v=A, qs=1152, ks=1152, vs=1152, dt=BF16, cu=A, B=4, maxl
     (dict(os_=386), ALIGN, "o base"),         # 386 fp32 = 1544 B, not a multiple of 16
     (dict(scale=float("inf")), INVALID, "scale"),
     (dict(scale=float("nan")), INVALID, "scale"),
-    (dict(B=65535, H=3000, maxlen=8192, qs=192000, ks=192000, vs=192000, os_=192000),
-     UNSUPPORTED, "grid"),
+    (dict(maxlen=65535 * 64 + 1), UNSUPPORTED, "max_seqlen"),
+    (dict(maxlen=8192, qs=192000, ks=192000, vs=192000, os_=192000), UNSUPPORTED, "2^31"),
 ])
 def test_attn_rejects(lib, kwargs, status, needle):
     assert attn(lib, **kwargs) == status

@@ -288,3 +288,14 @@ def test_dispatch_measurement_runs():
     for k, v in res.items():
         assert 0 < v["p10"] <= v["p50"] <= v["p90"] < 1e6, (k, v)
     pipe.close()
+
+
+def test_stage_measurement_runs():
+    w = wl.deits(4, 800)
+    bufs = _pipeline_buffers(w, torch.bfloat16)
+    pipe = _make_pipeline(w, bufs)
+    res = pipe.measure_stages(iters=20)
+    assert set(res) == {"pack", "attn", "unpack", "padded", "eager_pass", "graph_pass"}
+    for k, v in res.items():
+        assert 0 < v < 1e5, (k, v)
+    pipe.close()
