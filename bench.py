@@ -123,6 +123,8 @@ def algorithmic(w, out_bytes):
         "unpack": T * (2 * C * out_bytes + 4) + 4 * (B + 1),
         # padded: every position read and written, whatever the prune rate
         "padded": B * N * (3 * C * s_in + C * out_bytes) + B * N,
+        # the whole pass as one gathered launch: keep mask, kept q/k/v rows in, o rows out
+        "fused": B * N + T * (3 * C * s_in + C * out_bytes),
         "attn_flops": attn_flops,
         "padded_flops": int(4 * B * N * N * d * H),
     }
@@ -222,7 +224,7 @@ def sweep(steps):
             m = bf.pipe.measure_stages(it)
             rec = {"T": w.T, "pack_us": m["pack"], "attn_us": m["attn"], "unpack_us": m["unpack"],
                    "padded_attn_us": m["padded"], "pipeline_us": m["eager_pass"],
-                   "graph_pipeline_us": m["graph_pass"]}
+                   "graph_pipeline_us": m["graph_pass"], "fused_pass_us": m["fused_pass"]}
             rec["ragged_pipeline_vs_padded_attn"] = rec["padded_attn_us"] / rec["pipeline_us"]
             out["B%d_p%03d" % (B, p)] = rec
             print("sweep B=%d p=%03d: attn %.2f us, pipeline %.2f us" %
@@ -279,7 +281,8 @@ def main():
     out_bytes = 2
     alg = algorithmic(w, out_bytes)
     per_kernel = {}
-    for name in ("pack", "attn", "unpack", "padded"):
+    st["fused"] = st["fused_pass"]
+    for name in ("pack", "attn", "unpack", "padded", "fused"):
         us = st[name]
         per_kernel[name] = {"us": us, "alg_bytes": alg[name], "achieved_GBs": alg[name] / us * 1e-3,
                             "hbm_frac": alg[name] / us * 1e-3 / HBM_PEAK_GBS}
@@ -316,8 +319,10 @@ def main():
         "roofline": roofline,
         "kernels": per_kernel,
         "pipeline_us": {"eager_3_launches": st["eager_pass"], "graph": st["graph_pass"],
-                        "padded_attn_only": st["padded"],
-                        "ragged_pass_vs_padded_attn": st["padded"] / st["eager_pass"]},
+                        "fused_1_launch": st["fused_pass"], "padded_attn_only": st["padded"],
+                        "ragged_pass_vs_padded_attn": st["padded"] / st["eager_pass"],
+                        "fused_pass_vs_padded_attn": st["padded"] / st["fused_pass"]},
+        "fused_tokens_per_s": w.T / st["fused_pass"] * 1e6,
         "dispatch_floor_us": floor,
     }
     if not args.no_sweep:

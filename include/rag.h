@@ -180,6 +180,28 @@ RAG_API rag_status rag_attn_padded(const void* q, const void* k, const void* v,
                                    void* stream);
 
 /*
+ * rag_attn_gathered -- the whole pack -> attend -> unpack pass as ONE launch
+ * ([blog-method]: the same three steps; [abstract]: per-call dispatch is what
+ * hides the pruning savings, so fewer launches is the point).
+ *
+ * Same attention as rag_attn, but on the unpacked [B, N] layout: the rows of
+ * image b are b*N + n_0, b*N + n_1, ... where n_0 < n_1 < ... are the positions
+ * with keep[b*N + n] != 0, read straight from q/k/v (no packed copy), and O is
+ * written straight to those rows of o (no unpack copy).  No cu_seqlens or
+ * gather index is built: each workgroup ranks its image's keep row in LDS.
+ * Bit-for-bit equal to rag_pack -> rag_attn -> rag_unpack on the kept rows
+ * (same kernel arithmetic, same key order).  Rows of dropped tokens are left
+ * untouched, or zeroed with RAG_UNPACK_ZERO_DROPPED.  keep [B, N] uint8 (any
+ * alignment); other arguments as in rag_attn_padded.
+ */
+RAG_API rag_status rag_attn_gathered(const uint8_t* keep, int32_t B, int32_t N, const void* q,
+                                     const void* k, const void* v, int64_t q_row_stride,
+                                     int64_t k_row_stride, int64_t v_row_stride,
+                                     rag_dtype in_dtype, int32_t H, int32_t head_dim, float scale,
+                                     void* o, int64_t o_row_stride, rag_dtype out_dtype,
+                                     uint32_t flags, void* stream);
+
+/*
  * A whole pack -> attend -> unpack pass captured once into a HIP graph, so
  * that each later pass costs one host call ([abstract]: the per-call host
  * dispatch cost is what hides the pruning savings).
@@ -218,6 +240,9 @@ RAG_API rag_status rag_pipeline_create(const rag_pipeline_desc* desc, rag_pipeli
 RAG_API rag_status rag_pipeline_launch(rag_pipeline* p, void* stream);
 /* Enqueue the same pass as three plain launches (no graph) on `stream`. */
 RAG_API rag_status rag_pipeline_launch_eager(rag_pipeline* p, void* stream);
+/* Enqueue the same pass as one rag_attn_gathered launch on `stream`: src -> dst
+ * directly (packed, o_packed, cu_seqlens and gather_idx are not touched). */
+RAG_API rag_status rag_pipeline_launch_fused(rag_pipeline* p, void* stream);
 /* Free the graph; the caller must make sure no launch is still pending. */
 RAG_API void rag_pipeline_destroy(rag_pipeline* p);
 
@@ -232,9 +257,11 @@ RAG_API void rag_pipeline_destroy(rag_pipeline* p);
  *   [12..14] pack + attn + unpack as three launches: launch + sync
  *   [15..17] the same pass as one hipGraphLaunch: launch + sync
  *   [18..20] rag_attn_padded on the desc's src/keep (output into dst): launch + sync
+ *   [21..23] the pass as one rag_attn_gathered launch: launch + sync
+ *   [24..26] rag_attn_gathered: host enqueue only
  * `out_us` must hold RAG_FLOOR_N doubles.  Runs work on `stream`.
  */
-#define RAG_FLOOR_N 21
+#define RAG_FLOOR_N 27
 RAG_API rag_status rag_measure_dispatch(rag_pipeline* p, int32_t warmup, int32_t iters,
                                         double* out_us, void* stream);
 
@@ -246,10 +273,11 @@ RAG_API rag_status rag_measure_dispatch(rag_pipeline* p, int32_t warmup, int32_t
  * with no host overhead when the kernel outlasts its own enqueue.
  *   [0] rag_pack  [1] rag_attn  [2] rag_unpack  [3] rag_attn_padded (on the
  *   desc's src / keep, output into dst)  [4] pack + attn + unpack as three
- *   launches  [5] the same pass as one hipGraphLaunch
+ *   launches  [5] the same pass as one hipGraphLaunch  [6] the same pass as one
+ *   rag_attn_gathered launch
  * `out_us` must hold RAG_STAGES_N doubles.  Overwrites the desc's buffers.
  */
-#define RAG_STAGES_N 6
+#define RAG_STAGES_N 7
 RAG_API rag_status rag_measure_stages(rag_pipeline* p, int32_t iters, double* out_us, void* stream);
 
 /* Message for the last non-OK status returned on the calling thread. */

@@ -24,12 +24,13 @@ RAG_DTYPE_F32 = 0
 RAG_DTYPE_BF16 = 1
 RAG_UNPACK_ZERO_DROPPED = 1
 RAG_HEAD_DIM = 64
-RAG_FLOOR_N = 21
-RAG_STAGES_N = 6
+RAG_FLOOR_N = 27
+RAG_STAGES_N = 7
 
 #: Every symbol include/rag.h declares.
-EXPORTS = ("rag_pack", "rag_attn", "rag_unpack", "rag_attn_padded", "rag_pipeline_create",
-           "rag_pipeline_launch", "rag_pipeline_launch_eager", "rag_pipeline_destroy",
+EXPORTS = ("rag_pack", "rag_attn", "rag_unpack", "rag_attn_padded", "rag_attn_gathered",
+           "rag_pipeline_create", "rag_pipeline_launch", "rag_pipeline_launch_eager",
+           "rag_pipeline_launch_fused", "rag_pipeline_destroy",
            "rag_measure_dispatch", "rag_measure_stages", "rag_last_error", "rag_status_string",
            "rag_version")
 
@@ -77,7 +78,10 @@ def load(path: str = LIB_PATH):
     lib.rag_unpack.argtypes = [vp, i64, i32, vp, vp, i32, i32, vp, i64, u32, vp]
     lib.rag_attn_padded.argtypes = [vp, vp, vp, i64, i64, i64, i32, vp, i32, i32, i32, i32, f32,
                                     vp, i64, i32, vp]
+    lib.rag_attn_gathered.argtypes = [vp, i32, i32, vp, vp, vp, i64, i64, i64, i32, i32, i32, f32,
+                                      vp, i64, i32, u32, vp]
     lib.rag_pipeline_create.argtypes = [ctypes.POINTER(PipelineDesc), ctypes.POINTER(vp)]
+    lib.rag_pipeline_launch_fused.argtypes = [vp, vp]
     lib.rag_pipeline_launch.argtypes = [vp, vp]
     lib.rag_pipeline_launch_eager.argtypes = [vp, vp]
     lib.rag_pipeline_destroy.argtypes = [vp]
@@ -88,9 +92,9 @@ def load(path: str = LIB_PATH):
     lib.rag_status_string.argtypes = [i32]
     lib.rag_status_string.restype = ctypes.c_char_p
     lib.rag_version.restype = i32
-    for name in ("rag_pack", "rag_attn", "rag_unpack", "rag_attn_padded", "rag_pipeline_create",
-                 "rag_pipeline_launch", "rag_pipeline_launch_eager", "rag_measure_dispatch",
-                 "rag_measure_stages"):
+    for name in ("rag_pack", "rag_attn", "rag_unpack", "rag_attn_padded", "rag_attn_gathered",
+                 "rag_pipeline_create", "rag_pipeline_launch", "rag_pipeline_launch_eager",
+                 "rag_pipeline_launch_fused", "rag_measure_dispatch", "rag_measure_stages"):
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -234,6 +238,28 @@ def rag_attn_padded(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, keep: tor
                                   _stream(stream)))
 
 
+def rag_attn_gathered(keep: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                      o: torch.Tensor, H: int, scale: float, flags: int = 0,
+                      head_dim: int = RAG_HEAD_DIM, stream=None) -> None:
+    """Pack + attend + unpack in one launch: q/k/v/o rows b*N + n of the [B, N]
+    layout; attention over each image's kept rows, written to those rows of o."""
+    qp, qs = _rows(q, "q")
+    kp, ks = _rows(k, "k")
+    vp, vs = _rows(v, "v")
+    op, os_ = _rows(o, "o")
+    _gpu(keep, "keep")
+    if keep.dtype != torch.uint8 or keep.dim() != 2 or not keep.is_contiguous():
+        raise ValueError("keep must be a contiguous uint8 [B, N] tensor")
+    B, N = keep.shape
+    if min(q.shape[0], k.shape[0], v.shape[0], o.shape[0]) < B * N:
+        raise ValueError("q/k/v/o need B*N rows")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    _check(load().rag_attn_gathered(keep.data_ptr(), B, N, qp, kp, vp, qs, ks, vs, _dtype_code(q),
+                                    int(H), int(head_dim), float(scale), op, os_, _dtype_code(o),
+                                    int(flags), _stream(stream)))
+
+
 class Pipeline:
     """pack -> attend -> unpack captured once into a HIP graph.
 
@@ -279,11 +305,15 @@ class Pipeline:
     def launch_eager(self, stream=None) -> None:
         _check(load().rag_pipeline_launch_eager(self._h, _stream(stream)))
 
+    def launch_fused(self, stream=None) -> None:
+        _check(load().rag_pipeline_launch_fused(self._h, _stream(stream)))
+
     def measure_dispatch(self, warmup: int = 100, iters: int = 1000, stream=None) -> dict:
         out = (ctypes.c_double * RAG_FLOOR_N)()
         _check(load().rag_measure_dispatch(self._h, int(warmup), int(iters), out, _stream(stream)))
         keys = ["empty_roundtrip", "empty_enqueue", "attn_roundtrip", "attn_enqueue",
-                "eager3_roundtrip", "graph_roundtrip", "padded_roundtrip"]
+                "eager3_roundtrip", "graph_roundtrip", "padded_roundtrip", "fused_roundtrip",
+                "fused_enqueue"]
         res = {}
         for i, k in enumerate(keys):
             res[k] = {"p10": out[3 * i], "p50": out[3 * i + 1], "p90": out[3 * i + 2]}
@@ -293,7 +323,8 @@ class Pipeline:
         """Device microseconds per launch of each stage (see rag_measure_stages)."""
         out = (ctypes.c_double * RAG_STAGES_N)()
         _check(load().rag_measure_stages(self._h, int(iters), out, _stream(stream)))
-        return dict(zip(("pack", "attn", "unpack", "padded", "eager_pass", "graph_pass"), list(out)))
+        return dict(zip(("pack", "attn", "unpack", "padded", "eager_pass", "graph_pass",
+                         "fused_pass"), list(out)))
 
     def close(self) -> None:
         if getattr(self, "_h", None) is not None and self._h.value:

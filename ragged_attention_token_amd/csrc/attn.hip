@@ -38,6 +38,7 @@
 //     consecutive lanes with 16-byte stores.
 #include <hip/hip_runtime.h>
 
+#include "rag_device.h"
 #include "rag_internal.h"
 
 namespace rag {
@@ -46,7 +47,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+using dev::u32x4;
 
 constexpr int kD = 64;         // head dimension
 constexpr int kBM = 64;        // query rows per workgroup
@@ -54,7 +55,13 @@ constexpr int kBN = 64;        // keys per LDS tile
 constexpr int kThreads = 256;  // 4 waves x 16 query rows
 constexpr int kKS = 72;        // LDS row stride of the K tile (bf16): 144 B
 constexpr int kVS = 68;        // LDS row stride of the V^T tile (bf16): 136 B
-constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw 32-bit buffer, gfx9 family
+
+// Where the rows of one image live.
+enum Layout : int {
+    kRagged = 0,    // packed rows cu[b] .. cu[b+1]-1
+    kPadded = 1,    // all N rows b*N .. b*N+N-1, dropped keys masked
+    kGathered = 2,  // the kept rows of b*N .. b*N+N-1, found from the keep row
+};
 
 struct AttnParams {
     const void* q;
@@ -63,8 +70,8 @@ struct AttnParams {
     void* o;
     int64_t qs, ks, vs, os;  // row strides, elements
     const int32_t* cu;       // ragged
-    const uint8_t* keep;     // padded
-    int32_t B, N, H, total_rows, max_len, n_qtiles;
+    const uint8_t* keep;     // padded and gathered
+    int32_t B, N, H, total_rows, max_len, n_qtiles, zero_dropped;
     float scale_log2;        // scale * log2(e)
 };
 
@@ -95,17 +102,9 @@ __device__ __forceinline__ float row_sum(float x)
 
 __device__ __forceinline__ uint32_t bits(__bf16 x) { return __builtin_bit_cast(uint16_t, x); }
 
-// A buffer resource over [base, base + bytes); accesses outside read zeros /
-// are dropped.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
-}
-
-__device__ __forceinline__ u32x4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t off)
-{
-    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-}
+using dev::kDropOffset;
+using dev::ld16;
+using dev::make_rsrc;
 
 // Eight consecutive input elements at byte offset `off` as bf16 (hi) and, for
 // fp32 input, the bf16 remainder x - hi (lo).
@@ -127,9 +126,28 @@ __device__ __forceinline__ void load8(__amdgpu_buffer_rsrc_t r, uint32_t off, bf
     }
 }
 
-template <bool IN_F32, bool OUT_F32, bool PADDED>
+// Gathered layout with RAG_UNPACK_ZERO_DROPPED: head h of every dropped row of
+// the image is set to zero (one workgroup per (image, head) does it).
+template <bool OUT_F32>
+__device__ void zero_dropped_head(const AttnParams& p, int64_t row0, int h)
+{
+    constexpr int OES = OUT_F32 ? 4 : 2;
+    constexpr int CHUNKS = kD * OES / 16;
+    const uint32_t osb = (uint32_t)(p.os * OES);
+    const auto ro = make_rsrc(static_cast<char*>(p.o) + (row0 * p.os + (int64_t)h * kD) * OES,
+                              (uint32_t)(p.N - 1) * osb + kD * OES);
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    for (int i = threadIdx.x; i < p.N * CHUNKS; i += kThreads) {
+        const int n = i / CHUNKS, cix = i - n * CHUNKS;
+        if (p.keep[row0 + n] == 0) dev::st16(zero, ro, (uint32_t)n * osb + 16 * cix);
+    }
+}
+
+template <bool IN_F32, bool OUT_F32, int LAYOUT>
 __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
 {
+    constexpr bool PADDED = LAYOUT == kPadded;
+    constexpr bool GATHERED = LAYOUT == kGathered;
     constexpr int NP = IN_F32 ? 2 : 1;  // bf16 planes: hi (and lo)
     constexpr int ES = IN_F32 ? 4 : 2;  // input element bytes
     constexpr int OES = OUT_F32 ? 4 : 2;
@@ -142,6 +160,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
     __bf16* sK = reinterpret_cast<__bf16*>(smem);
     __bf16* sVt = sK + NP * K_PLANE;
     __shared__ uint8_t sKeep[kBN];
+    extern __shared__ int s_pos[];  // gathered: the image's kept positions by rank (N ints)
+    __shared__ int s_wsum[4];
 
     // ---- which (head, image, q-tile): a 3-D grid with the q-tile slowest, so
     // that the first q-tile of every (image, head) -- the only one most pruned
@@ -155,6 +175,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
     if constexpr (PADDED) {
         row0 = (int64_t)b * p.N;
         L = p.N;
+    } else if constexpr (GATHERED) {
+        row0 = (int64_t)b * p.N;
+        L = dev::rank_kept(p.keep + row0, p.N, s_pos, s_wsum);
+        if (p.zero_dropped && qt == 0) zero_dropped_head<OUT_F32>(p, row0, h);
     } else {
         const int s = min(max(p.cu[b], 0), p.total_rows);
         const int e = min(max(p.cu[b + 1], s), p.total_rows);
@@ -169,20 +193,28 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
     const bool wave_active = q0 + wave * 16 < L;
     const int64_t hoff = (int64_t)h * kD;
 
-    // Buffer resources covering rows row0 .. row0+L-1 of this head.
+    // Buffer resources covering this head's rows of the image: rows row0 ..
+    // row0+span-1 (the L packed rows, or all N batch rows when gathered).
+    const int span = GATHERED ? p.N : L;
     const uint32_t qsb = (uint32_t)(p.qs * ES), ksb = (uint32_t)(p.ks * ES),
                    vsb = (uint32_t)(p.vs * ES), osb = (uint32_t)(p.os * OES);
     const auto rq = make_rsrc(static_cast<const char*>(p.q) + (row0 * p.qs + hoff) * ES,
-                              (uint32_t)(L - 1) * qsb + kD * ES);
+                              (uint32_t)(span - 1) * qsb + kD * ES);
     const auto rk = make_rsrc(static_cast<const char*>(p.k) + (row0 * p.ks + hoff) * ES,
-                              (uint32_t)(L - 1) * ksb + kD * ES);
+                              (uint32_t)(span - 1) * ksb + kD * ES);
     const auto rv = make_rsrc(static_cast<const char*>(p.v) + (row0 * p.vs + hoff) * ES,
-                              (uint32_t)(L - 1) * vsb + kD * ES);
+                              (uint32_t)(span - 1) * vsb + kD * ES);
+    // Byte offset of the row of rank `r` (the r-th row of the sequence); rows
+    // past the sequence fall outside the resource (zeros in, stores dropped).
+    auto row_off = [&](int r, uint32_t stride) -> uint32_t {
+        if constexpr (GATHERED) return r < L ? (uint32_t)s_pos[r] * stride : kDropOffset;
+        else return (uint32_t)r * stride;
+    };
 
     // Q^T as the B operand: lane holds query row r16, d = 8g..8g+7 and 32+8g..
     bf16x8 qh0, qh1, ql0, ql1;
     {
-        const uint32_t off = (uint32_t)(q0 + wave * 16 + r16) * qsb + 8 * g * ES;
+        const uint32_t off = row_off(q0 + wave * 16 + r16, qsb) + 8 * g * ES;
         load8<IN_F32>(rq, off, qh0, ql0);
         load8<IN_F32>(rq, off + 32 * ES, qh1, ql1);
     }
@@ -199,11 +231,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
     const int k_key0 = tid >> 3, k_key1 = (tid + kThreads) >> 3, k_dg = tid & 7;
     const int v_kp = tid >> 3, v_dg = tid & 7;
     auto fetch = [&](int kt) {
-        load8<IN_F32>(rk, (uint32_t)(kt + k_key0) * ksb + 8 * k_dg * ES, kh0, kl0);
-        load8<IN_F32>(rk, (uint32_t)(kt + k_key1) * ksb + 8 * k_dg * ES, kh1, kl1);
-        const uint32_t off = (uint32_t)(kt + 2 * v_kp) * vsb + 8 * v_dg * ES;
-        load8<IN_F32>(rv, off, vh0, vl0);
-        load8<IN_F32>(rv, off + vsb, vh1, vl1);
+        load8<IN_F32>(rk, row_off(kt + k_key0, ksb) + 8 * k_dg * ES, kh0, kl0);
+        load8<IN_F32>(rk, row_off(kt + k_key1, ksb) + 8 * k_dg * ES, kh1, kl1);
+        load8<IN_F32>(rv, row_off(kt + 2 * v_kp, vsb) + 8 * v_dg * ES, vh0, vl0);
+        load8<IN_F32>(rv, row_off(kt + 2 * v_kp + 1, vsb) + 8 * v_dg * ES, vh1, vl1);
     };
     auto stash = [&]() {
         // K row-major; V transposed with keys 2kp, 2kp+1 side by side (one
@@ -357,25 +388,28 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
     __builtin_amdgcn_wave_barrier();
     const auto ro = make_rsrc(static_cast<char*>(p.o) + (row0 * p.os + hoff) * OES,
-                              (uint32_t)(L - 1) * osb + kD * OES);
+                              (uint32_t)(span - 1) * osb + kD * OES);
     constexpr int CHUNKS = kD * OES / 16;  // 16-byte pieces per row: 8 (bf16) or 16 (fp32)
 #pragma unroll
     for (int j = 0; j < 16 * CHUNKS / 64; ++j) {
         const int piece = lane + 64 * j;
         const int r = piece / CHUNKS, cix = piece % CHUNKS;
         const u32x4 val = *reinterpret_cast<const u32x4*>(so + r * OUT_ROW + 16 * cix);
-        __builtin_amdgcn_raw_buffer_store_b128(val, ro, (uint32_t)(q0 + wave * 16 + r) * osb + 16 * cix, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(val, ro, row_off(q0 + wave * 16 + r, osb) + 16 * cix, 0, 0);
     }
 }
 
 template <bool IN_F32, bool OUT_F32>
-void launch_variant(const AttnParams& p, bool padded, hipStream_t st)
+void launch_variant(const AttnParams& p, int layout, hipStream_t st)
 {
     const dim3 grid(p.H, p.B, p.n_qtiles), block(kThreads);
-    if (padded)
-        hipLaunchKernelGGL((attn_kernel<IN_F32, OUT_F32, true>), grid, block, 0, st, p);
+    if (layout == kPadded)
+        hipLaunchKernelGGL((attn_kernel<IN_F32, OUT_F32, kPadded>), grid, block, 0, st, p);
+    else if (layout == kGathered)
+        hipLaunchKernelGGL((attn_kernel<IN_F32, OUT_F32, kGathered>), grid, block,
+                           sizeof(int) * (size_t)p.N, st, p);
     else
-        hipLaunchKernelGGL((attn_kernel<IN_F32, OUT_F32, false>), grid, block, 0, st, p);
+        hipLaunchKernelGGL((attn_kernel<IN_F32, OUT_F32, kRagged>), grid, block, 0, st, p);
 }
 
 }  // namespace
@@ -384,7 +418,8 @@ int launch_attn(const void* q, const void* k, const void* v, int64_t q_row_strid
                 int64_t k_row_stride, int64_t v_row_stride, int32_t in_dtype,
                 const int32_t* cu_seqlens, const uint8_t* keep, int32_t B, int32_t N,
                 int32_t max_seqlen, int32_t total_rows, int32_t H, float scale, void* o,
-                int64_t o_row_stride, int32_t out_dtype, bool padded, void* stream)
+                int64_t o_row_stride, int32_t out_dtype, int layout, uint32_t flags,
+                void* stream)
 {
     AttnParams p;
     p.q = q;
@@ -401,15 +436,16 @@ int launch_attn(const void* q, const void* k, const void* v, int64_t q_row_strid
     p.N = N;
     p.H = H;
     p.total_rows = total_rows;
-    p.max_len = padded ? N : max_seqlen;
+    p.max_len = layout == kRagged ? max_seqlen : N;
     p.n_qtiles = (p.max_len + kBM - 1) / kBM;
+    p.zero_dropped = (flags & RAG_UNPACK_ZERO_DROPPED) ? 1 : 0;
     p.scale_log2 = scale * 1.4426950408889634f;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool in_f32 = in_dtype == RAG_DTYPE_F32, out_f32 = out_dtype == RAG_DTYPE_F32;
-    if (in_f32 && out_f32) launch_variant<true, true>(p, padded, st);
-    else if (in_f32) launch_variant<true, false>(p, padded, st);
-    else if (out_f32) launch_variant<false, true>(p, padded, st);
-    else launch_variant<false, false>(p, padded, st);
+    if (in_f32 && out_f32) launch_variant<true, true>(p, layout, st);
+    else if (in_f32) launch_variant<true, false>(p, layout, st);
+    else if (out_f32) launch_variant<false, true>(p, layout, st);
+    else launch_variant<false, false>(p, layout, st);
     return (int)hipGetLastError();
 }
 

@@ -25,6 +25,7 @@
 // An extra workgroup row (b == B) computes max_b L_b when asked for.
 #include <hip/hip_runtime.h>
 
+#include "rag_device.h"
 #include "rag_internal.h"
 
 namespace rag {
@@ -34,10 +35,11 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kUnroll = 4;                           // 16-byte vectors per lane per batch
 constexpr int kBatch = kThreads * kUnroll;           // vectors per workgroup per batch
-constexpr uint32_t kRsrcWord3 = 0x00020000u;        // raw 32-bit buffer, gfx9 family
-constexpr uint32_t kDropOffset = 0xFFFFFFF0u;       // outside every resource below
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+using dev::kDropOffset;
+using dev::ld16;
+using dev::make_rsrc;
+using dev::st16;
+using dev::u32x4;
 
 struct PackParams {
     const uint8_t* keep;
@@ -60,21 +62,6 @@ struct UnpackParams {
     int64_t dst_stride;
     int32_t B, N, row_vecs, rows, zero_dropped;
 };
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
-}
-
-__device__ __forceinline__ u32x4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t off)
-{
-    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-}
-
-__device__ __forceinline__ void st16(u32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t off)
-{
-    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
-}
 
 // Number of nonzero bytes in a 32-bit word: bit 7 of each byte of
 // ((w & 0x7f..) + 0x7f..) | w is set exactly when that byte is nonzero, and the
@@ -133,32 +120,6 @@ __device__ int count_kept_prefix(const uint8_t* keep, int64_t nbytes, int* red)
     const uint32_t tail0 = nwords << 4;
     if (tid < nbytes - tail0) cnt += keep[tail0 + tid] != 0;
     return block_sum(cnt, red);
-}
-
-// Lists image b's kept positions by rank into pos[] and returns L_b.
-__device__ int rank_image(const uint8_t* krow, int N, int* pos, int* wsum)
-{
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    int L = 0;
-    for (int base = 0; base < N; base += kThreads) {
-        const int n = base + tid;
-        const bool kept = n < N && krow[n] != 0;
-        const uint64_t m = __ballot(kept);
-        const int below = __popcll(m & ((1ull << lane) - 1ull));
-        if (lane == 0) wsum[wave] = __popcll(m);
-        __syncthreads();
-        int before = 0, total = 0;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            const int x = wsum[w];
-            before += (w < wave) ? x : 0;
-            total += x;
-        }
-        if (kept) pos[L + before + below] = n;
-        L += total;
-        __syncthreads();
-    }
-    return L;
 }
 
 // max_b L_b, by the extra workgroup row.  Per-image counts are accumulated in
@@ -246,7 +207,7 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(PackParams p)
         return;
     }
     const int64_t img_row0 = (int64_t)b * p.N;
-    const int L = rank_image(p.keep + img_row0, p.N, s_pos, s_red);
+    const int L = dev::rank_kept(p.keep + img_row0, p.N, s_pos, s_red);
     const int r0 = c * p.rows;
     if (c > 0 && r0 >= L) return;  // nothing to copy; chunk 0 still writes cu
     const int nr = max(0, min(p.rows, L - r0));

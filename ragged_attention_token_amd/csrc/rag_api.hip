@@ -60,7 +60,7 @@ extern "C" RAG_API rag_status rag_attn(const void* q, const void* k, const void*
     if (s != RAG_OK) return s;
     return hip_status(rag::launch_attn(q, k, v, q_row_stride, k_row_stride, v_row_stride, in_dtype,
                                        cu_seqlens, nullptr, B, 0, max_seqlen, total_rows, H, scale,
-                                       o, o_row_stride, out_dtype, false, stream),
+                                       o, o_row_stride, out_dtype, rag::kLayoutRagged, 0u, stream),
                       "rag_attn launch");
 }
 
@@ -92,8 +92,26 @@ extern "C" RAG_API rag_status rag_attn_padded(const void* q, const void* k, cons
     if (s != RAG_OK) return s;
     return hip_status(rag::launch_attn(q, k, v, q_row_stride, k_row_stride, v_row_stride, in_dtype,
                                        nullptr, keep, B, N, N, B * N, H, scale, o, o_row_stride,
-                                       out_dtype, true, stream),
+                                       out_dtype, rag::kLayoutPadded, 0u, stream),
                       "rag_attn_padded launch");
+}
+
+extern "C" RAG_API rag_status rag_attn_gathered(const uint8_t* keep, int32_t B, int32_t N,
+                                                const void* q, const void* k, const void* v,
+                                                int64_t q_row_stride, int64_t k_row_stride,
+                                                int64_t v_row_stride, rag_dtype in_dtype,
+                                                int32_t H, int32_t head_dim, float scale, void* o,
+                                                int64_t o_row_stride, rag_dtype out_dtype,
+                                                uint32_t flags, void* stream)
+{
+    rag_status s = rag::validate_attn_gathered(keep, B, N, q, k, v, q_row_stride, k_row_stride,
+                                               v_row_stride, in_dtype, H, head_dim, scale, o,
+                                               o_row_stride, out_dtype, flags);
+    if (s != RAG_OK) return s;
+    return hip_status(rag::launch_attn(q, k, v, q_row_stride, k_row_stride, v_row_stride, in_dtype,
+                                       nullptr, keep, B, N, N, B * N, H, scale, o, o_row_stride,
+                                       out_dtype, rag::kLayoutGathered, flags, stream),
+                      "rag_attn_gathered launch");
 }
 
 // ---------------------------------------------------------------- pipeline
@@ -120,11 +138,26 @@ rag_status enqueue_pass(const rag_pipeline_desc& d, void* stream)
     e = rag::launch_attn(base, base + C * in_es, base + 2 * C * in_es, ps, ps, ps, d.in_dtype,
                          d.cu_seqlens, nullptr, d.B, 0, d.max_seqlen ? d.max_seqlen : d.N,
                          d.B * d.N, d.H, d.scale, d.o_packed, d.o_packed_row_stride / out_es,
-                         d.out_dtype, false, stream);
+                         d.out_dtype, rag::kLayoutRagged, 0u, stream);
     if (e != (int)hipSuccess) return hip_status(e, "pipeline attn");
     e = rag::launch_unpack(d.o_packed, d.o_packed_row_stride, out_row, d.cu_seqlens, d.gather_idx,
                            d.B, d.N, d.dst, d.dst_row_stride, d.unpack_flags, stream);
     return hip_status(e, "pipeline unpack");
+}
+
+// The same pass as one launch: attention on the kept rows of src, output
+// written to their rows of dst (no packed buffers, no offsets).
+rag_status enqueue_fused(const rag_pipeline_desc& d, void* stream)
+{
+    const int64_t C = (int64_t)d.H * d.head_dim;
+    const int in_es = rag::dtype_bytes(d.in_dtype), out_es = rag::dtype_bytes(d.out_dtype);
+    const char* sr = static_cast<const char*>(d.src);
+    const int64_t ss = d.src_row_stride / in_es;
+    const int e = rag::launch_attn(sr, sr + C * in_es, sr + 2 * C * in_es, ss, ss, ss, d.in_dtype,
+                                   nullptr, d.keep, d.B, d.N, d.N, d.B * d.N, d.H, d.scale, d.dst,
+                                   d.dst_row_stride / out_es, d.out_dtype, rag::kLayoutGathered,
+                                   d.unpack_flags, stream);
+    return hip_status(e, "pipeline fused attn");
 }
 
 }  // namespace
@@ -172,6 +205,12 @@ extern "C" RAG_API rag_status rag_pipeline_launch_eager(rag_pipeline* p, void* s
 {
     if (!p) return set_error(RAG_ERR_INVALID_ARG, "pipeline is NULL");
     return enqueue_pass(p->d, stream);
+}
+
+extern "C" RAG_API rag_status rag_pipeline_launch_fused(rag_pipeline* p, void* stream)
+{
+    if (!p) return set_error(RAG_ERR_INVALID_ARG, "pipeline is NULL");
+    return enqueue_fused(p->d, stream);
 }
 
 extern "C" RAG_API void rag_pipeline_destroy(rag_pipeline* p)
@@ -259,12 +298,18 @@ extern "C" RAG_API rag_status rag_measure_dispatch(rag_pipeline* p, int32_t warm
                                d.keep, d.B, d.N, d.H, d.head_dim, d.scale, d.dst,
                                d.dst_row_stride / out_es, d.out_dtype, st);
     };
+    auto fused = [&]() {
+        return rag_attn_gathered(d.keep, d.B, d.N, sr, sr + C * in_es, sr + 2 * C * in_es, ss, ss,
+                                 ss, d.in_dtype, d.H, d.head_dim, d.scale, d.dst,
+                                 d.dst_row_stride / out_es, d.out_dtype, d.unpack_flags, st);
+    };
     rag_status s;
     if ((s = time_calls(empty, st, warmup, iters, out_us + 0, out_us + 3)) != RAG_OK) return s;
     if ((s = time_calls(attn, st, warmup, iters, out_us + 6, out_us + 9)) != RAG_OK) return s;
     if ((s = time_calls(eager, st, warmup, iters, out_us + 12, nullptr)) != RAG_OK) return s;
     if ((s = time_calls(graph, st, warmup, iters, out_us + 15, nullptr)) != RAG_OK) return s;
     if ((s = time_calls(padded, st, warmup, iters, out_us + 18, nullptr)) != RAG_OK) return s;
+    if ((s = time_calls(fused, st, warmup, iters, out_us + 21, out_us + 24)) != RAG_OK) return s;
     return RAG_OK;
 }
 
@@ -293,7 +338,8 @@ extern "C" RAG_API rag_status rag_measure_stages(rag_pipeline* p, int32_t iters,
         return hip_status(rag::launch_attn(pk, pk + C * in_es, pk + 2 * C * in_es, ps, ps, ps,
                                            d.in_dtype, d.cu_seqlens, nullptr, d.B, 0, maxlen,
                                            d.B * d.N, d.H, d.scale, d.o_packed,
-                                           d.o_packed_row_stride / out_es, d.out_dtype, false, st),
+                                           d.o_packed_row_stride / out_es, d.out_dtype,
+                                           rag::kLayoutRagged, 0u, st),
                           "attn");
     };
     auto unpack = [&]() {
@@ -306,11 +352,12 @@ extern "C" RAG_API rag_status rag_measure_stages(rag_pipeline* p, int32_t iters,
         return hip_status(rag::launch_attn(sr, sr + C * in_es, sr + 2 * C * in_es, ss, ss, ss,
                                            d.in_dtype, nullptr, d.keep, d.B, d.N, d.N, d.B * d.N,
                                            d.H, d.scale, d.dst, d.dst_row_stride / out_es,
-                                           d.out_dtype, true, st),
+                                           d.out_dtype, rag::kLayoutPadded, 0u, st),
                           "padded");
     };
     auto eager = [&]() { return enqueue_pass(d, st); };
     auto graph = [&]() { return rag_pipeline_launch(p, st); };
+    auto fused = [&]() { return enqueue_fused(d, st); };
     hipEvent_t e0 = nullptr, e1 = nullptr;
     rag_status s = hip_status((int)hipEventCreate(&e0), "hipEventCreate");
     if (s == RAG_OK) s = hip_status((int)hipEventCreate(&e1), "hipEventCreate");
@@ -340,6 +387,7 @@ extern "C" RAG_API rag_status rag_measure_stages(rag_pipeline* p, int32_t iters,
     if (s == RAG_OK) s = timed(padded, out_us + 3);
     if (s == RAG_OK) s = timed(eager, out_us + 4);
     if (s == RAG_OK) s = timed(graph, out_us + 5);
+    if (s == RAG_OK) s = timed(fused, out_us + 6);
     if (e0) (void)hipEventDestroy(e0);
     if (e1) (void)hipEventDestroy(e1);
     return s;

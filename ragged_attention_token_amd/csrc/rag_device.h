@@ -1,0 +1,66 @@
+// rag_device.h -- device helpers shared by the kernels of librag.so (HIP only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace rag {
+namespace dev {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw 32-bit buffer resource, gfx9 family
+// Outside every resource the kernels build (all span < 2^31 bytes), with room
+// for the column offsets (< 64 KiB) added to it without wrapping.
+constexpr uint32_t kDropOffset = 0xFFFF0000u;
+
+// A buffer resource over [base, base + bytes).  Loads outside it return zeros
+// and stores outside it are dropped by the hardware.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
+}
+
+__device__ __forceinline__ u32x4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+__device__ __forceinline__ void st16(u32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+}
+
+// Lists the positions n < N with krow[n] != 0 in ascending order into pos[]
+// (the rank of a kept position is its index in pos) and returns their number.
+// A 256-lane workgroup reads the row once: a 64-lane ballot plus popcount gives
+// each kept position its rank inside its wave, and a 4-entry LDS table (wsum)
+// the ranks of the waves before it.  Every thread of the workgroup must call it.
+__device__ __forceinline__ int rank_kept(const uint8_t* krow, int N, int* pos, int* wsum)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int L = 0;
+    for (int base = 0; base < N; base += 256) {
+        const int n = base + tid;
+        const bool kept = n < N && krow[n] != 0;
+        const uint64_t m = __ballot(kept);
+        const int below = __popcll(m & ((1ull << lane) - 1ull));
+        if (lane == 0) wsum[wave] = __popcll(m);
+        __syncthreads();
+        int before = 0, total = 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const int x = wsum[w];
+            before += (w < wave) ? x : 0;
+            total += x;
+        }
+        if (kept) pos[L + before + below] = n;
+        L += total;
+        __syncthreads();
+    }
+    return L;
+}
+
+}  // namespace dev
+}  // namespace rag

@@ -32,6 +32,11 @@ rag_status validate_attn_padded(const void* q, const void* k, const void* v,
                                 int32_t in_dtype, const uint8_t* keep, int32_t B, int32_t N,
                                 int32_t H, int32_t head_dim, float scale, const void* o,
                                 int64_t o_row_stride, int32_t out_dtype);
+rag_status validate_attn_gathered(const uint8_t* keep, int32_t B, int32_t N, const void* q,
+                                  const void* k, const void* v, int64_t q_row_stride,
+                                  int64_t k_row_stride, int64_t v_row_stride, int32_t in_dtype,
+                                  int32_t H, int32_t head_dim, float scale, const void* o,
+                                  int64_t o_row_stride, int32_t out_dtype, uint32_t flags);
 rag_status validate_pipeline(const rag_pipeline_desc* d);
 
 inline int dtype_bytes(int32_t dt) { return dt == RAG_DTYPE_F32 ? 4 : 2; }
@@ -49,10 +54,15 @@ int launch_pack(const uint8_t* keep, int32_t B, int32_t N, const void* src,
 int launch_unpack(const void* packed, int64_t packed_row_stride, int32_t row_bytes,
                   const int32_t* cu_seqlens, const int32_t* gather_idx, int32_t B, int32_t N,
                   void* dst, int64_t dst_row_stride, uint32_t flags, void* stream);
+// layout: 0 = packed ragged rows (cu_seqlens), 1 = padded [B, N] rows with
+// dropped keys masked, 2 = gathered: the kept rows of the [B, N] layout, found
+// from the keep row, output written to those rows (flags: zero-dropped).
+enum { kLayoutRagged = 0, kLayoutPadded = 1, kLayoutGathered = 2 };
 int launch_attn(const void* q, const void* k, const void* v, int64_t q_row_stride,
                 int64_t k_row_stride, int64_t v_row_stride, int32_t in_dtype,
                 const int32_t* cu_seqlens, const uint8_t* keep, int32_t B, int32_t N,
                 int32_t max_seqlen, int32_t total_rows, int32_t H, float scale, void* o,
-                int64_t o_row_stride, int32_t out_dtype, bool padded, void* stream);
+                int64_t o_row_stride, int32_t out_dtype, int layout, uint32_t flags,
+                void* stream);
 
 }  // namespace rag

@@ -295,7 +295,79 @@ def test_stage_measurement_runs():
     bufs = _pipeline_buffers(w, torch.bfloat16)
     pipe = _make_pipeline(w, bufs)
     res = pipe.measure_stages(iters=20)
-    assert set(res) == {"pack", "attn", "unpack", "padded", "eager_pass", "graph_pass"}
+    assert set(res) == {"pack", "attn", "unpack", "padded", "eager_pass", "graph_pass", "fused_pass"}
     for k, v in res.items():
         assert 0 < v < 1e5, (k, v)
+    pipe.close()
+
+
+def _gathered(w, out_dtype, flags=0):
+    src = to_gpu_rows(w)
+    keep = torch.from_numpy(w.keep).cuda()
+    C = w.C
+    o = sentinel_like((w.B * w.N, C), out_dtype)
+    binding.rag_attn_gathered(keep, src[:, :C], src[:, C:2 * C], src[:, 2 * C:], o, H=w.H,
+                              scale=w.scale, flags=flags)
+    torch.cuda.synchronize()
+    return o
+
+
+@pytest.mark.parametrize("name", ["tiny", "deits_b4_p800", "deitb_ragged_b64", "empty_and_full",
+                                  "n1", "tile_edges", "n577_two", "f32_odd", "n5_golden_like"])
+def test_gathered_equals_three_stage_pipeline_and_oracle(name):
+    w = FULL[name]()
+    print("gathered case", name, flush=True)
+    ref = _oracle_pack(w)
+    packed_ref, cu_ref, gather_ref = ref
+    g = gpu_pack(w)
+    for out_dtype in (torch.float32, torch.bfloat16):
+        staged = gpu_attn(g["packed"], g["cu"], w, out_dtype)
+        fused = _gathered(w, out_dtype)
+        fz = as_numpy_rows(fused)
+        sz = as_numpy_rows(staged)
+        T = w.T
+        # bit for bit the packed result, at the kept rows; dropped rows untouched
+        assert (fz[gather_ref].view(np.uint8) == sz[:T].view(np.uint8)).all()
+        dropped = np.setdiff1d(np.arange(w.B * w.N), gather_ref)
+        assert (fz[dropped].view(np.uint8) == SENTINEL_BYTE).all()
+    got = as_numpy_rows(_gathered(w, torch.float32)).astype(np.float64)
+    for b, want in _oracle_attn_images(w, ref, range(w.B)).items():
+        s_, e_ = int(cu_ref[b]), int(cu_ref[b + 1])
+        assert np.abs(got[gather_ref[s_:e_]] - want).max() <= ATOL, b
+
+
+@pytest.mark.parametrize("name", ["deits_b256_p800", "deitb384_b32", "deits_b256_p000"])
+def test_gathered_full_size_sampled(name):
+    make, nsample = SAMPLED[name]
+    w = make()
+    print("gathered full-size case", name, flush=True)
+    ref = _oracle_pack(w)
+    _, cu_ref, gather_ref = ref
+    got = as_numpy_rows(_gathered(w, torch.float32)).astype(np.float64)
+    rng = np.random.default_rng(1)
+    images = sorted(set(rng.choice(w.B, size=min(nsample, w.B), replace=False).tolist()) | {w.B - 1})
+    for b, want in _oracle_attn_images(w, ref, images).items():
+        s_, e_ = int(cu_ref[b]), int(cu_ref[b + 1])
+        assert np.abs(got[gather_ref[s_:e_]] - want).max() <= ATOL, b
+    dropped = np.setdiff1d(np.arange(w.B * w.N), gather_ref)
+    assert (as_numpy_rows(_gathered(w, torch.bfloat16))[dropped].view(np.uint8) == SENTINEL_BYTE).all()
+
+
+def test_gathered_zero_dropped_and_fused_pipeline():
+    w = wl.custom(B=5, N=197, H=6, lengths=[0, 197, 1, 40, 64], seed=14)
+    o = _gathered(w, torch.float32, flags=binding.RAG_UNPACK_ZERO_DROPPED).cpu().numpy()
+    assert (o[w.keep.reshape(-1) == 0] == 0).all()
+    bufs = _pipeline_buffers(w, torch.float32)
+    pipe = _make_pipeline(w, bufs)
+    pipe.launch_eager()
+    torch.cuda.synchronize()
+    staged = bufs["dst"].clone()
+    bufs["dst"].view(torch.uint8).fill_(SENTINEL_BYTE)
+    pipe.launch_fused()
+    torch.cuda.synchronize()
+    assert torch.equal(bufs["dst"].view(torch.uint8), staged.view(torch.uint8))
+    res = pipe.measure_dispatch(warmup=3, iters=10)
+    assert res["fused_roundtrip"]["p50"] > 0
+    st = pipe.measure_stages(iters=10)
+    assert st["fused_pass"] > 0
     pipe.close()
