@@ -102,6 +102,20 @@ __device__ __forceinline__ float row_sum(float x)
 
 __device__ __forceinline__ uint32_t bits(__bf16 x) { return __builtin_bit_cast(uint16_t, x); }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats as packed bf16 high parts (round to nearest even, one
+// v_cvt_pk_bf16_f32) and packed bf16 remainders x - hi (exact in fp32, then
+// rounded the same way): together they carry about 16 significant bits.
+__device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uint32_t& lo)
+{
+    hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, bf16x2));
+    const float h0 = __uint_as_float(hi << 16);
+    const float h1 = __uint_as_float(hi & 0xFFFF0000u);
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0 - h0, x1 - h1}, bf16x2));
+}
+
 using dev::kDropOffset;
 using dev::ld16;
 using dev::make_rsrc;
@@ -267,30 +281,36 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
         if (!wave_active) continue;
 
         // ---- S^T = K Q^T: block kb holds keys kt+16kb+4g+i (i<4), query r16 --
-        const int nblk = (nk + 15) >> 4;
+        // All four blocks are computed: K rows past the sequence are zero in LDS.
         f32x4 s[4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-            s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (kb < nblk) {
-                const __bf16* kr = &sK[(kb * 16 + r16) * kKS + 8 * g];
-                const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kr);
-                const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kr + 32);
-                s[kb] = mfma(a0, qh0, s[kb]);
-                s[kb] = mfma(a1, qh1, s[kb]);
-                if constexpr (IN_F32) {
-                    const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(kr + K_PLANE);
-                    const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(kr + K_PLANE + 32);
-                    s[kb] = mfma(b0, qh0, s[kb]);
-                    s[kb] = mfma(b1, qh1, s[kb]);
-                    s[kb] = mfma(a0, ql0, s[kb]);
-                    s[kb] = mfma(a1, ql1, s[kb]);
-                }
+            const __bf16* kr = &sK[(kb * 16 + r16) * kKS + 8 * g];
+            const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kr);
+            const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kr + 32);
+            s[kb] = mfma(a0, qh0, f32x4{0.f, 0.f, 0.f, 0.f});
+            s[kb] = mfma(a1, qh1, s[kb]);
+            if constexpr (IN_F32) {
+                const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(kr + K_PLANE);
+                const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(kr + K_PLANE + 32);
+                s[kb] = mfma(b0, qh0, s[kb]);
+                s[kb] = mfma(b1, qh1, s[kb]);
+                s[kb] = mfma(a0, ql0, s[kb]);
+                s[kb] = mfma(a1, ql1, s[kb]);
             }
         }
 
         // ---- online softmax (fp32, base 2) ----------------------------------
-        // x = scale*log2(e)*s; keys past the tile (or dropped, padded) -> -inf.
+        // The exponent is c*s - m with c = scale*log2(e).  For c > 0 the max is
+        // taken on the raw scores and the scale folds into one FMA per score;
+        // otherwise the scores are scaled first (a rare, uniform branch).  Keys
+        // past the tile (or dropped, padded form) become -inf.
+        float cm = c;
+        if (!(c > 0.f)) {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) s[kb] *= c;
+            cm = 1.f;
+        }
         if (PADDED || nk < kBN) {
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
@@ -299,18 +319,14 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
                     const int key = kb * 16 + 4 * g + i;
                     bool ok = key < nk;
                     if constexpr (PADDED) ok = ok && sKeep[key] != 0;
-                    s[kb][i] = ok ? s[kb][i] * c : -INFINITY;
+                    s[kb][i] = ok ? s[kb][i] : -INFINITY;
                 }
             }
-        } else {
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) s[kb] *= c;
         }
-        float mloc = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                           fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-        mloc = fmaxf(mloc, fmaxf(fmaxf(fmaxf(s[2][0], s[2][1]), fmaxf(s[2][2], s[2][3])),
-                                 fmaxf(fmaxf(s[3][0], s[3][1]), fmaxf(s[3][2], s[3][3]))));
-        mloc = row_max(mloc);
+        float mloc = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]), fmaxf(fmaxf(s[0][3], s[1][0]), s[1][1]));
+        mloc = fmaxf(mloc, fmaxf(fmaxf(fmaxf(s[1][2], s[1][3]), s[2][0]), fmaxf(fmaxf(s[2][1], s[2][2]), s[2][3])));
+        mloc = fmaxf(mloc, fmaxf(fmaxf(s[3][0], s[3][1]), fmaxf(s[3][2], s[3][3])));
+        mloc = row_max(mloc) * cm;
         const float m_new = fmaxf(m_run, mloc);
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
         if (kt > 0) {
@@ -325,7 +341,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
         for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float e = fast_exp2(s[kb][i] - m_use);
+                const float e = fast_exp2(__builtin_fmaf(s[kb][i], cm, -m_use));
                 s[kb][i] = e;
                 psum += e;
             }
@@ -338,14 +354,18 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
             if (cc * 32 < nk) {
-                bf16x8 ph, pl;
+                u32x4 phw, plw;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float x = e < 4 ? s[2 * cc][e] : s[2 * cc + 1][e - 4];
-                    const __bf16 hh = static_cast<__bf16>(x);
-                    ph[e] = hh;
-                    pl[e] = static_cast<__bf16>(x - static_cast<float>(hh));
+                for (int e = 0; e < 4; ++e) {
+                    const float x0 = e < 2 ? s[2 * cc][2 * e] : s[2 * cc + 1][2 * e - 4];
+                    const float x1 = e < 2 ? s[2 * cc][2 * e + 1] : s[2 * cc + 1][2 * e - 3];
+                    uint32_t hw, lw;
+                    split_pair(x0, x1, hw, lw);
+                    phw[e] = hw;
+                    plw[e] = lw;
                 }
+                const bf16x8 ph = __builtin_bit_cast(bf16x8, phw);
+                const bf16x8 pl = __builtin_bit_cast(bf16x8, plw);
 #pragma unroll
                 for (int db = 0; db < 4; ++db) {
                     const int vo = (db * 16 + r16) * kVS + 32 * cc + 4 * g;

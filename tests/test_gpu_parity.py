@@ -139,13 +139,17 @@ def test_keep_bytes_other_than_one_count_as_kept():
     _check_pack(w, gpu_pack(w), ref)
 
 
-def test_length_one_returns_v_row_exactly():
+def test_length_one_returns_v_row():
+    """A one-token image attends only to itself, so O is its V row.  The
+    kernel's exponent is fma(s, c, -m) with m the rounded c*s_max, so the single
+    weight is 2^r (r = that rounding residual, |r| <= 2^-24 |m|) carried as
+    bf16 hi + lo: O matches V to about 2^-16 relative, not bit for bit."""
     w = wl.custom(B=7, N=33, H=6, lengths=[1] * 7, seed=11)
     g = gpu_pack(w)
     o = gpu_attn(g["packed"], g["cu"], w, torch.float32).cpu().numpy()
     packed_ref, cu_ref, _ = _oracle_pack(w)
     v = bf16_bits_to_f64(packed_ref[:, 2 * w.C:3 * w.C])
-    assert (o[:w.T].astype(np.float64) == v).all()
+    assert (np.abs(o[:w.T].astype(np.float64) - v) <= np.abs(v) * 2.0 ** -14 + 1e-30).all()
 
 
 def test_attention_is_deterministic():
