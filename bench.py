@@ -82,9 +82,13 @@ class Bufs:
         self.o_packed = torch.empty(B * N, C, dtype=out_dtype, device="cuda")
         self.dst = torch.zeros(B * N, C, dtype=out_dtype, device="cuda")
         self.o_pad = torch.empty(B * N, C, dtype=out_dtype, device="cuda")
+        # host bound of the kept count per image: a top-k pruning rate fixes it
+        # (every image keeps the same number of tokens), so no device value is
+        # read back to size the attention launches
+        self.max_seqlen = int(w.lengths.max())
         self.pipe = binding.Pipeline(self.keep, self.src, self.packed, self.cu, self.gather,
                                      self.o_packed, self.dst, H=w.H, scale=w.scale,
-                                     max_seqlen_dev=self.mx)
+                                     max_seqlen=self.max_seqlen, max_seqlen_dev=self.mx)
         self.binding = binding
 
     # the three stages and the comparator, each one launch on the current stream
@@ -94,7 +98,7 @@ class Bufs:
     def attn(self):
         C = self.w.C
         p = self.packed
-        self.binding.rag_attn(p[:, :C], p[:, C:2 * C], p[:, 2 * C:], self.cu, self.w.N,
+        self.binding.rag_attn(p[:, :C], p[:, C:2 * C], p[:, 2 * C:], self.cu, self.max_seqlen,
                               self.o_packed, H=self.w.H, scale=self.w.scale)
 
     def unpack(self):

@@ -193,8 +193,15 @@ RAG_API rag_status rag_attn_padded(const void* q, const void* k, const void* v,
  * (same kernel arithmetic, same key order).  Rows of dropped tokens are left
  * untouched, or zeroed with RAG_UNPACK_ZERO_DROPPED.  keep [B, N] uint8 (any
  * alignment); other arguments as in rag_attn_padded.
+ *   max_seqlen  host-side upper bound of the kept count per image, in [0, N];
+ *               0 means N.  It sizes the launch (LDS and waves per workgroup),
+ *               so a tight bound (e.g. the pruning method's kept count) is
+ *               faster.  As in rag_attn, an image with more kept rows is
+ *               treated as its first max_seqlen kept rows (later kept rows are
+ *               neither attended nor written).
  */
-RAG_API rag_status rag_attn_gathered(const uint8_t* keep, int32_t B, int32_t N, const void* q,
+RAG_API rag_status rag_attn_gathered(const uint8_t* keep, int32_t B, int32_t N,
+                                     int32_t max_seqlen, const void* q,
                                      const void* k, const void* v, int64_t q_row_stride,
                                      int64_t k_row_stride, int64_t v_row_stride,
                                      rag_dtype in_dtype, int32_t H, int32_t head_dim, float scale,

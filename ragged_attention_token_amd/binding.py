@@ -78,7 +78,7 @@ def load(path: str = LIB_PATH):
     lib.rag_unpack.argtypes = [vp, i64, i32, vp, vp, i32, i32, vp, i64, u32, vp]
     lib.rag_attn_padded.argtypes = [vp, vp, vp, i64, i64, i64, i32, vp, i32, i32, i32, i32, f32,
                                     vp, i64, i32, vp]
-    lib.rag_attn_gathered.argtypes = [vp, i32, i32, vp, vp, vp, i64, i64, i64, i32, i32, i32, f32,
+    lib.rag_attn_gathered.argtypes = [vp, i32, i32, i32, vp, vp, vp, i64, i64, i64, i32, i32, i32, f32,
                                       vp, i64, i32, u32, vp]
     lib.rag_pipeline_create.argtypes = [ctypes.POINTER(PipelineDesc), ctypes.POINTER(vp)]
     lib.rag_pipeline_launch_fused.argtypes = [vp, vp]
@@ -240,9 +240,10 @@ def rag_attn_padded(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, keep: tor
 
 def rag_attn_gathered(keep: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                       o: torch.Tensor, H: int, scale: float, flags: int = 0,
-                      head_dim: int = RAG_HEAD_DIM, stream=None) -> None:
+                      head_dim: int = RAG_HEAD_DIM, max_seqlen: int = 0, stream=None) -> None:
     """Pack + attend + unpack in one launch: q/k/v/o rows b*N + n of the [B, N]
-    layout; attention over each image's kept rows, written to those rows of o."""
+    layout; attention over each image's kept rows, written to those rows of o.
+    max_seqlen: host bound of the kept count per image (0 = N)."""
     qp, qs = _rows(q, "q")
     kp, ks = _rows(k, "k")
     vp, vs = _rows(v, "v")
@@ -255,7 +256,7 @@ def rag_attn_gathered(keep: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: t
         raise ValueError("q/k/v/o need B*N rows")
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k, v must share a dtype")
-    _check(load().rag_attn_gathered(keep.data_ptr(), B, N, qp, kp, vp, qs, ks, vs, _dtype_code(q),
+    _check(load().rag_attn_gathered(keep.data_ptr(), B, N, int(max_seqlen), qp, kp, vp, qs, ks, vs, _dtype_code(q),
                                     int(H), int(head_dim), float(scale), op, os_, _dtype_code(o),
                                     int(flags), _stream(stream)))
 

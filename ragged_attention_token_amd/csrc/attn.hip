@@ -38,6 +38,8 @@
 //     consecutive lanes with 16-byte stores.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "rag_device.h"
 #include "rag_internal.h"
 
@@ -72,6 +74,7 @@ struct AttnParams {
     const int32_t* cu;       // ragged
     const uint8_t* keep;     // padded and gathered
     int32_t B, N, H, total_rows, max_len, n_qtiles, zero_dropped;
+    int32_t lds_rows;        // LDS-resident kernel: K / V rows held, max_len rounded up to 32
     float scale_log2;        // scale * log2(e)
 };
 
@@ -82,22 +85,14 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c)
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Combine a per-lane value over the four 16-lane rows of the wave (lanes l,
-// l^16, l^32, l^48), which hold the same query row.
+// Maximum of a per-lane value over the four 16-lane rows of the wave (lanes
+// l, l^16, l^32, l^48), which hold the same query row.
 __device__ __forceinline__ float row_max(float x)
 {
     auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
     auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-
-__device__ __forceinline__ float row_sum(float x)
-{
-    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 __device__ __forceinline__ uint32_t bits(__bf16 x) { return __builtin_bit_cast(uint16_t, x); }
@@ -140,6 +135,138 @@ __device__ __forceinline__ void load8(__amdgpu_buffer_rsrc_t r, uint32_t off, bf
     }
 }
 
+// ---- online softmax shared by both kernels --------------------------------
+//
+// Exponents are taken in base 2 with c = scale * log2(e) folded into one FMA
+// per score, c * s - m, where m is the row's running reference maximum (of
+// c * s).  c must be positive: fold_scale negates Q for a negative scale and
+// turns a zero scale into a tiny positive one (every product then rounds to
+// an exponent of 0: uniform weights), so no tile pays for the other signs.
+//
+// Lazy rescaling: the reference m only moves when some row of the wave sees
+// a tile maximum more than kLazyLog2 above it.  Otherwise the stale m is kept
+// and the tile's probabilities are at most 2^kLazyLog2 (no overflow risk in
+// fp32), which skips the accumulator rescale on almost every tile; O = acc / l
+// does not depend on the reference.
+//
+// Row sums come from the MFMA unit: the same P.V product with an all-ones A
+// operand gives, in every element of the lane's result, the sum of the
+// probabilities of the lane's query row (the same bf16 hi + lo values that
+// weight V, so numerator and denominator use identical P).
+constexpr float kLazyLog2 = 8.f;
+
+struct Online {
+    float m;        // reference maximum of c * s for the lane's query row
+    f32x4 acc[4];   // O^T: acc[db][i] = O[query r16][16 db + 4 g + i] (unnormalised)
+    f32x4 lsum;     // row sums of P (all four elements equal)
+};
+
+__device__ __forceinline__ void online_init(Online& st)
+{
+    st.m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st.acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    st.lsum = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+__device__ __forceinline__ bf16x8 negate_bf16(bf16x8 x)
+{
+    return __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, x) ^ 0x80008000u);
+}
+
+// Returns the positive exponent scale to use; negates the Q operand registers
+// when c < 0 (c s = (-c)(-s)).
+__device__ __forceinline__ float fold_scale(float c, bf16x8& q0, bf16x8& q1, bf16x8& q2, bf16x8& q3)
+{
+    if (c < 0.f) {
+        q0 = negate_bf16(q0);
+        q1 = negate_bf16(q1);
+        q2 = negate_bf16(q2);
+        q3 = negate_bf16(q3);
+        c = -c;
+    }
+    return c > 0.f ? c : 1e-30f;
+}
+
+// Scores -> probabilities for one 64-key tile, in place.  s[kb][i] is the raw
+// score of the lane's query and key 16 kb + 4 g + i of the tile.  FULL: all 64
+// keys are present; otherwise keys >= nk are absent (their blocks need not be
+// computed) and get probability 0.  PADDED: keys with keep byte 0 (keep_tile,
+// indexed by key within the tile) are masked too.  `first`: the first tile of
+// the row (the reference is set, nothing to rescale).
+template <bool FULL, bool PADDED>
+__device__ __forceinline__ void online_probs(f32x4 (&s)[4], int nk, const uint8_t* keep_tile,
+                                             int g, float c, bool first, Online& st)
+{
+    if constexpr (!FULL || PADDED) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int key = kb * 16 + 4 * g + i;
+                bool ok = FULL || key < nk;
+                if constexpr (PADDED) ok = ok && keep_tile[key] != 0;
+                s[kb][i] = ok ? s[kb][i] : -INFINITY;
+            }
+        }
+    }
+    float mloc = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]), fmaxf(fmaxf(s[0][3], s[1][0]), s[1][1]));
+    mloc = fmaxf(mloc, fmaxf(fmaxf(fmaxf(s[1][2], s[1][3]), s[2][0]), fmaxf(fmaxf(s[2][1], s[2][2]), s[2][3])));
+    mloc = fmaxf(mloc, fmaxf(fmaxf(s[3][0], s[3][1]), fmaxf(s[3][2], s[3][3])));
+    mloc = row_max(mloc) * c;
+    if (first) {
+        st.m = mloc;
+    } else if (__ballot(mloc > st.m + kLazyLog2)) {  // uniform over the wave
+        const float m_new = fmaxf(st.m, mloc);
+        const float alpha = fast_exp2(st.m - m_new);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) st.acc[db] *= alpha;
+        st.lsum *= alpha;
+        st.m = m_new;
+    }
+    const float m_use = (st.m == -INFINITY) ? 0.f : st.m;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        if (FULL || 16 * kb < nk) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s[kb][i] = fast_exp2(__builtin_fmaf(s[kb][i], c, -m_use));
+        } else {
+            s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+}
+
+// The P operand (B of O^T += V^T P^T) for keys 32 cc .. 32 cc + 31 of the
+// tile, as bf16 hi + lo: k-slot e of lane group g is key 32cc + 4g + e (e < 4)
+// or 32cc + 16 + 4g + e - 4 (e >= 4), the keys of s[2cc][e] and s[2cc+1][e-4].
+// Also adds the chunk's row sums to st.lsum.
+__device__ __forceinline__ void p_operand(const f32x4 (&s)[4], int cc, bf16x8& ph, bf16x8& pl,
+                                          Online& st)
+{
+    u32x4 phw, plw;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float x0 = e < 2 ? s[2 * cc][2 * e] : s[2 * cc + 1][2 * e - 4];
+        const float x1 = e < 2 ? s[2 * cc][2 * e + 1] : s[2 * cc + 1][2 * e - 3];
+        uint32_t hw, lw;
+        split_pair(x0, x1, hw, lw);
+        phw[e] = hw;
+        plw[e] = lw;
+    }
+    ph = __builtin_bit_cast(bf16x8, phw);
+    pl = __builtin_bit_cast(bf16x8, plw);
+    const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+    st.lsum = mfma(ones, ph, st.lsum);
+    st.lsum = mfma(ones, pl, st.lsum);
+}
+
+// 1 / l for the lane's query row (0 for a row without keys).
+__device__ __forceinline__ float online_inv(const Online& st)
+{
+    const float l = st.lsum[0];
+    return l > 0.f ? 1.f / l : 0.f;
+}
+
 // Gathered layout with RAG_UNPACK_ZERO_DROPPED: head h of every dropped row of
 // the image is set to zero (one workgroup per (image, head) does it).
 template <bool OUT_F32>
@@ -151,7 +278,7 @@ __device__ void zero_dropped_head(const AttnParams& p, int64_t row0, int h)
     const auto ro = make_rsrc(static_cast<char*>(p.o) + (row0 * p.os + (int64_t)h * kD) * OES,
                               (uint32_t)(p.N - 1) * osb + kD * OES);
     const u32x4 zero = {0u, 0u, 0u, 0u};
-    for (int i = threadIdx.x; i < p.N * CHUNKS; i += kThreads) {
+    for (int i = threadIdx.x; i < p.N * CHUNKS; i += blockDim.x) {
         const int n = i / CHUNKS, cix = i - n * CHUNKS;
         if (p.keep[row0 + n] == 0) dev::st16(zero, ro, (uint32_t)n * osb + 16 * cix);
     }
@@ -191,7 +318,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
         L = p.N;
     } else if constexpr (GATHERED) {
         row0 = (int64_t)b * p.N;
-        L = dev::rank_kept(p.keep + row0, p.N, s_pos, s_wsum);
+        L = min(dev::rank_kept(p.keep + row0, p.N, s_pos, s_wsum), p.max_len);
         if (p.zero_dropped && qt == 0) zero_dropped_head<OUT_F32>(p, row0, h);
     } else {
         const int s = min(max(p.cu[b], 0), p.total_rows);
@@ -226,18 +353,15 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
     };
 
     // Q^T as the B operand: lane holds query row r16, d = 8g..8g+7 and 32+8g..
-    bf16x8 qh0, qh1, ql0, ql1;
+    bf16x8 qh0, qh1, ql0 = {}, ql1 = {};
     {
         const uint32_t off = row_off(q0 + wave * 16 + r16, qsb) + 8 * g * ES;
         load8<IN_F32>(rq, off, qh0, ql0);
         load8<IN_F32>(rq, off + 32 * ES, qh1, ql1);
     }
-
-    f32x4 acc[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.f;
-    const float c = p.scale_log2;
+    const float c = fold_scale(p.scale_log2, qh0, qh1, ql0, ql1);
+    Online st;
+    online_init(st);
 
     // Registers carrying one K/V tile from global memory to LDS: this thread's
     // two 16-byte K pieces and its V key pair (hi and, for fp32 input, lo).
@@ -269,132 +393,81 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
     };
     fetch(0);
 
-    for (int kt = 0; kt < L; kt += kBN) {
-        const int nk = min(kBN, L - kt);
-        if (kt > 0) __syncthreads();  // the previous tile is no longer read
-        stash();
-        if (kt + kBN < L) fetch(kt + kBN);  // in flight while this tile is computed
-        if constexpr (PADDED) {
-            if (tid < kBN) sKeep[tid] = (tid < nk) ? p.keep[row0 + kt + tid] : 0;
-        }
-        __syncthreads();
-        if (!wave_active) continue;
-
-        // ---- S^T = K Q^T: block kb holds keys kt+16kb+4g+i (i<4), query r16 --
-        // All four blocks are computed: K rows past the sequence are zero in LDS.
-        f32x4 s[4];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            const __bf16* kr = &sK[(kb * 16 + r16) * kKS + 8 * g];
-            const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kr);
-            const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kr + 32);
-            s[kb] = mfma(a0, qh0, f32x4{0.f, 0.f, 0.f, 0.f});
-            s[kb] = mfma(a1, qh1, s[kb]);
-            if constexpr (IN_F32) {
-                const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(kr + K_PLANE);
-                const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(kr + K_PLANE + 32);
-                s[kb] = mfma(b0, qh0, s[kb]);
-                s[kb] = mfma(b1, qh1, s[kb]);
-                s[kb] = mfma(a0, ql0, s[kb]);
-                s[kb] = mfma(a1, ql1, s[kb]);
+    // Stage the tile at key kt into LDS (the next one's loads go out meanwhile),
+    // then compute it; FULL: all 64 keys present (no key-range masking).  The
+    // full tiles run in one loop and the partial last tile after it.
+    auto tile = [&](auto full_tag, const int kt) {
+            constexpr bool FULL = decltype(full_tag)::value;
+            const int nk = min(kBN, L - kt);
+            if (kt > 0) __syncthreads();  // the previous tile is no longer read
+            stash();
+            if (kt + kBN < L) fetch(kt + kBN);  // in flight while this tile is computed
+            if constexpr (PADDED) {
+                if (tid < kBN) sKeep[tid] = (tid < nk) ? p.keep[row0 + kt + tid] : 0;
             }
-        }
+            __syncthreads();
+            if (!wave_active) return;
 
-        // ---- online softmax (fp32, base 2) ----------------------------------
-        // The exponent is c*s - m with c = scale*log2(e).  For c > 0 the max is
-        // taken on the raw scores and the scale folds into one FMA per score;
-        // otherwise the scores are scaled first (a rare, uniform branch).  Keys
-        // past the tile (or dropped, padded form) become -inf.
-        float cm = c;
-        if (!(c > 0.f)) {
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) s[kb] *= c;
-            cm = 1.f;
-        }
-        if (PADDED || nk < kBN) {
+            // ---- S^T = K Q^T: block kb holds keys kt+16kb+4g+i (i<4), query r16
+            f32x4 s[4];
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int key = kb * 16 + 4 * g + i;
-                    bool ok = key < nk;
-                    if constexpr (PADDED) ok = ok && sKeep[key] != 0;
-                    s[kb][i] = ok ? s[kb][i] : -INFINITY;
-                }
-            }
-        }
-        float mloc = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]), fmaxf(fmaxf(s[0][3], s[1][0]), s[1][1]));
-        mloc = fmaxf(mloc, fmaxf(fmaxf(fmaxf(s[1][2], s[1][3]), s[2][0]), fmaxf(fmaxf(s[2][1], s[2][2]), s[2][3])));
-        mloc = fmaxf(mloc, fmaxf(fmaxf(s[3][0], s[3][1]), fmaxf(s[3][2], s[3][3])));
-        mloc = row_max(mloc) * cm;
-        const float m_new = fmaxf(m_run, mloc);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        if (kt > 0) {
-            const float alpha = fast_exp2(m_run - m_use);
-            l_run *= alpha;
-#pragma unroll
-            for (int db = 0; db < 4; ++db) acc[db] *= alpha;
-        }
-        m_run = m_new;
-        float psum = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float e = fast_exp2(__builtin_fmaf(s[kb][i], cm, -m_use));
-                s[kb][i] = e;
-                psum += e;
-            }
-        }
-        l_run += psum;
-
-        // ---- O^T += V^T P^T, 32 keys per MFMA ---------------------------------
-        // k-slot e of lane group g: e<4 -> key 32c+4g+e, e>=4 -> key 32c+16+4g+e-4;
-        // these are exactly the keys of s[2c][e] and s[2c+1][e-4].
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-            if (cc * 32 < nk) {
-                u32x4 phw, plw;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float x0 = e < 2 ? s[2 * cc][2 * e] : s[2 * cc + 1][2 * e - 4];
-                    const float x1 = e < 2 ? s[2 * cc][2 * e + 1] : s[2 * cc + 1][2 * e - 3];
-                    uint32_t hw, lw;
-                    split_pair(x0, x1, hw, lw);
-                    phw[e] = hw;
-                    plw[e] = lw;
-                }
-                const bf16x8 ph = __builtin_bit_cast(bf16x8, phw);
-                const bf16x8 pl = __builtin_bit_cast(bf16x8, plw);
-#pragma unroll
-                for (int db = 0; db < 4; ++db) {
-                    const int vo = (db * 16 + r16) * kVS + 32 * cc + 4 * g;
-                    const bf16x4 v0 = *reinterpret_cast<const bf16x4*>(&sVt[vo]);
-                    const bf16x4 v1 = *reinterpret_cast<const bf16x4*>(&sVt[vo + 16]);
-                    const bf16x8 av = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-                    acc[db] = mfma(av, ph, acc[db]);
-                    acc[db] = mfma(av, pl, acc[db]);
+                if (FULL || kb == 0 || 16 * kb < nk) {
+                    const __bf16* kr = &sK[(kb * 16 + r16) * kKS + 8 * g];
+                    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kr);
+                    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kr + 32);
+                    s[kb] = mfma(a0, qh0, f32x4{0.f, 0.f, 0.f, 0.f});
+                    s[kb] = mfma(a1, qh1, s[kb]);
                     if constexpr (IN_F32) {
-                        const bf16x4 w0 = *reinterpret_cast<const bf16x4*>(&sVt[V_PLANE + vo]);
-                        const bf16x4 w1 = *reinterpret_cast<const bf16x4*>(&sVt[V_PLANE + vo + 16]);
-                        const bf16x8 al = __builtin_shufflevector(w0, w1, 0, 1, 2, 3, 4, 5, 6, 7);
-                        acc[db] = mfma(al, ph, acc[db]);
+                        const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(kr + K_PLANE);
+                        const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(kr + K_PLANE + 32);
+                        s[kb] = mfma(b0, qh0, s[kb]);
+                        s[kb] = mfma(b1, qh1, s[kb]);
+                        s[kb] = mfma(a0, ql0, s[kb]);
+                        s[kb] = mfma(a1, ql1, s[kb]);
+                    }
+                } else {
+                    s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};  // absent keys, masked below
+                }
+            }
+            online_probs<FULL, PADDED>(s, nk, sKeep, g, c, kt == 0, st);
+            // ---- O^T += V^T P^T, 32 keys per MFMA ----------------------------
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                if (FULL || cc * 32 < nk) {
+                    bf16x8 ph, pl;
+                    p_operand(s, cc, ph, pl, st);
+#pragma unroll
+                    for (int db = 0; db < 4; ++db) {
+                        const int vo = (db * 16 + r16) * kVS + 32 * cc + 4 * g;
+                        const bf16x4 v0 = *reinterpret_cast<const bf16x4*>(&sVt[vo]);
+                        const bf16x4 v1 = *reinterpret_cast<const bf16x4*>(&sVt[vo + 16]);
+                        const bf16x8 av = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+                        st.acc[db] = mfma(av, ph, st.acc[db]);
+                        st.acc[db] = mfma(av, pl, st.acc[db]);
+                        if constexpr (IN_F32) {
+                            const bf16x4 w0 = *reinterpret_cast<const bf16x4*>(&sVt[V_PLANE + vo]);
+                            const bf16x4 w1 = *reinterpret_cast<const bf16x4*>(&sVt[V_PLANE + vo + 16]);
+                            const bf16x8 al = __builtin_shufflevector(w0, w1, 0, 1, 2, 3, 4, 5, 6, 7);
+                            st.acc[db] = mfma(al, ph, st.acc[db]);
+                        }
                     }
                 }
             }
-        }
-    }
+    };
+    int kt = 0;
+    for (; kt + kBN <= L; kt += kBN) tile(std::true_type{}, kt);
+    if (kt < L) tile(std::false_type{}, kt);
 
     // ---- epilogue: O = acc / l, staged through LDS for row-contiguous stores --
     __syncthreads();  // every wave is done with the K / V tiles
     if (!wave_active) return;
-    const float lt = row_sum(l_run);
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float inv = online_inv(st);
     char* so = smem + wave * 16 * OUT_ROW;
     // lane holds O[r16][16db + 4g + i]
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-        const f32x4 r = acc[db] * inv;
+        const f32x4 r = st.acc[db] * inv;
         char* dst = so + r16 * OUT_ROW + (16 * db + 4 * g) * OES;
         if constexpr (OUT_F32) {
             *reinterpret_cast<f32x4*>(dst) = r;
@@ -417,6 +490,275 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
         const u32x4 val = *reinterpret_cast<const u32x4*>(so + r * OUT_ROW + 16 * cix);
         __builtin_amdgcn_raw_buffer_store_b128(val, ro, row_off(q0 + wave * 16 + r, osb) + 16 * cix, 0, 0);
     }
+}
+
+// ---- LDS-resident kernel (bf16 input, sequences of up to kLdsMaxRows keys) --
+//
+// One workgroup = one (head, image, query split) with W = blockDim.x / 64
+// waves, and every wave owns exactly one 16-row query block (block
+// qs * W + wave).  The image's whole K and V for the head are copied from
+// global memory straight into LDS by buffer loads that write LDS (gfx950
+// buffer_load ... lds: no registers and no ALU work on the way), followed by
+// ONE barrier; after it each wave runs its block over all keys with no
+// further synchronisation, and waves without a block exit.  Compared with a
+// tile loop this removes the per-tile barriers and register staging, reads K
+// and V once per (image, head) and query split, and lets the last partial key
+// tile skip its empty 16-key blocks.
+//
+// LDS rows are 128 bytes (64 bf16) in natural row-major order, with the eight
+// 16-byte chunks of row r permuted by XOR with swz(r).  The permutation makes
+// both operand reads conflict-free across 16 consecutive rows: the K reads
+// (ds_read_b128, lane = row) and the V reads with gfx950's transposing read
+// ds_read_b64_tr_b16, which delivers V^T's MFMA operand from row-major V.
+constexpr int kRowBytes = kD * 2;     // one head's bf16 row
+constexpr int kLdsRowAlign = 32;      // K / V rows in LDS: a multiple of the P.V k-depth
+constexpr int kMaxWaves = 16;         // 16 query blocks: every block of kLdsMaxRows rows
+constexpr int kLdsMaxRows = 256;      // 64 KiB of K + V: two workgroups per CU
+
+// Slot of chunk c of row r is c ^ swz(r); swz depends on r mod 16 only.
+__device__ __forceinline__ int swz(int row) { return (row ^ ((row >> 3) & 1)) & 7; }
+
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) short4_t lds_short4_t;
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Four bf16 of one LDS column: lane j of each 16-lane group receives element
+// (k, j) of the 4 x 16 block whose row segments the group's lanes address.
+__device__ __forceinline__ bf16x4 ld_tr4(const char* lds_addr)
+{
+    return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)lds_addr));
+}
+
+template <bool OUT_F32, int LAYOUT, bool MULTI>
+__global__ __launch_bounds__(64 * kMaxWaves) void attn_lds_kernel(AttnParams p)
+{
+    constexpr bool PADDED = LAYOUT == kPadded;
+    constexpr bool GATHERED = LAYOUT == kGathered;
+    constexpr int OES = OUT_F32 ? 4 : 2;
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    __shared__ int s_wsum[kMaxWaves];
+
+    const int h = blockIdx.x, b = blockIdx.y, qs = blockIdx.z;
+    const int nw = blockDim.x >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r16 = lane & 15, g = lane >> 4;
+
+    // LDS: K rows [0, R), V rows [0, R), then the gathered layout's kept
+    // positions (N ints) or the padded layout's keep bytes (N rounded up to 64).
+    const int R = p.lds_rows;
+    char* sK = lds;
+    char* sV = lds + R * kRowBytes;
+    int* s_pos = reinterpret_cast<int*>(lds + 2 * R * kRowBytes);
+    uint8_t* s_keep = reinterpret_cast<uint8_t*>(lds + 2 * R * kRowBytes);
+
+    int64_t row0;
+    int L;
+    if constexpr (PADDED) {
+        row0 = (int64_t)b * p.N;
+        L = p.N;
+        const int nkeep = (p.N + 63) & ~63;
+        for (int n = tid; n < nkeep; n += blockDim.x) s_keep[n] = n < p.N ? p.keep[row0 + n] : 0;
+    } else if constexpr (GATHERED) {
+        row0 = (int64_t)b * p.N;
+        L = min(dev::rank_kept_waves(p.keep + row0, p.N, s_pos, s_wsum, nw), p.max_len);
+        if (p.zero_dropped && qs == 0) zero_dropped_head<OUT_F32>(p, row0, h);
+    } else {
+        const int s = min(max(p.cu[b], 0), p.total_rows);
+        const int e = min(max(p.cu[b + 1], s), p.total_rows);
+        row0 = s;
+        L = min(e - s, p.max_len);
+    }
+    const int nqb = (L + 15) >> 4;  // 16-row query blocks
+    if (qs * nw >= nqb) return;     // uniform over the workgroup
+
+    const int64_t hoff = (int64_t)h * kD;
+    const int span = GATHERED ? p.N : L;
+    const uint32_t qsb = (uint32_t)(p.qs * 2), ksb = (uint32_t)(p.ks * 2), vsb = (uint32_t)(p.vs * 2),
+                   osb = (uint32_t)(p.os * OES);
+    const auto rq = make_rsrc(static_cast<const char*>(p.q) + (row0 * p.qs + hoff) * 2,
+                              (uint32_t)(span - 1) * qsb + kRowBytes);
+    const auto rk = make_rsrc(static_cast<const char*>(p.k) + (row0 * p.ks + hoff) * 2,
+                              (uint32_t)(span - 1) * ksb + kRowBytes);
+    const auto rv = make_rsrc(static_cast<const char*>(p.v) + (row0 * p.vs + hoff) * 2,
+                              (uint32_t)(span - 1) * vsb + kRowBytes);
+    auto row_off = [&](int r, uint32_t stride) -> uint32_t {
+        if constexpr (GATHERED) return r < L ? (uint32_t)s_pos[r] * stride : kDropOffset;
+        else return (uint32_t)r * stride;
+    };
+
+    // ---- K, V -> LDS: one instruction moves 8 rows (1 KiB); lane l writes
+    // LDS bytes [16 l, 16 l + 16) of the block, i.e. slot l & 7 of row l >> 3,
+    // so it fetches the global chunk that the permutation puts in that slot
+    // (the permutation repeats every 16 rows: one lane offset per row parity
+    // of the 8-row block).  Rows past the sequence, up to the multiple of 32,
+    // read as zeros.
+    {
+        const int nrb = ((L + kLdsRowAlign - 1) & ~(kLdsRowAlign - 1)) >> 3;
+        const int lr = lane >> 3, slot = lane & 7;
+        const uint32_t c16e = 16u * (uint32_t)(slot ^ swz(lr)), c16o = 16u * (uint32_t)(slot ^ swz(8 + lr));
+        for (int j = wave; j < nrb; j += nw) {
+            const int row = 8 * j + lr;
+            const uint32_t c16 = (j & 1) ? c16o : c16e;
+            // (offsets computed first: a lambda call inside the builtin's
+            // argument list stops clang's host pass from emitting the stub)
+            const uint32_t koff = row_off(row, ksb) + c16, voff = row_off(row, vsb) + c16;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(sK + 1024 * j), 16, koff, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(sV + 1024 * j), 16, voff, 0, 0, 0);
+        }
+    }
+
+    // Q^T as the B operand of S^T = K Q^T: lane holds query row r16 of the
+    // block, d = 8g..8g+7 and 32+8g..32+8g+7.  The wave's blocks are
+    // qs * W + wave + k * gridDim.z * W: one of them, or (MULTI) one or more.
+    int qb = qs * nw + wave;
+    const int qstride = gridDim.z * nw;
+    bf16x8 qa0, qa1;
+    auto load_q = [&](int blk) {
+        const uint32_t off = row_off(16 * blk + r16, qsb) + 16 * g;
+        qa0 = __builtin_bit_cast(bf16x8, ld16(rq, off));
+        qa1 = __builtin_bit_cast(bf16x8, ld16(rq, off + 64));
+    };
+    if (qb < nqb) load_q(qb);
+    __builtin_amdgcn_s_waitcnt(0);  // every load of this wave has landed (LDS included)
+    __syncthreads();
+    if (qb >= nqb) return;
+
+    // Per-lane LDS offsets inside a 16-row block.
+    //  K (A operand of S^T): row r16, chunks g and g + 4 of the row.
+    const uint32_t koff0 = 128u * r16 + 16u * (uint32_t)(g ^ swz(r16));
+    const uint32_t koff1 = koff0 ^ 64u;
+    //  V (A operand of O^T += V^T P^T, transposing read): lane i of group g
+    //  addresses row 4g + i/4, columns 16 db + 4 (i % 4) .. + 3; it receives
+    //  V[4g + k][16 db + i] for k = 0..3 -- keys 4g..4g+3 of d-row i, the
+    //  k-slots that match the probabilities' layout below.
+    const int vrow = 4 * g + (r16 >> 2);
+    uint32_t voff[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+        voff[db] = 128u * vrow + 16u * (uint32_t)((2 * db + ((r16 & 3) >> 1)) ^ swz(vrow)) + 8u * (r16 & 1);
+
+    const auto ro = make_rsrc(static_cast<char*>(p.o) + (row0 * p.os + hoff) * OES,
+                              (uint32_t)(span - 1) * osb + kD * OES);
+    for (;;) {
+    bf16x8 unused0 = {}, unused1 = {};
+    const float c = fold_scale(p.scale_log2, qa0, qa1, unused0, unused1);
+    Online st;
+    online_init(st);
+
+    // One tile at key kt; FULL: all 64 keys present (no key-range masking).
+    // The full tiles run in one loop and the partial last tile after it.
+    auto tile = [&](auto full_tag, const int kt) {
+            constexpr bool FULL = decltype(full_tag)::value;
+            const int nk = min(kBN, L - kt);
+            const char* kbase = sK + kt * kRowBytes;
+            const char* vbase = sV + kt * kRowBytes;
+            // ---- S^T = K Q^T over the 16-key blocks that hold keys ----------
+            f32x4 s[4];
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                if (FULL || kb == 0 || 16 * kb < nk) {
+                    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kbase + 2048 * kb + koff0);
+                    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kbase + 2048 * kb + koff1);
+                    s[kb] = mfma(a0, qa0, f32x4{0.f, 0.f, 0.f, 0.f});
+                    s[kb] = mfma(a1, qa1, s[kb]);
+                } else {
+                    s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};  // absent keys, masked below
+                }
+            }
+            online_probs<FULL, PADDED>(s, nk, s_keep + kt, g, c, kt == 0, st);
+            // ---- O^T += V^T P^T, 32 keys per MFMA ----------------------------
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                if (FULL || cc * 32 < nk) {
+                    bf16x8 ph, pl;
+                    p_operand(s, cc, ph, pl, st);
+#pragma unroll
+                    for (int db = 0; db < 4; ++db) {
+                        const bf16x4 v0 = ld_tr4(vbase + 4096 * cc + voff[db]);
+                        const bf16x4 v1 = ld_tr4(vbase + 4096 * cc + 2048 + voff[db]);
+                        const bf16x8 av = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+                        st.acc[db] = mfma(av, ph, st.acc[db]);
+                        st.acc[db] = mfma(av, pl, st.acc[db]);
+                    }
+                }
+            }
+    };
+    int kt = 0;
+    for (; kt + kBN <= L; kt += kBN) tile(std::true_type{}, kt);
+    if (kt < L) tile(std::false_type{}, kt);
+
+    // ---- epilogue: O = acc / l; lane holds O[16 qb + r16][16 db + 4g + i] ----
+    const float inv = online_inv(st);
+    const uint32_t orow = row_off(16 * qb + r16, osb);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+        const f32x4 r = st.acc[db] * inv;
+        const uint32_t off = orow + (uint32_t)(16 * db + 4 * g) * OES;
+        if constexpr (OUT_F32) {
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, r), ro, off, 0, 0);
+        } else {
+            bf16x4 o4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o4[i] = static_cast<__bf16>(r[i]);
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o4), ro, off, 0, 0);
+        }
+    }
+    if constexpr (!MULTI) break;  // (single-block launches: one block per wave)
+    qb += qstride;
+    if (qb >= nqb) break;
+    load_q(qb);
+    }
+}
+
+// LDS bytes of attn_lds_kernel for a launch, or 0 where it does not apply
+// (fp32 input, or more than 64 KiB: K + V of up to kLdsMaxRows rows plus the
+// layout's keep data, so that at least two workgroups share a CU).
+size_t lds_kernel_bytes(const AttnParams& p, bool in_f32, int layout)
+{
+    if (in_f32) return 0;
+    const int rows = (p.max_len + kLdsRowAlign - 1) & ~(kLdsRowAlign - 1);
+    if (rows > kLdsMaxRows) return 0;
+    size_t bytes = (size_t)2 * rows * kRowBytes;
+    if (layout == kGathered) bytes += sizeof(int) * (size_t)p.N;
+    if (layout == kPadded) bytes += (size_t)((p.N + 63) & ~63);
+    return bytes <= 64 * 1024 ? bytes : 0;
+}
+
+template <bool OUT_F32, bool MULTI>
+void launch_lds_layout(const AttnParams& p, int layout, dim3 grid, dim3 block, size_t lds_bytes,
+                       hipStream_t st)
+{
+    if (layout == kPadded)
+        hipLaunchKernelGGL((attn_lds_kernel<OUT_F32, kPadded, MULTI>), grid, block, lds_bytes, st, p);
+    else if (layout == kGathered)
+        hipLaunchKernelGGL((attn_lds_kernel<OUT_F32, kGathered, MULTI>), grid, block, lds_bytes, st, p);
+    else
+        hipLaunchKernelGGL((attn_lds_kernel<OUT_F32, kRagged, MULTI>), grid, block, lds_bytes, st, p);
+}
+
+template <bool OUT_F32>
+void launch_lds_variant(AttnParams p, int layout, size_t lds_bytes, hipStream_t st)
+{
+    // With many (image, head) pairs a workgroup holds all of an image's 16-row
+    // query blocks (K and V are read once): one block per wave up to 8 blocks,
+    // two per wave beyond (so that two workgroups fit a CU and one's K / V load
+    // overlaps the other's compute).  With few pairs the blocks are split over
+    // gridDim.z workgroups of at most 4 waves, one block each, so that more CUs
+    // share the work.
+    const int nqb = (p.max_len + 15) / 16;
+    int waves;
+    if ((int64_t)p.B * p.H >= 256)  // one block per wave up to 8, else two
+        waves = nqb <= 8 ? nqb : (nqb + 1) / 2;
+    else
+        waves = min(nqb, 4);
+    const int splits = (int64_t)p.B * p.H >= 256 ? 1 : (nqb + waves - 1) / waves;
+    p.lds_rows = (p.max_len + kLdsRowAlign - 1) & ~(kLdsRowAlign - 1);
+    const dim3 grid(p.H, p.B, splits), block(64 * waves);
+    if (waves * splits >= nqb)
+        launch_lds_layout<OUT_F32, false>(p, layout, grid, block, lds_bytes, st);
+    else
+        launch_lds_layout<OUT_F32, true>(p, layout, grid, block, lds_bytes, st);
 }
 
 template <bool IN_F32, bool OUT_F32>
@@ -456,13 +798,18 @@ int launch_attn(const void* q, const void* k, const void* v, int64_t q_row_strid
     p.N = N;
     p.H = H;
     p.total_rows = total_rows;
-    p.max_len = layout == kRagged ? max_seqlen : N;
+    p.max_len = layout == kPadded ? N : max_seqlen;
     p.n_qtiles = (p.max_len + kBM - 1) / kBM;
     p.zero_dropped = (flags & RAG_UNPACK_ZERO_DROPPED) ? 1 : 0;
+    p.lds_rows = 0;
     p.scale_log2 = scale * 1.4426950408889634f;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool in_f32 = in_dtype == RAG_DTYPE_F32, out_f32 = out_dtype == RAG_DTYPE_F32;
-    if (in_f32 && out_f32) launch_variant<true, true>(p, layout, st);
+    const size_t lds_bytes = lds_kernel_bytes(p, in_f32, layout);
+    if (lds_bytes) {
+        if (out_f32) launch_lds_variant<true>(p, layout, lds_bytes, st);
+        else launch_lds_variant<false>(p, layout, lds_bytes, st);
+    } else if (in_f32 && out_f32) launch_variant<true, true>(p, layout, st);
     else if (in_f32) launch_variant<true, false>(p, layout, st);
     else if (out_f32) launch_variant<false, true>(p, layout, st);
     else launch_variant<false, false>(p, layout, st);

@@ -6,22 +6,29 @@
 // token rows into one flat buffer.  Unpack (same section, write-back): copy each
 // packed row back to its batch position.
 //
-// One launch each.  Workgroup (b, c) serves rows [c*R, c*R + R) of image b; the
-// chunk index is the slowest grid dimension, so the first chunk of every image
-// is dispatched before the later chunks, which pruned images mostly lack.
-//   1. ranks inside image b: the image's N keep bytes are read once; a 64-lane
+// One launch each.
+//
+// Pack: workgroup (b, s) copies column slice s (a contiguous range of 16-byte
+// vectors, the same for every row) of ALL kept rows of image b, so every
+// workgroup of an image with kept rows has work whatever the prune rate, and
+// the grid (B x S, S chosen so that about 1024 workgroups cover the batch) is
+// filled in one dispatch round.
+//   1. the offset of image b (number of kept tokens in images 0..b-1) is
+//      counted from 16-byte words of the keep mask; those loads are issued
+//      first so that they travel together with the keep row's (each workgroup
+//      recounts the prefix, at most B*N bytes that stay in L2: no atomics and
+//      no inter-workgroup waits, so the result is deterministic);
+//   2. ranks inside image b: the image's N keep bytes are read once; a 64-lane
 //      ballot + popcount gives each kept position its rank, and the kept
 //      positions are listed by rank in LDS;
-//   2. the chunk's source rows are requested (four 16-byte loads per lane in
-//      flight), and while they travel:
-//   3. offset of image b = number of kept tokens in images 0..b-1, counted from
-//      16-byte words of the keep mask (each workgroup recounts the prefix, at
-//      most B*N bytes that stay in L2; no atomics and no inter-workgroup waits,
-//      so the result is deterministic);
-//   4. the rows are stored.
-// All row traffic goes through buffer resources: a lane past the chunk's end
-// gets an offset outside the resource, so its load reads zero and its store is
-// dropped by the hardware; no predicated register arrays are needed.
+//   3. the slice's source rows are requested (up to kUnroll 16-byte loads per
+//      lane in flight), the prefix count is reduced, and the rows are stored.
+// Unpack: workgroup (b, c) serves packed rows [c*R, c*R + R) of image b; the
+// chunk index is the slowest grid dimension, so the first chunk of every image
+// is dispatched before the later chunks, which pruned images mostly lack.
+// All row traffic goes through buffer resources: a lane past the end gets an
+// offset outside the resource, so its load reads zero and its store is dropped
+// by the hardware; no predicated register arrays are needed.
 // An extra workgroup row (b == B) computes max_b L_b when asked for.
 #include <hip/hip_runtime.h>
 
@@ -33,8 +40,11 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kUnroll = 4;                           // 16-byte vectors per lane per batch
+constexpr int kUnroll = 4;                           // unpack: 16-byte vectors per lane per batch
 constexpr int kBatch = kThreads * kUnroll;           // vectors per workgroup per batch
+constexpr int kPackUnroll = 8;                       // pack: 16-byte vectors per lane per batch
+constexpr int kPrefixLoads = 8;                      // keep-mask words per lane per round
+constexpr int kPackTargetGroups = 512;               // workgroups a pack launch aims for
 using dev::kDropOffset;
 using dev::ld16;
 using dev::make_rsrc;
@@ -50,7 +60,8 @@ struct PackParams {
     int32_t* max_len;
     int64_t src_stride;
     int64_t packed_stride;
-    int32_t B, N, row_vecs, rows;
+    int32_t B, N, row_vecs, slice_vecs;  // slice s: vectors [s*slice_vecs, ...) of a row
+    uint32_t n_magic;                     // floor(2^32 / N) + 1
 };
 
 struct UnpackParams {
@@ -100,25 +111,51 @@ __device__ __forceinline__ int block_sum(int v, int* red)
     return t;
 }
 
-// Kept tokens in keep[0, nbytes): 16-byte words through a buffer resource
-// (words past the range read as zero), eight loads in flight per lane.
-__device__ int count_kept_prefix(const uint8_t* keep, int64_t nbytes, int* red)
+// Kept tokens in keep[0, nbytes), counted by the workgroup from 16-byte words
+// (kPrefixLoads per lane per round) through a buffer resource over the full
+// words; words past it read as zero.  prefix_load issues a round, prefix_count
+// adds up the loaded round, the further rounds and the tail bytes, and reduces
+// over the workgroup (every thread gets the total).
+struct Prefix {
+    __amdgpu_buffer_rsrc_t rk;
+    uint32_t nwords;
+    u32x4 x[kPrefixLoads];
+};
+
+__device__ __forceinline__ void prefix_load(Prefix& pf, uint32_t w0)
 {
-    const int tid = threadIdx.x;
-    const uint32_t nwords = (uint32_t)(nbytes >> 4);
-    const auto rk = make_rsrc(keep, nwords << 4);
+#pragma unroll
+    for (int j = 0; j < kPrefixLoads; ++j) pf.x[j] = ld16(pf.rk, (w0 + threadIdx.x + j * kThreads) << 4);
+}
+
+__device__ __forceinline__ int prefix_words(const Prefix& pf)
+{
     int cnt = 0;
-    for (uint32_t w0 = 0; w0 < nwords; w0 += kThreads * 8) {
-        u32x4 x[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = ld16(rk, (w0 + tid + j * kThreads) << 4);
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            cnt += nonzero_bytes(x[j][0]) + nonzero_bytes(x[j][1]) + nonzero_bytes(x[j][2]) +
-                   nonzero_bytes(x[j][3]);
+    for (int j = 0; j < kPrefixLoads; ++j)
+        cnt += nonzero_bytes(pf.x[j][0]) + nonzero_bytes(pf.x[j][1]) + nonzero_bytes(pf.x[j][2]) +
+               nonzero_bytes(pf.x[j][3]);
+    return cnt;
+}
+
+__device__ __forceinline__ Prefix prefix_begin(const uint8_t* keep, int64_t nbytes)
+{
+    Prefix pf;
+    pf.nwords = (uint32_t)(nbytes >> 4);
+    pf.rk = make_rsrc(keep, pf.nwords << 4);
+    prefix_load(pf, 0);
+    return pf;
+}
+
+__device__ int prefix_count(Prefix& pf, const uint8_t* keep, int64_t nbytes, int* red)
+{
+    int cnt = prefix_words(pf);
+    for (uint32_t w0 = kThreads * kPrefixLoads; w0 < pf.nwords; w0 += kThreads * kPrefixLoads) {
+        prefix_load(pf, w0);
+        cnt += prefix_words(pf);
     }
-    const uint32_t tail0 = nwords << 4;
-    if (tid < nbytes - tail0) cnt += keep[tail0 + tid] != 0;
+    const uint32_t tail0 = pf.nwords << 4;
+    if ((int64_t)threadIdx.x < nbytes - tail0) cnt += keep[tail0 + threadIdx.x] != 0;
     return block_sum(cnt, red);
 }
 
@@ -136,21 +173,39 @@ __device__ void max_length_pass(const PackParams& p, int* cnt, int window, int* 
         const uint32_t lo = (uint32_t)img0 * N, hi = (uint32_t)(img0 + nimg) * N;
         const uint32_t wlo = (lo + 15u) >> 4, whi = hi >> 4;  // full 16-byte words
         if (N >= 16) {
+            // kPrefixLoads words per lane in flight, then counted
             const uint4* kw = reinterpret_cast<const uint4*>(p.keep);
-            for (uint32_t w = wlo + tid; w < whi; w += kThreads) {
-                const uint4 x = kw[w];
-                const uint32_t P = w << 4;
-                const uint32_t f = P / N;             // image of the word's first byte
-                const uint32_t e = (f + 1u) * N;      // first byte of the next image
-                const uint32_t words[4] = {x.x, x.y, x.z, x.w};
-                int first = 0, second = 0;
+            for (uint32_t w0 = wlo; w0 < whi; w0 += kThreads * kPrefixLoads) {
+                uint4 x[kPrefixLoads];
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const bool nz = ((words[j >> 2] >> (8 * (j & 3))) & 0xFFu) != 0u;
-                    if (P + (uint32_t)j < e) first += nz; else second += nz;
+                for (int j = 0; j < kPrefixLoads; ++j) {
+                    const uint32_t w = w0 + tid + j * kThreads;
+                    x[j] = w < whi ? kw[w] : make_uint4(0u, 0u, 0u, 0u);
                 }
-                if (first) atomicAdd(&cnt[f - img0], first);
-                if (second) atomicAdd(&cnt[f + 1u - img0], second);
+#pragma unroll
+                for (int j = 0; j < kPrefixLoads; ++j) {
+                    const uint32_t w = w0 + tid + j * kThreads;
+                    if (w >= whi) continue;
+                    const uint32_t P = w << 4;
+                    // image of the word's first byte: P / N by a multiply-high
+                    // with n_magic = floor(2^32 / N) + 1 (an over-estimate by
+                    // less than one, corrected once)
+                    uint32_t f = __umulhi(P, p.n_magic);
+                    f -= (f * N > P) ? 1u : 0u;
+                    // bytes of the word that belong to image f; the rest to f + 1
+                    const int nfirst = (int)min((f + 1u) * N - P, 16u);
+                    const uint32_t words[4] = {x[j].x, x[j].y, x[j].z, x[j].w};
+                    int first = 0, second = 0;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const int fb = nfirst - 4 * k;  // bytes of dword k in image f
+                        const uint32_t m = fb >= 4 ? 0xFFFFFFFFu : (fb <= 0 ? 0u : (1u << (8 * fb)) - 1u);
+                        first += nonzero_bytes(words[k] & m);
+                        second += nonzero_bytes(words[k] & ~m);
+                    }
+                    if (first) atomicAdd(&cnt[f - img0], first);
+                    if (second) atomicAdd(&cnt[f + 1u - img0], second);
+                }
             }
         } else {
             for (uint32_t i = (wlo << 4) + tid; i < (whi << 4); i += kThreads)
@@ -177,69 +232,83 @@ __device__ void max_length_pass(const PackParams& p, int* cnt, int window, int* 
     }
 }
 
-// Byte offset, inside image b's source rows, of 16-byte vector v of the chunk;
-// a vector past the chunk re-reads the chunk's first row (its store is dropped).
-__device__ __forceinline__ uint32_t pack_src_off(const PackParams& p, const int* pos, int r0,
-                                                 int total, int v)
-{
-    const int vv = v < total ? v : 0;
-    const int r = vv / p.row_vecs;
-    const int col = vv - r * p.row_vecs;
-    return (uint32_t)pos[r0 + r] * (uint32_t)p.src_stride + 16u * col;
-}
-
-__device__ __forceinline__ uint32_t pack_dst_off(const PackParams& p, int total, int v)
-{
-    if (v >= total) return kDropOffset;
-    const int r = v / p.row_vecs;
-    const int col = v - r * p.row_vecs;
-    return (uint32_t)r * (uint32_t)p.packed_stride + 16u * col;
-}
-
 __global__ __launch_bounds__(kThreads) void pack_kernel(PackParams p)
 {
     extern __shared__ int s_pos[];  // max(N, 256) ints
     __shared__ int s_red[kWaves];
     const int tid = threadIdx.x;
-    const int b = blockIdx.x, c = blockIdx.y;  // chunk slowest: chunk 0 of every image first
+    const int b = blockIdx.x, sl = blockIdx.y;
     if (b == p.B) {
-        if (c == 0) max_length_pass(p, s_pos, max(p.N, kThreads), s_red);
+        if (sl == 0) max_length_pass(p, s_pos, max(p.N, kThreads), s_red);
         return;
     }
     const int64_t img_row0 = (int64_t)b * p.N;
+    Prefix pf = prefix_begin(p.keep, img_row0);  // in flight during the ranking
     const int L = dev::rank_kept(p.keep + img_row0, p.N, s_pos, s_red);
-    const int r0 = c * p.rows;
-    if (c > 0 && r0 >= L) return;  // nothing to copy; chunk 0 still writes cu
-    const int nr = max(0, min(p.rows, L - r0));
-    const int total = nr * p.row_vecs;
+    if (L == 0 && sl > 0) return;  // uniform; slice 0 still writes cu
 
-    // source rows of image b; destination rows are placed once the offset is known
+    // this slice: vectors [c0, c0 + w) of every row.  Lane tid starts at
+    // vector tid of the slice (row tid / w, column tid % w) and steps by
+    // kThreads vectors at a time: a cursor (row, col) advanced by (dr, dc) with
+    // a carry, so no per-vector division.  A vector on a row >= L re-reads
+    // row 0 and its store gets an offset outside the destination.
+    const int c0 = sl * p.slice_vecs;
+    const int w = min(p.slice_vecs, p.row_vecs - c0);
+    const int dr = kThreads / w, dc = kThreads - dr * w;
+    const uint32_t sstride = (uint32_t)p.src_stride, pstride = (uint32_t)p.packed_stride;
     const auto rs = make_rsrc(p.src + img_row0 * p.src_stride, (uint32_t)(p.N * p.src_stride));
-    int v = tid;
-    u32x4 x0 = ld16(rs, pack_src_off(p, s_pos, r0, total, v));
-    u32x4 x1 = ld16(rs, pack_src_off(p, s_pos, r0, total, v + kThreads));
-    u32x4 x2 = ld16(rs, pack_src_off(p, s_pos, r0, total, v + 2 * kThreads));
-    u32x4 x3 = ld16(rs, pack_src_off(p, s_pos, r0, total, v + 3 * kThreads));
+    auto advance = [&](int& r, int& col) {
+        r += dr;
+        col += dc;
+        if (col >= w) {
+            col -= w;
+            r += 1;
+        }
+    };
+    // Loads the batch starting at cursor (r, col): all LDS position reads
+    // first, then all row loads (one LDS and one memory round trip).
+    auto load_batch = [&](int r, int col, u32x4 (&dst)[kPackUnroll]) {
+        int pos[kPackUnroll];
+        uint32_t cb[kPackUnroll];
+#pragma unroll
+        for (int j = 0; j < kPackUnroll; ++j) {
+            pos[j] = s_pos[r < L ? r : 0];
+            cb[j] = 16u * (uint32_t)(c0 + col);
+            advance(r, col);
+        }
+#pragma unroll
+        for (int j = 0; j < kPackUnroll; ++j) dst[j] = ld16(rs, (uint32_t)pos[j] * sstride + cb[j]);
+    };
+    int r = tid / w, col = tid - (tid / w) * w;  // cursor of the current batch
+    u32x4 x[kPackUnroll];
+    load_batch(r, col, x);
 
-    const int offset = count_kept_prefix(p.keep, img_row0, s_red);
-    if (c == 0 && tid == 0) {
-        p.cu[b + 1] = offset + L;
-        if (b == 0) p.cu[0] = 0;
+    const int offset = prefix_count(pf, p.keep, img_row0, s_red);
+    if (sl == 0) {
+        if (tid == 0) {
+            p.cu[b + 1] = offset + L;
+            if (b == 0) p.cu[0] = 0;
+        }
+        for (int t = tid; t < L; t += kThreads) p.gather[offset + t] = (int32_t)(img_row0 + s_pos[t]);
     }
-    if (tid < nr) p.gather[offset + r0 + tid] = (int32_t)(img_row0 + s_pos[r0 + tid]);
-    const auto rd = make_rsrc(p.packed + ((int64_t)offset + r0) * p.packed_stride,
-                              (uint32_t)(nr * p.packed_stride));
-    for (;;) {
-        st16(x0, rd, pack_dst_off(p, total, v));
-        st16(x1, rd, pack_dst_off(p, total, v + kThreads));
-        st16(x2, rd, pack_dst_off(p, total, v + 2 * kThreads));
-        st16(x3, rd, pack_dst_off(p, total, v + 3 * kThreads));
-        v += kBatch;
-        if (v - tid >= total) break;  // uniform: every lane sees the same v - tid
-        x0 = ld16(rs, pack_src_off(p, s_pos, r0, total, v));
-        x1 = ld16(rs, pack_src_off(p, s_pos, r0, total, v + kThreads));
-        x2 = ld16(rs, pack_src_off(p, s_pos, r0, total, v + 2 * kThreads));
-        x3 = ld16(rs, pack_src_off(p, s_pos, r0, total, v + 3 * kThreads));
+    if (L == 0) return;
+    const auto rd = make_rsrc(p.packed + (int64_t)offset * p.packed_stride, (uint32_t)L * pstride);
+    const int total = L * w;
+    for (int vb = 0;; vb += kPackUnroll * kThreads) {  // vb: the batch's first vector (uniform)
+        const bool more = vb + kPackUnroll * kThreads < total;
+        int rn = r, cn = col;
+#pragma unroll
+        for (int j = 0; j < kPackUnroll; ++j) advance(rn, cn);  // next batch's cursor
+        u32x4 y[kPackUnroll];
+        if (more) load_batch(rn, cn, y);
+#pragma unroll
+        for (int j = 0; j < kPackUnroll; ++j) {
+            st16(x[j], rd, r < L ? (uint32_t)r * pstride + 16u * (uint32_t)(c0 + col) : kDropOffset);
+            advance(r, col);
+        }
+        if (!more) break;
+#pragma unroll
+        for (int j = 0; j < kPackUnroll; ++j) x[j] = y[j];
     }
 }
 
@@ -336,8 +405,14 @@ int launch_pack(const uint8_t* keep, int32_t B, int32_t N, const void* src,
     p.B = B;
     p.N = N;
     p.row_vecs = row_bytes / 16;
-    p.rows = rows_per_chunk(row_bytes);
-    const dim3 grid(B + (max_seqlen_dev ? 1 : 0), (N + p.rows - 1) / p.rows);
+    p.n_magic = (uint32_t)((1ull << 32) / (uint64_t)N + 1ull);
+    // slices: enough for about kPackTargetGroups workgroups, each at least 16
+    // vectors (256 bytes) of every row
+    const int max_slices = max(1, p.row_vecs / 16);
+    const int slices = min(max_slices, max(1, (kPackTargetGroups + B - 1) / B));
+    p.slice_vecs = (p.row_vecs + slices - 1) / slices;
+    const int used = (p.row_vecs + p.slice_vecs - 1) / p.slice_vecs;  // no empty slice
+    const dim3 grid(B + (max_seqlen_dev ? 1 : 0), used);
     const size_t lds = sizeof(int) * (size_t)max(N, kThreads);
     hipLaunchKernelGGL(pack_kernel, grid, dim3(kThreads), lds, static_cast<hipStream_t>(stream), p);
     return (int)hipGetLastError();

@@ -97,20 +97,21 @@ extern "C" RAG_API rag_status rag_attn_padded(const void* q, const void* k, cons
 }
 
 extern "C" RAG_API rag_status rag_attn_gathered(const uint8_t* keep, int32_t B, int32_t N,
-                                                const void* q, const void* k, const void* v,
+                                                int32_t max_seqlen, const void* q, const void* k, const void* v,
                                                 int64_t q_row_stride, int64_t k_row_stride,
                                                 int64_t v_row_stride, rag_dtype in_dtype,
                                                 int32_t H, int32_t head_dim, float scale, void* o,
                                                 int64_t o_row_stride, rag_dtype out_dtype,
                                                 uint32_t flags, void* stream)
 {
-    rag_status s = rag::validate_attn_gathered(keep, B, N, q, k, v, q_row_stride, k_row_stride,
+    rag_status s = rag::validate_attn_gathered(keep, B, N, max_seqlen, q, k, v, q_row_stride, k_row_stride,
                                                v_row_stride, in_dtype, H, head_dim, scale, o,
                                                o_row_stride, out_dtype, flags);
     if (s != RAG_OK) return s;
     return hip_status(rag::launch_attn(q, k, v, q_row_stride, k_row_stride, v_row_stride, in_dtype,
-                                       nullptr, keep, B, N, N, B * N, H, scale, o, o_row_stride,
-                                       out_dtype, rag::kLayoutGathered, flags, stream),
+                                       nullptr, keep, B, N, max_seqlen ? max_seqlen : N, B * N, H,
+                                       scale, o, o_row_stride, out_dtype, rag::kLayoutGathered,
+                                       flags, stream),
                       "rag_attn_gathered launch");
 }
 
@@ -154,7 +155,8 @@ rag_status enqueue_fused(const rag_pipeline_desc& d, void* stream)
     const char* sr = static_cast<const char*>(d.src);
     const int64_t ss = d.src_row_stride / in_es;
     const int e = rag::launch_attn(sr, sr + C * in_es, sr + 2 * C * in_es, ss, ss, ss, d.in_dtype,
-                                   nullptr, d.keep, d.B, d.N, d.N, d.B * d.N, d.H, d.scale, d.dst,
+                                   nullptr, d.keep, d.B, d.N, d.max_seqlen ? d.max_seqlen : d.N,
+                                   d.B * d.N, d.H, d.scale, d.dst,
                                    d.dst_row_stride / out_es, d.out_dtype, rag::kLayoutGathered,
                                    d.unpack_flags, stream);
     return hip_status(e, "pipeline fused attn");
@@ -299,7 +301,7 @@ extern "C" RAG_API rag_status rag_measure_dispatch(rag_pipeline* p, int32_t warm
                                d.dst_row_stride / out_es, d.out_dtype, st);
     };
     auto fused = [&]() {
-        return rag_attn_gathered(d.keep, d.B, d.N, sr, sr + C * in_es, sr + 2 * C * in_es, ss, ss,
+        return rag_attn_gathered(d.keep, d.B, d.N, d.max_seqlen, sr, sr + C * in_es, sr + 2 * C * in_es, ss, ss,
                                  ss, d.in_dtype, d.H, d.head_dim, d.scale, d.dst,
                                  d.dst_row_stride / out_es, d.out_dtype, d.unpack_flags, st);
     };

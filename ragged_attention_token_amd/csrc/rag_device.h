@@ -34,14 +34,16 @@ __device__ __forceinline__ void st16(u32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t
 
 // Lists the positions n < N with krow[n] != 0 in ascending order into pos[]
 // (the rank of a kept position is its index in pos) and returns their number.
-// A 256-lane workgroup reads the row once: a 64-lane ballot plus popcount gives
-// each kept position its rank inside its wave, and a 4-entry LDS table (wsum)
-// the ranks of the waves before it.  Every thread of the workgroup must call it.
-__device__ __forceinline__ int rank_kept(const uint8_t* krow, int N, int* pos, int* wsum)
+// A workgroup of nw wave64s reads the row once: a 64-lane ballot plus popcount
+// gives each kept position its rank inside its wave, and an nw-entry LDS table
+// (wsum) the ranks of the waves before it.  Every thread of the workgroup must
+// call it; blockDim.x must be 64 * nw.
+__device__ __forceinline__ int rank_kept_waves(const uint8_t* krow, int N, int* pos, int* wsum,
+                                               int nw)
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int L = 0;
-    for (int base = 0; base < N; base += 256) {
+    for (int base = 0; base < N; base += 64 * nw) {
         const int n = base + tid;
         const bool kept = n < N && krow[n] != 0;
         const uint64_t m = __ballot(kept);
@@ -49,8 +51,7 @@ __device__ __forceinline__ int rank_kept(const uint8_t* krow, int N, int* pos, i
         if (lane == 0) wsum[wave] = __popcll(m);
         __syncthreads();
         int before = 0, total = 0;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
+        for (int w = 0; w < nw; ++w) {
             const int x = wsum[w];
             before += (w < wave) ? x : 0;
             total += x;
@@ -60,6 +61,12 @@ __device__ __forceinline__ int rank_kept(const uint8_t* krow, int N, int* pos, i
         __syncthreads();
     }
     return L;
+}
+
+// rank_kept_waves for a 256-thread workgroup (wsum holds 4 ints).
+__device__ __forceinline__ int rank_kept(const uint8_t* krow, int N, int* pos, int* wsum)
+{
+    return rank_kept_waves(krow, N, pos, wsum, 4);
 }
 
 }  // namespace dev

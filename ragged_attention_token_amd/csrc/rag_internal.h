@@ -32,7 +32,8 @@ rag_status validate_attn_padded(const void* q, const void* k, const void* v,
                                 int32_t in_dtype, const uint8_t* keep, int32_t B, int32_t N,
                                 int32_t H, int32_t head_dim, float scale, const void* o,
                                 int64_t o_row_stride, int32_t out_dtype);
-rag_status validate_attn_gathered(const uint8_t* keep, int32_t B, int32_t N, const void* q,
+rag_status validate_attn_gathered(const uint8_t* keep, int32_t B, int32_t N, int32_t max_seqlen,
+                                  const void* q,
                                   const void* k, const void* v, int64_t q_row_stride,
                                   int64_t k_row_stride, int64_t v_row_stride, int32_t in_dtype,
                                   int32_t H, int32_t head_dim, float scale, const void* o,
@@ -57,6 +58,7 @@ int launch_unpack(const void* packed, int64_t packed_row_stride, int32_t row_byt
 // layout: 0 = packed ragged rows (cu_seqlens), 1 = padded [B, N] rows with
 // dropped keys masked, 2 = gathered: the kept rows of the [B, N] layout, found
 // from the keep row, output written to those rows (flags: zero-dropped).
+// max_seqlen bounds the rows per image for layouts 0 and 2 (ignored for 1).
 enum { kLayoutRagged = 0, kLayoutPadded = 1, kLayoutGathered = 2 };
 int launch_attn(const void* q, const void* k, const void* v, int64_t q_row_stride,
                 int64_t k_row_stride, int64_t v_row_stride, int32_t in_dtype,

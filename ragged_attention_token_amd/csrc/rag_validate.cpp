@@ -186,14 +186,16 @@ rag_status validate_attn_padded(const void* q, const void* k, const void* v,
                       out_dtype);
 }
 
-rag_status validate_attn_gathered(const uint8_t* keep, int32_t B, int32_t N, const void* q,
-                                  const void* k, const void* v, int64_t q_row_stride,
+rag_status validate_attn_gathered(const uint8_t* keep, int32_t B, int32_t N, int32_t max_seqlen,
+                                  const void* q, const void* k, const void* v, int64_t q_row_stride,
                                   int64_t k_row_stride, int64_t v_row_stride, int32_t in_dtype,
                                   int32_t H, int32_t head_dim, float scale, const void* o,
                                   int64_t o_row_stride, int32_t out_dtype, uint32_t flags)
 {
     if (flags & ~RAG_UNPACK_ZERO_DROPPED)
         return set_error(RAG_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
+    if (max_seqlen < 0 || max_seqlen > N)
+        return set_error(RAG_ERR_INVALID_ARG, "max_seqlen=%d must lie in [0, N=%d]", max_seqlen, N);
     return validate_attn_padded(q, k, v, q_row_stride, k_row_stride, v_row_stride, in_dtype, keep,
                                 B, N, H, head_dim, scale, o, o_row_stride, out_dtype);
 }
@@ -231,7 +233,7 @@ rag_status validate_pipeline(const rag_pipeline_desc* d)
     if (s != RAG_OK) return s;
     if (d->src_row_stride % in_es || d->dst_row_stride % out_es)
         return set_error(RAG_ERR_ALIGNMENT, "row strides must be whole elements");
-    return validate_attn_gathered(d->keep, d->B, d->N, d->src, d->src, d->src,
+    return validate_attn_gathered(d->keep, d->B, d->N, d->max_seqlen, d->src, d->src, d->src,
                                   d->src_row_stride / in_es, d->src_row_stride / in_es,
                                   d->src_row_stride / in_es, d->in_dtype, d->H, d->head_dim,
                                   d->scale, d->dst, d->dst_row_stride / out_es, d->out_dtype,

@@ -149,12 +149,14 @@ def test_binding_refuses_cpu_tensors():
 
 def test_attn_gathered_rejects(lib):
     def call(keep=A, B=4, N=197, q=A, qs=1152, dt=BF16, H=6, hd=64, scale=0.125, o=A, os_=384,
-             odt=F32, flags=0):
-        return lib.rag_attn_gathered(keep, B, N, q, q, q, qs, qs, qs, dt, H, hd, scale, o, os_, odt,
-                                     flags, None)
+             odt=F32, flags=0, max_seqlen=0):
+        return lib.rag_attn_gathered(keep, B, N, max_seqlen, q, q, q, qs, qs, qs, dt, H, hd, scale,
+                                     o, os_, odt, flags, None)
     assert call(flags=2) == UNSUPPORTED and "flags" in binding.last_error()
     assert call(keep=None) == INVALID
     assert call(N=0) == INVALID
+    assert call(max_seqlen=-1) == INVALID and "max_seqlen" in binding.last_error()
+    assert call(max_seqlen=198) == INVALID
     assert call(hd=128) == UNSUPPORTED
     assert call(q=A + 4) == ALIGN
     assert call(scale=float("nan")) == INVALID

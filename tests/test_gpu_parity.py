@@ -375,3 +375,77 @@ def test_gathered_zero_dropped_and_fused_pipeline():
     st = pipe.measure_stages(iters=10)
     assert st["fused_pass"] > 0
     pipe.close()
+
+
+def test_lds_resident_and_tile_kernels_agree_bit_for_bit():
+    """bf16 input takes the LDS-resident kernel when max_seqlen is small enough
+    for the image's K and V to sit in LDS, and the 64-key tile kernel otherwise.
+    Both do the same arithmetic in the same order, so the outputs are equal bit
+    for bit; the oracle checks the values."""
+    w = wl.custom(B=4, N=577, H=2, lengths=[200, 5, 77, 0], seed=15)
+    ref = _oracle_pack(w)
+    g = gpu_pack(w)
+    for out_dtype in (torch.float32, torch.bfloat16):
+        tile = gpu_attn(g["packed"], g["cu"], w, out_dtype, max_seqlen=577)
+        lds = gpu_attn(g["packed"], g["cu"], w, out_dtype, max_seqlen=200)
+        assert torch.equal(tile[:w.T].view(torch.uint8), lds[:w.T].view(torch.uint8)), out_dtype
+    o32 = gpu_attn(g["packed"], g["cu"], w, torch.float32, max_seqlen=200)
+    o16 = gpu_attn(g["packed"], g["cu"], w, torch.bfloat16, max_seqlen=200)
+    _check_attn(w, ref, o32, o16, range(w.B))
+
+
+def _truncate_keep(keep: np.ndarray, m: int) -> np.ndarray:
+    """The first m kept positions of every image (what a max_seqlen of m keeps)."""
+    out = np.zeros_like(keep)
+    for b in range(keep.shape[0]):
+        pos = np.flatnonzero(keep[b])[:m]
+        out[b, pos] = keep[b, pos]
+    return out
+
+
+def test_gathered_max_seqlen_bound_and_truncation():
+    w = wl.custom(B=6, N=197, H=6, lengths=[40, 40, 12, 0, 40, 33], seed=16)
+    src = to_gpu_rows(w)
+    keep = torch.from_numpy(w.keep).cuda()
+    C = w.C
+
+    def run(m):
+        o = sentinel_like((w.B * w.N, C), torch.float32)
+        binding.rag_attn_gathered(keep, src[:, :C], src[:, C:2 * C], src[:, 2 * C:], o, H=w.H,
+                                  scale=w.scale, max_seqlen=m)
+        torch.cuda.synchronize()
+        return o
+
+    full = run(0)
+    tight = run(40)  # the exact bound: same result, smaller launch
+    assert torch.equal(full.view(torch.int32), tight.view(torch.int32))
+    # a bound below some images' kept count: those images are their first 25
+    # kept rows; the later kept rows are not written
+    got = run(25).cpu().numpy().astype(np.float64)
+    kt = _truncate_keep(w.keep, 25)
+    packed_t, cu_t, gather_t = oracle.pack(kt, wl.rows(w))
+    for b in range(w.B):
+        s, e = int(cu_t[b]), int(cu_t[b + 1])
+        if e > s:
+            q, k, v = wl.split_qkv(packed_t[s:e], C)
+            want = oracle.attn(q, k, v, np.array([0, e - s], np.int32), w.H, w.d, w.scale)
+            assert np.abs(got[gather_t[s:e]] - want).max() <= ATOL, b
+    unwritten = np.setdiff1d(np.arange(w.B * w.N), gather_t)
+    assert (as_numpy_rows(run(25))[unwritten].view(np.uint8) == SENTINEL_BYTE).all()
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.3, 1e-6, 2.5])
+def test_attention_any_scale(scale):
+    """The kernels fold the scale's sign into Q (a zero scale becomes a tiny
+    positive one); the oracle takes the scale as given.  Both kernels (LDS
+    resident: max_seqlen 130; 64-key tiles: fp32 input) are covered.  A zero
+    scale gives every image the mean of its V rows."""
+    for w in (wl.custom(B=3, N=130, H=2, lengths=[130, 7, 64], seed=17),
+              wl.custom(B=2, N=70, H=2, lengths=[70, 3], dtype="f32", seed=18)):
+        w.scale = scale
+        ref = _oracle_pack(w)
+        g = gpu_pack(w)
+        o32 = gpu_attn(g["packed"], g["cu"], w, torch.float32)
+        o16 = gpu_attn(g["packed"], g["cu"], w, torch.bfloat16)
+        worst = _check_attn(w, ref, o32, o16, range(w.B))
+        print("scale", scale, w.dtype, "max abs err", worst, flush=True)
