@@ -17,7 +17,8 @@ the host dispatch floor (measured in C++), and the CPU oracle's throughput on th
 host cores.
 
 Other modes (used under rocprofv3, see profiles/):
-    --kernels-only   run only the timed pipeline steps (no sweep, no oracle)
+    --kernels-only   run only the timed pipeline steps, then as many fused passes
+                     (no sweep, no oracle)
     --pmc-calib      run a plain device copy of a known size (counter scale)
 """
 from __future__ import annotations
@@ -274,6 +275,11 @@ def main():
     tokens_per_s = w.T * args.steps / wall
     print("timed %d steps: %.3f ms/step" % (args.steps, ms_per_step), file=sys.stderr, flush=True)
     if args.kernels_only:
+        # the same passes as one gathered launch each, so that a profiler run of
+        # this mode also sees the fused kernel
+        for _ in range(args.steps):
+            bf.pipe.launch_fused()
+        torch.cuda.synchronize()
         print(json.dumps({"metric": METRIC, "value": tokens_per_s, "unit": "packed tokens/s",
                           "ms_per_step": ms_per_step, "steps": args.steps}))
         return

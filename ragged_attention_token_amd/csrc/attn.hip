@@ -302,7 +302,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
     __bf16* sVt = sK + NP * K_PLANE;
     __shared__ uint8_t sKeep[kBN];
     extern __shared__ int s_pos[];  // gathered: the image's kept positions by rank (N ints)
-    __shared__ int s_wsum[4];
+    __shared__ int s_wsum[16];  // keep ranking: up to 4 planes x 4 waves
 
     // ---- which (head, image, q-tile): a 3-D grid with the q-tile slowest, so
     // that the first q-tile of every (image, head) -- the only one most pruned
@@ -318,7 +318,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
         L = p.N;
     } else if constexpr (GATHERED) {
         row0 = (int64_t)b * p.N;
-        L = min(dev::rank_kept(p.keep + row0, p.N, s_pos, s_wsum), p.max_len);
+        L = p.N <= 4 * kThreads ? dev::rank_kept_planes<4>(p.keep + row0, p.N, s_pos, s_wsum, 4)
+                                : dev::rank_kept(p.keep + row0, p.N, s_pos, s_wsum);
+        L = min(L, p.max_len);
         if (p.zero_dropped && qt == 0) zero_dropped_head<OUT_F32>(p, row0, h);
     } else {
         const int s = min(max(p.cu[b], 0), p.total_rows);
@@ -537,7 +539,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void attn_lds_kernel(AttnParams p)
     constexpr bool GATHERED = LAYOUT == kGathered;
     constexpr int OES = OUT_F32 ? 4 : 2;
     extern __shared__ __attribute__((aligned(16))) char lds[];
-    __shared__ int s_wsum[kMaxWaves];
+    __shared__ int s_wsum[4 * kMaxWaves];  // keep ranking: up to 4 planes x W waves
 
     const int h = blockIdx.x, b = blockIdx.y, qs = blockIdx.z;
     const int nw = blockDim.x >> 6;
@@ -561,7 +563,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void attn_lds_kernel(AttnParams p)
         for (int n = tid; n < nkeep; n += blockDim.x) s_keep[n] = n < p.N ? p.keep[row0 + n] : 0;
     } else if constexpr (GATHERED) {
         row0 = (int64_t)b * p.N;
-        L = min(dev::rank_kept_waves(p.keep + row0, p.N, s_pos, s_wsum, nw), p.max_len);
+        L = p.N <= 4 * 64 * nw ? dev::rank_kept_planes<4>(p.keep + row0, p.N, s_pos, s_wsum, nw)
+                               : dev::rank_kept_waves(p.keep + row0, p.N, s_pos, s_wsum, nw);
+        L = min(L, p.max_len);
         if (p.zero_dropped && qs == 0) zero_dropped_head<OUT_F32>(p, row0, h);
     } else {
         const int s = min(max(p.cu[b], 0), p.total_rows);

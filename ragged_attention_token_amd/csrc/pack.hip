@@ -13,14 +13,15 @@
 // workgroup of an image with kept rows has work whatever the prune rate, and
 // the grid (B x S, S chosen so that about 1024 workgroups cover the batch) is
 // filled in one dispatch round.
-//   1. the offset of image b (number of kept tokens in images 0..b-1) is
-//      counted from 16-byte words of the keep mask; those loads are issued
-//      first so that they travel together with the keep row's (each workgroup
-//      recounts the prefix, at most B*N bytes that stay in L2: no atomics and
-//      no inter-workgroup waits, so the result is deterministic);
-//   2. ranks inside image b: the image's N keep bytes are read once; a 64-lane
+//   1. ranks inside image b: the image's N keep bytes are read once; a 64-lane
 //      ballot + popcount gives each kept position its rank, and the kept
 //      positions are listed by rank in LDS;
+//   2. the offset of image b (number of kept tokens in images 0..b-1) is
+//      counted from 16-byte words of the keep mask; those loads are issued
+//      right after the image's keep bytes, so they travel during the ranking
+//      (each workgroup recounts the prefix, at most B*N bytes that stay in L2:
+//      no atomics and no inter-workgroup waits, so the result is
+//      deterministic);
 //   3. the slice's source rows are requested (up to kUnroll 16-byte loads per
 //      lane in flight), the prefix count is reduced, and the rows are stored.
 // Unpack: workgroup (b, c) serves packed rows [c*R, c*R + R) of image b; the
@@ -243,8 +244,20 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(PackParams p)
         return;
     }
     const int64_t img_row0 = (int64_t)b * p.N;
-    Prefix pf = prefix_begin(p.keep, img_row0);  // in flight during the ranking
-    const int L = dev::rank_kept(p.keep + img_row0, p.N, s_pos, s_red);
+    // The image's keep bytes are requested first and the prefix words after
+    // them, so the ranking waits for the former only.
+    int L;
+    Prefix pf;
+    if (p.N <= kThreads) {
+        // (a buffer load: positions past N read as zero, no branch)
+        const uint32_t kbyte = __builtin_amdgcn_raw_buffer_load_b8(
+            make_rsrc(p.keep + img_row0, (uint32_t)p.N), (uint32_t)tid, 0, 0);
+        pf = prefix_begin(p.keep, img_row0);
+        L = dev::rank_kept_preloaded(kbyte != 0u, s_pos, s_red, kWaves);
+    } else {
+        pf = prefix_begin(p.keep, img_row0);
+        L = dev::rank_kept(p.keep + img_row0, p.N, s_pos, s_red);
+    }
     if (L == 0 && sl > 0) return;  // uniform; slice 0 still writes cu
 
     // this slice: vectors [c0, c0 + w) of every row.  Lane tid starts at

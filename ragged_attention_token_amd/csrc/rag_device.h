@@ -63,6 +63,66 @@ __device__ __forceinline__ int rank_kept_waves(const uint8_t* krow, int N, int* 
     return L;
 }
 
+// rank_kept_waves for rows of at most 64 * nw positions whose keep byte each
+// thread has already loaded (kept = this thread's position is kept), so that
+// the caller can issue other loads between the byte load and the ranking.
+__device__ __forceinline__ int rank_kept_preloaded(bool kept, int* pos, int* wsum, int nw)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint64_t m = __ballot(kept);
+    const int below = __popcll(m & ((1ull << lane) - 1ull));
+    if (lane == 0) wsum[wave] = __popcll(m);
+    __syncthreads();
+    int before = 0, total = 0;
+    for (int w = 0; w < nw; ++w) {
+        const int x = wsum[w];
+        before += (w < wave) ? x : 0;
+        total += x;
+    }
+    if (kept) pos[before + below] = tid;
+    __syncthreads();
+    return total;
+}
+
+// rank_kept_waves for rows of at most KMAX * 64 * nw positions, with every
+// keep byte requested before the first barrier (one memory round trip):
+// thread t of the workgroup covers positions t + k * 64 nw for k < KMAX, read
+// through a buffer resource over the row (positions past N read as zero).
+// Positions are ranked plane by plane (plane k = [k 64 nw, (k+1) 64 nw)),
+// which is ascending order.  wsum holds KMAX * nw ints.
+template <int KMAX>
+__device__ __forceinline__ int rank_kept_planes(const uint8_t* krow, int N, int* pos, int* wsum,
+                                                int nw)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nt = 64 * nw;
+    const auto rk = make_rsrc(krow, (uint32_t)N);
+    uint32_t kb[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) kb[k] = __builtin_amdgcn_raw_buffer_load_b8(rk, (uint32_t)(tid + k * nt), 0, 0);
+    int below[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        const uint64_t m = __ballot(kb[k] != 0u);
+        below[k] = __popcll(m & ((1ull << lane) - 1ull));
+        if (lane == 0) wsum[k * nw + wave] = __popcll(m);
+    }
+    __syncthreads();
+    int total = 0;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        int before = 0, plane = 0;
+        for (int w = 0; w < nw; ++w) {
+            const int x = wsum[k * nw + w];
+            before += (w < wave) ? x : 0;
+            plane += x;
+        }
+        if (kb[k] != 0u) pos[total + before + below[k]] = tid + k * nt;
+        total += plane;
+    }
+    __syncthreads();
+    return total;
+}
+
 // rank_kept_waves for a 256-thread workgroup (wsum holds 4 ints).
 __device__ __forceinline__ int rank_kept(const uint8_t* krow, int N, int* pos, int* wsum)
 {
