@@ -9,33 +9,35 @@
 // section 問題) runs the same attention over all N rows of every image with the
 // dropped keys masked out.
 //
-// Kernel design (ours, for gfx950; the pages' Triton kernel is not followed):
-//   * one workgroup = one (head, image, q-tile of 64 rows); 4 wave64s, each
-//     owning 16 query rows.  The q-tile is the slowest grid dimension, so the
-//     first tile of every (image, head) is dispatched before the later tiles,
-//     most of which exit at once for pruned sequences (the grid is sized from
-//     the host-side max_seqlen, never from device data).
-//   * all global traffic goes through buffer resources whose range ends at the
-//     image's last row: loads past the sequence end return zeros and stores
-//     past it are dropped by the hardware, so no per-lane predicate is needed
-//     and no uninitialised value can reach an MFMA.
-//   * K and V are staged through LDS 64 keys at a time: K row-major, V
-//     transposed (d-major) so that each lane's MFMA operand is contiguous.  The
-//     next tile's loads are issued into registers before the current tile is
-//     computed, so a long sequence costs one memory round trip, not one per tile.
+// Kernel design (ours, for gfx950; the pages' Triton kernel is not followed).
+// Two kernels compute it with the same arithmetic in the same order, so the
+// one the host picks (by input dtype and max_seqlen) never changes a bit:
+//   * attn_lds_kernel (bf16 input, up to 256 keys): an image's whole K and V
+//     for one head are copied straight into LDS by buffer loads that write
+//     LDS, one barrier, then every wave runs its 16-row query blocks over all
+//     keys with no further synchronisation (see the comment at the kernel);
+//   * attn_kernel (fp32 input, or longer sequences): one workgroup = one
+//     (head, image, q-tile of 64 rows), 4 wave64s of 16 query rows, K / V
+//     staged through LDS 64 keys at a time (K row-major, V transposed), the
+//     next tile's loads in registers while the current tile computes.
+// Both:
+//   * all global traffic goes through buffer resources whose range ends at
+//     the image's last row: loads past the sequence end return zeros and
+//     stores past it are dropped by the hardware, so no per-lane predicate is
+//     needed and no uninitialised value can reach an MFMA;
 //   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (fp32 accumulate): each lane
 //     holds the scores of ONE query row (lane & 15) for 4 keys per 16-key
-//     block, so the row max / row sum take two v_permlane{16,32}_swap steps.
-//   * online softmax in fp32 with exp2; masking only in a sequence's last,
-//     partial tile; no rescale on the first tile.  The probabilities are split
-//     into bf16 high + low parts and O^T += V^T P^T runs both through the same
-//     MFMA, so P is carried to about 16 mantissa bits.  fp32 inputs are split
-//     the same way (hi/lo for Q, K, V).
-//   * the probabilities never leave registers: the MFMA result layout of S^T is
-//     used directly as the B operand of the P.V product (keys are a summation
-//     index, so the k-order only has to agree between the two operands).
-//   * the output goes through LDS so that each row segment is written by
-//     consecutive lanes with 16-byte stores.
+//     block, so the row max takes two v_permlane{16,32}_swap steps;
+//   * online softmax in fp32 with exp2, a lazily moved reference maximum and
+//     row sums from the MFMA unit (see "online softmax shared by both
+//     kernels"); masking only in a sequence's last, partial tile;
+//   * the probabilities are split into bf16 high + low parts and O^T += V^T P^T
+//     runs both through the same MFMA, so P is carried to about 16 mantissa
+//     bits; fp32 inputs are split the same way (hi/lo for Q, K, V);
+//   * the probabilities never leave registers: the MFMA result layout of S^T
+//     is used directly as the B operand of the P.V product (keys are a
+//     summation index, so the k-order only has to agree between the two
+//     operands).
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -399,63 +401,63 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
     // then compute it; FULL: all 64 keys present (no key-range masking).  The
     // full tiles run in one loop and the partial last tile after it.
     auto tile = [&](auto full_tag, const int kt) {
-            constexpr bool FULL = decltype(full_tag)::value;
-            const int nk = min(kBN, L - kt);
-            if (kt > 0) __syncthreads();  // the previous tile is no longer read
-            stash();
-            if (kt + kBN < L) fetch(kt + kBN);  // in flight while this tile is computed
-            if constexpr (PADDED) {
-                if (tid < kBN) sKeep[tid] = (tid < nk) ? p.keep[row0 + kt + tid] : 0;
-            }
-            __syncthreads();
-            if (!wave_active) return;
+        constexpr bool FULL = decltype(full_tag)::value;
+        const int nk = min(kBN, L - kt);
+        if (kt > 0) __syncthreads();  // the previous tile is no longer read
+        stash();
+        if (kt + kBN < L) fetch(kt + kBN);  // in flight while this tile is computed
+        if constexpr (PADDED) {
+            if (tid < kBN) sKeep[tid] = (tid < nk) ? p.keep[row0 + kt + tid] : 0;
+        }
+        __syncthreads();
+        if (!wave_active) return;
 
-            // ---- S^T = K Q^T: block kb holds keys kt+16kb+4g+i (i<4), query r16
-            f32x4 s[4];
+        // ---- S^T = K Q^T: block kb holds keys kt+16kb+4g+i (i<4), query r16
+        f32x4 s[4];
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                if (FULL || kb == 0 || 16 * kb < nk) {
-                    const __bf16* kr = &sK[(kb * 16 + r16) * kKS + 8 * g];
-                    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kr);
-                    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kr + 32);
-                    s[kb] = mfma(a0, qh0, f32x4{0.f, 0.f, 0.f, 0.f});
-                    s[kb] = mfma(a1, qh1, s[kb]);
+        for (int kb = 0; kb < 4; ++kb) {
+            if (FULL || kb == 0 || 16 * kb < nk) {
+                const __bf16* kr = &sK[(kb * 16 + r16) * kKS + 8 * g];
+                const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kr);
+                const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kr + 32);
+                s[kb] = mfma(a0, qh0, f32x4{0.f, 0.f, 0.f, 0.f});
+                s[kb] = mfma(a1, qh1, s[kb]);
+                if constexpr (IN_F32) {
+                    const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(kr + K_PLANE);
+                    const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(kr + K_PLANE + 32);
+                    s[kb] = mfma(b0, qh0, s[kb]);
+                    s[kb] = mfma(b1, qh1, s[kb]);
+                    s[kb] = mfma(a0, ql0, s[kb]);
+                    s[kb] = mfma(a1, ql1, s[kb]);
+                }
+            } else {
+                s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};  // absent keys, masked below
+            }
+        }
+        online_probs<FULL, PADDED>(s, nk, sKeep, g, c, kt == 0, st);
+        // ---- O^T += V^T P^T, 32 keys per MFMA ----------------------------
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+            if (FULL || cc * 32 < nk) {
+                bf16x8 ph, pl;
+                p_operand(s, cc, ph, pl, st);
+#pragma unroll
+                for (int db = 0; db < 4; ++db) {
+                    const int vo = (db * 16 + r16) * kVS + 32 * cc + 4 * g;
+                    const bf16x4 v0 = *reinterpret_cast<const bf16x4*>(&sVt[vo]);
+                    const bf16x4 v1 = *reinterpret_cast<const bf16x4*>(&sVt[vo + 16]);
+                    const bf16x8 av = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+                    st.acc[db] = mfma(av, ph, st.acc[db]);
+                    st.acc[db] = mfma(av, pl, st.acc[db]);
                     if constexpr (IN_F32) {
-                        const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(kr + K_PLANE);
-                        const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(kr + K_PLANE + 32);
-                        s[kb] = mfma(b0, qh0, s[kb]);
-                        s[kb] = mfma(b1, qh1, s[kb]);
-                        s[kb] = mfma(a0, ql0, s[kb]);
-                        s[kb] = mfma(a1, ql1, s[kb]);
-                    }
-                } else {
-                    s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};  // absent keys, masked below
-                }
-            }
-            online_probs<FULL, PADDED>(s, nk, sKeep, g, c, kt == 0, st);
-            // ---- O^T += V^T P^T, 32 keys per MFMA ----------------------------
-#pragma unroll
-            for (int cc = 0; cc < 2; ++cc) {
-                if (FULL || cc * 32 < nk) {
-                    bf16x8 ph, pl;
-                    p_operand(s, cc, ph, pl, st);
-#pragma unroll
-                    for (int db = 0; db < 4; ++db) {
-                        const int vo = (db * 16 + r16) * kVS + 32 * cc + 4 * g;
-                        const bf16x4 v0 = *reinterpret_cast<const bf16x4*>(&sVt[vo]);
-                        const bf16x4 v1 = *reinterpret_cast<const bf16x4*>(&sVt[vo + 16]);
-                        const bf16x8 av = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-                        st.acc[db] = mfma(av, ph, st.acc[db]);
-                        st.acc[db] = mfma(av, pl, st.acc[db]);
-                        if constexpr (IN_F32) {
-                            const bf16x4 w0 = *reinterpret_cast<const bf16x4*>(&sVt[V_PLANE + vo]);
-                            const bf16x4 w1 = *reinterpret_cast<const bf16x4*>(&sVt[V_PLANE + vo + 16]);
-                            const bf16x8 al = __builtin_shufflevector(w0, w1, 0, 1, 2, 3, 4, 5, 6, 7);
-                            st.acc[db] = mfma(al, ph, st.acc[db]);
-                        }
+                        const bf16x4 w0 = *reinterpret_cast<const bf16x4*>(&sVt[V_PLANE + vo]);
+                        const bf16x4 w1 = *reinterpret_cast<const bf16x4*>(&sVt[V_PLANE + vo + 16]);
+                        const bf16x8 al = __builtin_shufflevector(w0, w1, 0, 1, 2, 3, 4, 5, 6, 7);
+                        st.acc[db] = mfma(al, ph, st.acc[db]);
                     }
                 }
             }
+        }
     };
     int kt = 0;
     for (; kt + kBN <= L; kt += kBN) tile(std::true_type{}, kt);
@@ -644,15 +646,15 @@ __global__ __launch_bounds__(64 * kMaxWaves) void attn_lds_kernel(AttnParams p)
 
     const auto ro = make_rsrc(static_cast<char*>(p.o) + (row0 * p.os + hoff) * OES,
                               (uint32_t)(span - 1) * osb + kD * OES);
-    for (;;) {
-    bf16x8 unused0 = {}, unused1 = {};
-    const float c = fold_scale(p.scale_log2, qa0, qa1, unused0, unused1);
-    Online st;
-    online_init(st);
+    for (;;) {  // the wave's query blocks
+        bf16x8 unused0 = {}, unused1 = {};
+        const float c = fold_scale(p.scale_log2, qa0, qa1, unused0, unused1);
+        Online st;
+        online_init(st);
 
-    // One tile at key kt; FULL: all 64 keys present (no key-range masking).
-    // The full tiles run in one loop and the partial last tile after it.
-    auto tile = [&](auto full_tag, const int kt) {
+        // One tile at key kt; FULL: all 64 keys present (no key-range masking).
+        // The full tiles run in one loop and the partial last tile after it.
+        auto tile = [&](auto full_tag, const int kt) {
             constexpr bool FULL = decltype(full_tag)::value;
             const int nk = min(kBN, L - kt);
             const char* kbase = sK + kt * kRowBytes;
@@ -687,31 +689,31 @@ __global__ __launch_bounds__(64 * kMaxWaves) void attn_lds_kernel(AttnParams p)
                     }
                 }
             }
-    };
-    int kt = 0;
-    for (; kt + kBN <= L; kt += kBN) tile(std::true_type{}, kt);
-    if (kt < L) tile(std::false_type{}, kt);
+        };
+        int kt = 0;
+        for (; kt + kBN <= L; kt += kBN) tile(std::true_type{}, kt);
+        if (kt < L) tile(std::false_type{}, kt);
 
-    // ---- epilogue: O = acc / l; lane holds O[16 qb + r16][16 db + 4g + i] ----
-    const float inv = online_inv(st);
-    const uint32_t orow = row_off(16 * qb + r16, osb);
+        // ---- epilogue: O = acc / l; lane holds O[16 qb + r16][16 db + 4g + i] ----
+        const float inv = online_inv(st);
+        const uint32_t orow = row_off(16 * qb + r16, osb);
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-        const f32x4 r = st.acc[db] * inv;
-        const uint32_t off = orow + (uint32_t)(16 * db + 4 * g) * OES;
-        if constexpr (OUT_F32) {
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, r), ro, off, 0, 0);
-        } else {
-            bf16x4 o4;
+        for (int db = 0; db < 4; ++db) {
+            const f32x4 r = st.acc[db] * inv;
+            const uint32_t off = orow + (uint32_t)(16 * db + 4 * g) * OES;
+            if constexpr (OUT_F32) {
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, r), ro, off, 0, 0);
+            } else {
+                bf16x4 o4;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) o4[i] = static_cast<__bf16>(r[i]);
-            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o4), ro, off, 0, 0);
+                for (int i = 0; i < 4; ++i) o4[i] = static_cast<__bf16>(r[i]);
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o4), ro, off, 0, 0);
+            }
         }
-    }
-    if constexpr (!MULTI) break;  // (single-block launches: one block per wave)
-    qb += qstride;
-    if (qb >= nqb) break;
-    load_q(qb);
+        if constexpr (!MULTI) break;  // (single-block launches: one block per wave)
+        qb += qstride;
+        if (qb >= nqb) break;
+        load_q(qb);
     }
 }
 
