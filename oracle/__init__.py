@@ -14,7 +14,10 @@ only marshals numpy arrays into it.  Sources for each routine are cited in
 * ragged attention: "Dispatch-Aware Ragged Attention for Pruned Vision
   Transformers", abstract (bidirectional attention over each image's surviving
   tokens) and the same blog section (the ragged attention kernel);
-* padded attention: the blog's section 問題 (problem): pad to one length, mask.
+* padded attention: the blog's section 問題 (problem): pad to one length, mask;
+* re-pack (a later pruning stage on packed tokens): the paper's earlier
+  abstract (fugumt.com summary page) lists the pruning methods, which drop
+  tokens at more than one depth; the compaction is the pack step above.
 
 Pins (see ``tests/test_oracle.py``): exhaustive bf16 decode against torch's own
 conversion; pack against ``numpy.flatnonzero``; hand-derived worked examples under
@@ -60,6 +63,8 @@ def _bind(path: str):
     lib.oracle_pack.restype = i64
     lib.oracle_unpack.argtypes = [vp, i64, i32, vp, vp, i32, vp, i64]
     lib.oracle_unpack.restype = None
+    lib.oracle_repack.argtypes = [vp, vp, vp, i32, vp, i64, i32, vp, i64, vp, vp]
+    lib.oracle_repack.restype = i64
     lib.oracle_attn.argtypes = [vp, vp, vp, i64, i64, i64, i32, vp, i32, i32, i32, dbl, vp,
                                 i64, vp, vp]
     lib.oracle_attn.restype = ctypes.c_int
@@ -110,6 +115,30 @@ def pack(keep: np.ndarray, src_rows: np.ndarray):
     T = _load().oracle_pack(_ptr(keep), B, N, _ptr(src), row_bytes, row_bytes, _ptr(packed),
                             row_bytes, _ptr(cu), _ptr(gather))
     return packed[:T].copy(), cu, gather[:T].copy()
+
+
+def repack(keep_packed: np.ndarray, cu_in: np.ndarray, gather_in: np.ndarray,
+           packed_rows: np.ndarray):
+    """Re-prune packed rows: keep_packed[t] != 0 keeps packed row t of the image
+    cu_in says it belongs to.  Returns (rows [T', row], cu_out int32 [B+1],
+    gather_out int32 [T']) with gather_out composed through gather_in."""
+    cu = np.ascontiguousarray(cu_in, dtype=np.int32)
+    B = cu.shape[0] - 1
+    T = int(cu[B])
+    if cu[0] != 0 or (np.diff(cu) < 0).any():
+        raise ValueError("cu_in must start at 0 and not decrease")
+    keep = np.ascontiguousarray(keep_packed, dtype=np.uint8)
+    g = np.ascontiguousarray(gather_in, dtype=np.int32)
+    src = np.ascontiguousarray(packed_rows).reshape(packed_rows.shape[0], -1)
+    if keep.shape[0] < T or g.shape[0] < T or src.shape[0] < T:
+        raise ValueError("keep / gather / rows shorter than cu_in[B]")
+    row_bytes = src.shape[1] * src.itemsize
+    out = np.zeros((max(T, 1), src.shape[1]), dtype=src.dtype)
+    cu_out = np.zeros(B + 1, dtype=np.int32)
+    g_out = np.zeros(max(T, 1), dtype=np.int32)
+    T2 = _load().oracle_repack(_ptr(keep), _ptr(cu), _ptr(g), B, _ptr(src), row_bytes, row_bytes,
+                               _ptr(out), row_bytes, _ptr(cu_out), _ptr(g_out))
+    return out[:T2].copy(), cu_out, g_out[:T2].copy()
 
 
 def unpack(packed: np.ndarray, cu_seqlens: np.ndarray, gather_idx: np.ndarray,

@@ -22,6 +22,8 @@
  *               results back to their original batch positions via cu_seqlens.
  *   [blog-problem] same page, section "問題：填充與派遣的瓶頸" (problem): the
  *               padded form pads every image to one length and masks.
+ *   [abstract-v1] the same paper's earlier abstract (fugumt.com summary
+ *               page): the four pruning methods it evaluates.
  *
  * Every routine below is the plain definition written out, with no blocking,
  * fusion or reordering: loops in the order the definition reads.
@@ -91,6 +93,40 @@ int64_t oracle_pack(const uint8_t* keep, int32_t B, int32_t N,
         cu_seqlens[b + 1] = (int32_t)t;
     }
     return t;
+}
+
+/*
+ * Re-pack: a later pruning stage on tokens that are already packed.  The
+ * pages' pruning methods ([abstract-v1]: Threshold-L2, DynamicViT, EViT, ATS)
+ * drop tokens at more than one depth of the network; the plainest reading of
+ * the pack step ([blog-method]) for a later stage is the same compaction
+ * applied to the packed rows, with each surviving row remembering its place
+ * in the original [B, N] batch.
+ *   Image b of the input is packed rows cu_in[b] .. cu_in[b+1]-1.  For each
+ *   image b in order, idx_b is the ascending list of those rows t with
+ *   keep[t] != 0 (one keep byte per packed row).  cu_out[0] = 0,
+ *   cu_out[b+1] = cu_out[b] + |idx_b|.  gather_out[cu_out[b] + i] =
+ *   gather_in[idx_b[i]] (the original batch row, not the packed row), and
+ *   output row cu_out[b] + i is a byte copy of input row idx_b[i].
+ * Row strides are in bytes.  Returns the total T' = cu_out[B].
+ */
+int64_t oracle_repack(const uint8_t* keep, const int32_t* cu_in, const int32_t* gather_in,
+                      int32_t B, const uint8_t* src, int64_t src_row_stride, int32_t row_bytes,
+                      uint8_t* out, int64_t out_row_stride, int32_t* cu_out, int32_t* gather_out)
+{
+    int64_t t_out = 0;
+    cu_out[0] = 0;
+    for (int32_t b = 0; b < B; ++b) {
+        for (int64_t t = cu_in[b]; t < cu_in[b + 1]; ++t) {
+            if (keep[t] != 0) {
+                gather_out[t_out] = gather_in[t];
+                memcpy(out + t_out * out_row_stride, src + t * src_row_stride, (size_t)row_bytes);
+                ++t_out;
+            }
+        }
+        cu_out[b + 1] = (int32_t)t_out;
+    }
+    return t_out;
 }
 
 /*

@@ -324,3 +324,58 @@ def test_workload_shapes_and_lengths():
     bits = wl._to_bf16_bits(x)
     back = (bits.astype(np.uint32) << 16).view(np.float32)
     assert (np.abs(back - x) <= np.abs(x) * 2.0 ** -8).all()
+
+
+def _random_keep(rng, shape, density):
+    keep = (rng.random(shape) < density).astype(np.uint8)
+    return keep * rng.integers(1, 256, shape).astype(np.uint8)  # any nonzero byte keeps
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("d1,d2", [(0.5, 0.5), (0.9, 0.2), (1.0, 1.0), (0.3, 0.0)])
+def test_repack_equals_pack_of_the_composed_mask(seed, d1, d2):
+    """Two pruning stages: pack with k1, then re-pack the packed rows with k2.
+    The result is pack with the composed mask (kept by both), gather indices
+    included: a second formulation of the same compaction."""
+    rng = np.random.default_rng(seed)
+    B, N = 6, 41
+    k1 = _random_keep(rng, (B, N), d1)
+    src = rng.integers(0, 2 ** 16, size=(B * N, 12), dtype=np.uint16)
+    p1, cu1, g1 = oracle.pack(k1, src)
+    k2 = _random_keep(rng, (p1.shape[0],), d2)
+    p2, cu2, g2 = oracle.repack(k2, cu1, g1, p1)
+    k12 = np.zeros(B * N, dtype=np.uint8)
+    k12[g1[k2 != 0]] = 1
+    ref_p, ref_cu, ref_g = oracle.pack(k12.reshape(B, N), src)
+    assert (cu2 == ref_cu).all()
+    assert (g2 == ref_g).all()
+    assert (p2 == ref_p).all()
+
+
+def test_repack_keep_all_is_identity_and_keep_none_is_empty():
+    w = wl.deitb_ragged(64)
+    rows = wl.rows(w)
+    p1, cu1, g1 = oracle.pack(w.keep, rows)
+    p2, cu2, g2 = oracle.repack(np.full(p1.shape[0], 7, np.uint8), cu1, g1, p1)
+    assert (cu2 == cu1).all() and (g2 == g1).all() and (p2 == p1).all()
+    p3, cu3, g3 = oracle.repack(np.zeros(p1.shape[0], np.uint8), cu1, g1, p1)
+    assert p3.shape[0] == 0 and (cu3 == 0).all() and g3.shape[0] == 0
+
+
+def test_repack_brute_force_per_image():
+    """Image by image with numpy: the surviving rows of image b, in order."""
+    rng = np.random.default_rng(5)
+    cu_in = np.array([0, 3, 3, 10, 11, 20], dtype=np.int32)
+    T = int(cu_in[-1])
+    gather_in = np.sort(rng.choice(1000, size=T, replace=False)).astype(np.int32)
+    rows = rng.integers(0, 2 ** 31, size=(T, 4), dtype=np.int32)
+    keep = _random_keep(rng, (T,), 0.6)
+    out, cu_out, g_out = oracle.repack(keep, cu_in, gather_in, rows)
+    t = 0
+    for b in range(cu_in.shape[0] - 1):
+        sel = [r for r in range(cu_in[b], cu_in[b + 1]) if keep[r] != 0]
+        assert cu_out[b] == t and cu_out[b + 1] == t + len(sel)
+        for i, r in enumerate(sel):
+            assert g_out[t + i] == gather_in[r]
+            assert (out[t + i] == rows[r]).all()
+        t += len(sel)

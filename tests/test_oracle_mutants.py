@@ -34,6 +34,10 @@ MUTANTS = {
     "unpack_off_by_one": ("for (int64_t t = 0; t < T; ++t)", "for (int64_t t = 1; t < T; ++t)"),
     "padded_ignores_mask": ("const uint8_t* ok = keep + (int64_t)b * N;", "const uint8_t* ok = NULL;"),
     "bf16_decode_shift": ("uint32_t w = ((uint32_t)bits) << 16;", "uint32_t w = ((uint32_t)bits) << 15;"),
+    "repack_gather_not_composed": ("gather_out[t_out] = gather_in[t];", "gather_out[t_out] = (int32_t)t;"),
+    "repack_skips_image_start": ("for (int64_t t = cu_in[b]; t < cu_in[b + 1]; ++t) {",
+                                 "for (int64_t t = cu_in[b] + 1; t < cu_in[b + 1]; ++t) {"),
+    "repack_keep_is_one": ("            if (keep[t] != 0) {", "            if (keep[t] == 1) {"),
 }
 
 PINS = [
@@ -49,6 +53,9 @@ PINS = [
     lambda: pins.test_attn_brute_force_tiny([4, 1, 5], 2, 8),
     lambda: pins.test_attn_matches_torch_sdpa_fp64("bf16"),
     pins.test_padded_kept_rows_equal_ragged_and_dropped_rows_match_masked_sdpa,
+    lambda: pins.test_repack_equals_pack_of_the_composed_mask(0, 0.5, 0.5),
+    pins.test_repack_keep_all_is_identity_and_keep_none_is_empty,
+    pins.test_repack_brute_force_per_image,
 ]
 
 
