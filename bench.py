@@ -212,6 +212,59 @@ def _cpu_model():
     return "unknown"
 
 
+def measure_repack(steps):
+    """A second pruning stage on a packed batch (SURVEY-style progressive
+    pruning): DeiT-S at B = 256 packed at 50% prune (99 kept per image), then
+    re-packed to 40 per image (the headline's kept count) with rag_repack.
+    Device time per launch from a captured run of back-to-back launches (no host
+    work between them), and the launch's algorithmic bytes."""
+    import torch
+    from ragged_attention_token_amd import binding
+    from ragged_attention_token_amd import workloads as wl
+
+    w = wl.deits(256, 500)
+    bf = Bufs(w)
+    bf.pack()
+    rows = w.B * w.N
+    k2 = torch.zeros(rows, dtype=torch.uint8, device="cuda")
+    k2_np = wl.second_stage_keep(w, 40, seed=1)
+    k2[:w.T] = torch.from_numpy(k2_np).cuda()
+    T2 = int(np.count_nonzero(k2_np))
+    dst = torch.empty_like(bf.packed)
+    cu2 = torch.zeros(w.B + 1, dtype=torch.int32, device="cuda")
+    g2 = torch.zeros(rows, dtype=torch.int32, device="cuda")
+
+    def call():
+        binding.rag_repack(k2, bf.cu, bf.gather, bf.max_seqlen, bf.packed, dst, cu2, g2)
+
+    call()
+    torch.cuda.synchronize()
+    eager = dst[:T2].clone()
+    per_graph = 50
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(per_graph):
+            call()
+    graph.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:T2].view(torch.uint8), eager.view(torch.uint8)), "replay differs"
+    reps = max(4, min(40, steps // per_graph))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * per_graph)
+    row_bytes = 3 * w.C * w.elem_bytes
+    alg = w.T + 4 * (w.B + 1) + T2 * (2 * row_bytes + 4 + 4) + 4 * (w.B + 1)
+    return {"workload": "deits_b256_n197_h6: packed at 50%% prune (T=%d), re-packed to 40 per "
+                        "image (T'=%d)" % (w.T, T2),
+            "us": us, "alg_bytes": alg, "achieved_GBs": alg / us * 1e-3,
+            "hbm_frac": alg / us * 1e-3 / HBM_PEAK_GBS,
+            "timing": "%d launches captured in one graph, %d replays, HIP events" % (per_graph, reps)}
+
+
 def sweep(steps):
     """Prune-rate sweep on the DeiT-S shape: per-launch device time of each kernel
     and of a whole pass (three launches, and one graph launch)."""
@@ -335,6 +388,7 @@ def main():
         "fused_tokens_per_s": w.T / st["fused_pass"] * 1e6,
         "dispatch_floor_us": floor,
     }
+    res["repack"] = measure_repack(args.steps)
     if not args.no_sweep:
         res["sweep"] = sweep(args.steps)
     if not args.no_cpu:

@@ -112,6 +112,44 @@ RAG_API rag_status rag_pack(const uint8_t* keep, int32_t B, int32_t N, const voi
                             int32_t* gather_idx, int32_t* max_seqlen_dev, void* stream);
 
 /*
+ * rag_repack -- a later pruning stage on already packed tokens: keep a subset
+ * of each image's packed rows, with no round trip through the [B, N] layout.
+ * The pages' pruning methods ([abstract-v1]: Threshold-L2, DynamicViT, EViT,
+ * ATS) drop tokens at more than one depth; this is the pack step
+ * ([blog-method]) applied to a packed buffer.
+ *
+ *   keep_packed  uint8, one byte per input packed row (nonzero keeps it), at
+ *                least total_rows bytes, 16-byte aligned base.
+ *   cu_in        int32[B+1], device: image b is input rows cu_in[b] ..
+ *                cu_in[b+1]-1; cu_in[0] = 0, non-decreasing (values are
+ *                clamped to [0, total_rows]).
+ *   gather_in    int32, device: the original batch row of each input row
+ *                (e.g. rag_pack's gather_idx).
+ *   max_rows_in  host bound of rows per input image (e.g. the max_seqlen of
+ *                the previous stage), 1 .. RAG_MAX_N.  Images must not be
+ *                longer (a longer image is read as its first max_rows_in rows
+ *                and the outputs are then unspecified, though every access
+ *                stays inside the buffers).
+ *   total_rows   rows of the input buffers (capacity).
+ *   src          input packed rows (row t at src + t*src_row_stride bytes).
+ *   dst          output rows, capacity total_rows; must not overlap src.
+ *   cu_out       out, int32[B+1]: cu_out[0] = 0, cu_out[b+1] = cu_out[b] + the
+ *                number of kept rows of image b.
+ *   gather_out   out, int32, capacity total_rows: gather_out[cu_out[b] + i] =
+ *                gather_in[t_i], t_0 < t_1 < ... the kept input rows of image
+ *                b -- the original batch row, so rag_unpack with cu_out /
+ *                gather_out writes straight back to the [B, N] layout.
+ *
+ * Bit-exact; same alignment and stride rules as rag_pack, with max_rows_in in
+ * the role of N.
+ */
+RAG_API rag_status rag_repack(const uint8_t* keep_packed, const int32_t* cu_in,
+                              const int32_t* gather_in, int32_t B, int32_t max_rows_in,
+                              int32_t total_rows, const void* src, int64_t src_row_stride,
+                              int32_t row_bytes, void* dst, int64_t dst_row_stride,
+                              int32_t* cu_out, int32_t* gather_out, void* stream);
+
+/*
  * rag_attn -- bidirectional multi-head attention on packed ragged sequences
  * ([abstract]; [blog-method], ragged attention kernel).
  *

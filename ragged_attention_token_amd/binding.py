@@ -28,7 +28,7 @@ RAG_FLOOR_N = 27
 RAG_STAGES_N = 7
 
 #: Every symbol include/rag.h declares.
-EXPORTS = ("rag_pack", "rag_attn", "rag_unpack", "rag_attn_padded", "rag_attn_gathered",
+EXPORTS = ("rag_pack", "rag_repack", "rag_attn", "rag_unpack", "rag_attn_padded", "rag_attn_gathered",
            "rag_pipeline_create", "rag_pipeline_launch", "rag_pipeline_launch_eager",
            "rag_pipeline_launch_fused", "rag_pipeline_destroy",
            "rag_measure_dispatch", "rag_measure_stages", "rag_last_error", "rag_status_string",
@@ -76,6 +76,7 @@ def load(path: str = LIB_PATH):
     lib.rag_attn.argtypes = [vp, vp, vp, i64, i64, i64, i32, vp, i32, i32, i32, i32, i32, f32, vp,
                              i64, i32, vp]
     lib.rag_unpack.argtypes = [vp, i64, i32, vp, vp, i32, i32, vp, i64, u32, vp]
+    lib.rag_repack.argtypes = [vp, vp, vp, i32, i32, i32, vp, i64, i32, vp, i64, vp, vp, vp]
     lib.rag_attn_padded.argtypes = [vp, vp, vp, i64, i64, i64, i32, vp, i32, i32, i32, i32, f32,
                                     vp, i64, i32, vp]
     lib.rag_attn_gathered.argtypes = [vp, i32, i32, i32, vp, vp, vp, i64, i64, i64, i32, i32, i32, f32,
@@ -92,7 +93,7 @@ def load(path: str = LIB_PATH):
     lib.rag_status_string.argtypes = [i32]
     lib.rag_status_string.restype = ctypes.c_char_p
     lib.rag_version.restype = i32
-    for name in ("rag_pack", "rag_attn", "rag_unpack", "rag_attn_padded", "rag_attn_gathered",
+    for name in ("rag_pack", "rag_repack", "rag_attn", "rag_unpack", "rag_attn_padded", "rag_attn_gathered",
                  "rag_pipeline_create", "rag_pipeline_launch", "rag_pipeline_launch_eager",
                  "rag_pipeline_launch_fused", "rag_measure_dispatch", "rag_measure_stages"):
         getattr(lib, name).restype = i32
@@ -174,6 +175,34 @@ def rag_pack(keep: torch.Tensor, src: torch.Tensor, packed: torch.Tensor, cu_seq
     _check(load().rag_pack(keep.data_ptr(), B, N, sp, ss * src.element_size(), rb, pp,
                            ps * packed.element_size(), cu_seqlens.data_ptr(),
                            gather_idx.data_ptr(), mp, _stream(stream)))
+
+
+def rag_repack(keep_packed: torch.Tensor, cu_in: torch.Tensor, gather_in: torch.Tensor,
+               max_rows_in: int, src: torch.Tensor, dst: torch.Tensor, cu_out: torch.Tensor,
+               gather_out: torch.Tensor, row_bytes: Optional[int] = None, stream=None) -> None:
+    """A later pruning stage on packed rows: keep_packed uint8 [>= rows] (one
+    byte per input row); cu_in int32 [B+1]; gather_in int32 [>= rows]; src /
+    dst rows [rows, ...]; cu_out int32 [B+1]; gather_out int32 [>= rows]."""
+    _gpu(keep_packed, "keep_packed")
+    if keep_packed.dtype != torch.uint8 or not keep_packed.is_contiguous():
+        raise ValueError("keep_packed must be a contiguous uint8 tensor")
+    for t, name in ((cu_in, "cu_in"), (gather_in, "gather_in"), (cu_out, "cu_out"),
+                    (gather_out, "gather_out")):
+        _gpu(t, name)
+        if t.dtype != torch.int32:
+            raise TypeError("%s must be int32" % name)
+    B = cu_in.numel() - 1
+    sp, ss = _rows(src, "src")
+    dp, ds = _rows(dst, "dst")
+    rows = src.shape[0]
+    if keep_packed.numel() < rows or gather_in.numel() < rows or dst.shape[0] < rows \
+            or gather_out.numel() < rows or cu_out.numel() < B + 1:
+        raise ValueError("buffers smaller than src's rows")
+    rb = _row_bytes(src) if row_bytes is None else int(row_bytes)
+    _check(load().rag_repack(keep_packed.data_ptr(), cu_in.data_ptr(), gather_in.data_ptr(), B,
+                             int(max_rows_in), rows, sp, ss * src.element_size(), rb, dp,
+                             ds * dst.element_size(), cu_out.data_ptr(), gather_out.data_ptr(),
+                             _stream(stream)))
 
 
 def rag_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,

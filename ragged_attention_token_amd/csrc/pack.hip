@@ -59,10 +59,14 @@ struct PackParams {
     int32_t* cu;
     int32_t* gather;
     int32_t* max_len;
+    const int32_t* cu_in;      // re-pack: the input's images (packed rows)
+    const int32_t* gather_in;  // re-pack: the input rows' original batch rows
     int64_t src_stride;
     int64_t packed_stride;
+    // N: rows per image (pack) or the host bound of rows per input image (re-pack)
     int32_t B, N, row_vecs, slice_vecs;  // slice s: vectors [s*slice_vecs, ...) of a row
-    uint32_t n_magic;                     // floor(2^32 / N) + 1
+    int32_t total_rows;                  // re-pack: rows of the input (cu_in is clamped to it)
+    uint32_t n_magic;                    // floor(2^32 / N) + 1
 };
 
 struct UnpackParams {
@@ -233,30 +237,48 @@ __device__ void max_length_pass(const PackParams& p, int* cnt, int window, int* 
     }
 }
 
+// RAGGED_IN = false: pack.  Image b's source rows are b*N .. b*N+N-1 and its
+// keep bytes keep[b*N ..]; gather entries are the source rows.
+// RAGGED_IN = true: re-pack (a later pruning stage).  Image b's source rows
+// are the packed rows cu_in[b] .. cu_in[b+1]-1 (at most N of them) with one
+// keep byte per packed row; gather entries are gather_in of the kept rows.
+// Either way the offset of image b counts the keep bytes before its first
+// row, and the rest is the same compaction.
+template <bool RAGGED_IN>
 __global__ __launch_bounds__(kThreads) void pack_kernel(PackParams p)
 {
     extern __shared__ int s_pos[];  // max(N, 256) ints
     __shared__ int s_red[kWaves];
     const int tid = threadIdx.x;
     const int b = blockIdx.x, sl = blockIdx.y;
-    if (b == p.B) {
+    if (!RAGGED_IN && b == p.B) {
         if (sl == 0) max_length_pass(p, s_pos, max(p.N, kThreads), s_red);
         return;
     }
-    const int64_t img_row0 = (int64_t)b * p.N;
+    int64_t img_row0;
+    int n_in;  // rows of the image in the input
+    if constexpr (RAGGED_IN) {
+        const int s = min(max(p.cu_in[b], 0), p.total_rows);
+        const int e = min(max(p.cu_in[b + 1], s), p.total_rows);
+        img_row0 = s;
+        n_in = min(e - s, p.N);
+    } else {
+        img_row0 = (int64_t)b * p.N;
+        n_in = p.N;
+    }
     // The image's keep bytes are requested first and the prefix words after
     // them, so the ranking waits for the former only.
     int L;
     Prefix pf;
     if (p.N <= kThreads) {
-        // (a buffer load: positions past N read as zero, no branch)
+        // (a buffer load: positions past the image read as zero, no branch)
         const uint32_t kbyte = __builtin_amdgcn_raw_buffer_load_b8(
-            make_rsrc(p.keep + img_row0, (uint32_t)p.N), (uint32_t)tid, 0, 0);
+            make_rsrc(p.keep + img_row0, (uint32_t)n_in), (uint32_t)tid, 0, 0);
         pf = prefix_begin(p.keep, img_row0);
         L = dev::rank_kept_preloaded(kbyte != 0u, s_pos, s_red, kWaves);
     } else {
         pf = prefix_begin(p.keep, img_row0);
-        L = dev::rank_kept(p.keep + img_row0, p.N, s_pos, s_red);
+        L = dev::rank_kept(p.keep + img_row0, n_in, s_pos, s_red);
     }
     if (L == 0 && sl > 0) return;  // uniform; slice 0 still writes cu
 
@@ -269,7 +291,7 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(PackParams p)
     const int w = min(p.slice_vecs, p.row_vecs - c0);
     const int dr = kThreads / w, dc = kThreads - dr * w;
     const uint32_t sstride = (uint32_t)p.src_stride, pstride = (uint32_t)p.packed_stride;
-    const auto rs = make_rsrc(p.src + img_row0 * p.src_stride, (uint32_t)(p.N * p.src_stride));
+    const auto rs = make_rsrc(p.src + img_row0 * p.src_stride, (uint32_t)(n_in * p.src_stride));
     auto advance = [&](int& r, int& col) {
         r += dr;
         col += dc;
@@ -302,7 +324,10 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(PackParams p)
             p.cu[b + 1] = offset + L;
             if (b == 0) p.cu[0] = 0;
         }
-        for (int t = tid; t < L; t += kThreads) p.gather[offset + t] = (int32_t)(img_row0 + s_pos[t]);
+        for (int t = tid; t < L; t += kThreads) {
+            if constexpr (RAGGED_IN) p.gather[offset + t] = p.gather_in[img_row0 + s_pos[t]];
+            else p.gather[offset + t] = (int32_t)(img_row0 + s_pos[t]);
+        }
     }
     if (L == 0) return;
     const auto rd = make_rsrc(p.packed + (int64_t)offset * p.packed_stride, (uint32_t)L * pstride);
@@ -413,6 +438,9 @@ int launch_pack(const uint8_t* keep, int32_t B, int32_t N, const void* src,
     p.cu = cu_seqlens;
     p.gather = gather_idx;
     p.max_len = max_seqlen_dev;
+    p.cu_in = nullptr;
+    p.gather_in = nullptr;
+    p.total_rows = 0;
     p.src_stride = src_row_stride;
     p.packed_stride = packed_row_stride;
     p.B = B;
@@ -427,7 +455,38 @@ int launch_pack(const uint8_t* keep, int32_t B, int32_t N, const void* src,
     const int used = (p.row_vecs + p.slice_vecs - 1) / p.slice_vecs;  // no empty slice
     const dim3 grid(B + (max_seqlen_dev ? 1 : 0), used);
     const size_t lds = sizeof(int) * (size_t)max(N, kThreads);
-    hipLaunchKernelGGL(pack_kernel, grid, dim3(kThreads), lds, static_cast<hipStream_t>(stream), p);
+    hipLaunchKernelGGL(pack_kernel<false>, grid, dim3(kThreads), lds, static_cast<hipStream_t>(stream), p);
+    return (int)hipGetLastError();
+}
+
+int launch_repack(const uint8_t* keep_packed, const int32_t* cu_in, const int32_t* gather_in,
+                  int32_t B, int32_t max_rows_in, int32_t total_rows, const void* src,
+                  int64_t src_row_stride, int32_t row_bytes, void* dst, int64_t dst_row_stride,
+                  int32_t* cu_out, int32_t* gather_out, void* stream)
+{
+    PackParams p;
+    p.keep = keep_packed;
+    p.src = static_cast<const uint8_t*>(src);
+    p.packed = static_cast<uint8_t*>(dst);
+    p.cu = cu_out;
+    p.gather = gather_out;
+    p.max_len = nullptr;
+    p.cu_in = cu_in;
+    p.gather_in = gather_in;
+    p.src_stride = src_row_stride;
+    p.packed_stride = dst_row_stride;
+    p.B = B;
+    p.N = max_rows_in;
+    p.total_rows = total_rows;
+    p.row_vecs = row_bytes / 16;
+    p.n_magic = 0;  // no max-length pass
+    const int max_slices = max(1, p.row_vecs / 16);
+    const int slices = min(max_slices, max(1, (kPackTargetGroups + B - 1) / B));
+    p.slice_vecs = (p.row_vecs + slices - 1) / slices;
+    const int used = (p.row_vecs + p.slice_vecs - 1) / p.slice_vecs;
+    const dim3 grid(B, used);
+    const size_t lds = sizeof(int) * (size_t)max(max_rows_in, kThreads);
+    hipLaunchKernelGGL(pack_kernel<true>, grid, dim3(kThreads), lds, static_cast<hipStream_t>(stream), p);
     return (int)hipGetLastError();
 }
 

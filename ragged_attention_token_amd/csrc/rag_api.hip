@@ -78,6 +78,23 @@ extern "C" RAG_API rag_status rag_unpack(const void* packed, int64_t packed_row_
                       "rag_unpack launch");
 }
 
+extern "C" RAG_API rag_status rag_repack(const uint8_t* keep_packed, const int32_t* cu_in,
+                                         const int32_t* gather_in, int32_t B, int32_t max_rows_in,
+                                         int32_t total_rows, const void* src,
+                                         int64_t src_row_stride, int32_t row_bytes, void* dst,
+                                         int64_t dst_row_stride, int32_t* cu_out,
+                                         int32_t* gather_out, void* stream)
+{
+    rag_status s = rag::validate_repack(keep_packed, cu_in, gather_in, B, max_rows_in, total_rows,
+                                        src, src_row_stride, row_bytes, dst, dst_row_stride,
+                                        cu_out, gather_out);
+    if (s != RAG_OK) return s;
+    return hip_status(rag::launch_repack(keep_packed, cu_in, gather_in, B, max_rows_in, total_rows,
+                                         src, src_row_stride, row_bytes, dst, dst_row_stride,
+                                         cu_out, gather_out, stream),
+                      "rag_repack launch");
+}
+
 extern "C" RAG_API rag_status rag_attn_padded(const void* q, const void* k, const void* v,
                                               int64_t q_row_stride, int64_t k_row_stride,
                                               int64_t v_row_stride, rag_dtype in_dtype,

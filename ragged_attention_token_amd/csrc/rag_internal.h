@@ -19,6 +19,11 @@ rag_status validate_pack(const uint8_t* keep, int32_t B, int32_t N, const void* 
                          int64_t src_row_stride, int32_t row_bytes, const void* packed,
                          int64_t packed_row_stride, const int32_t* cu_seqlens,
                          const int32_t* gather_idx);
+rag_status validate_repack(const uint8_t* keep_packed, const int32_t* cu_in,
+                           const int32_t* gather_in, int32_t B, int32_t max_rows_in,
+                           int32_t total_rows, const void* src, int64_t src_row_stride,
+                           int32_t row_bytes, const void* dst, int64_t dst_row_stride,
+                           const int32_t* cu_out, const int32_t* gather_out);
 rag_status validate_unpack(const void* packed, int64_t packed_row_stride, int32_t row_bytes,
                            const int32_t* cu_seqlens, const int32_t* gather_idx, int32_t B,
                            int32_t N, const void* dst, int64_t dst_row_stride, uint32_t flags);
@@ -52,6 +57,10 @@ int launch_pack(const uint8_t* keep, int32_t B, int32_t N, const void* src,
                 int64_t src_row_stride, int32_t row_bytes, void* packed,
                 int64_t packed_row_stride, int32_t* cu_seqlens, int32_t* gather_idx,
                 int32_t* max_seqlen_dev, void* stream);
+int launch_repack(const uint8_t* keep_packed, const int32_t* cu_in, const int32_t* gather_in,
+                  int32_t B, int32_t max_rows_in, int32_t total_rows, const void* src,
+                  int64_t src_row_stride, int32_t row_bytes, void* dst, int64_t dst_row_stride,
+                  int32_t* cu_out, int32_t* gather_out, void* stream);
 int launch_unpack(const void* packed, int64_t packed_row_stride, int32_t row_bytes,
                   const int32_t* cu_seqlens, const int32_t* gather_idx, int32_t B, int32_t N,
                   void* dst, int64_t dst_row_stride, uint32_t flags, void* stream);

@@ -90,6 +90,29 @@ rag_status validate_pack(const uint8_t* keep, int32_t B, int32_t N, const void* 
     return check_image_span("packed", N, packed_row_stride);
 }
 
+rag_status validate_repack(const uint8_t* keep_packed, const int32_t* cu_in,
+                           const int32_t* gather_in, int32_t B, int32_t max_rows_in,
+                           int32_t total_rows, const void* src, int64_t src_row_stride,
+                           int32_t row_bytes, const void* dst, int64_t dst_row_stride,
+                           const int32_t* cu_out, const int32_t* gather_out)
+{
+    rag_status s = check_batch(B, max_rows_in);
+    if (s != RAG_OK) return s;
+    if (total_rows < 0) return set_error(RAG_ERR_INVALID_ARG, "total_rows=%d must be >= 0", total_rows);
+    if (!keep_packed) return set_error(RAG_ERR_INVALID_ARG, "keep_packed is NULL");
+    if (!aligned16(keep_packed))
+        return set_error(RAG_ERR_ALIGNMENT, "keep_packed must be 16-byte aligned");
+    if (!cu_in || !gather_in || !cu_out || !gather_out)
+        return set_error(RAG_ERR_INVALID_ARG, "cu_in, gather_in, cu_out and gather_out must not be NULL");
+    if (row_bytes < 16) return set_error(RAG_ERR_INVALID_ARG, "row_bytes=%d must be >= 16", row_bytes);
+    if (row_bytes & 15) return set_error(RAG_ERR_ALIGNMENT, "row_bytes=%d must be a multiple of 16", row_bytes);
+    if ((s = check_rows("src", src, src_row_stride, row_bytes)) != RAG_OK) return s;
+    if ((s = check_rows("dst", dst, dst_row_stride, row_bytes)) != RAG_OK) return s;
+    if (src == dst) return set_error(RAG_ERR_INVALID_ARG, "src and dst must not overlap");
+    if ((s = check_image_span("src", max_rows_in, src_row_stride)) != RAG_OK) return s;
+    return check_image_span("dst", max_rows_in, dst_row_stride);
+}
+
 rag_status validate_unpack(const void* packed, int64_t packed_row_stride, int32_t row_bytes,
                            const int32_t* cu_seqlens, const int32_t* gather_idx, int32_t B,
                            int32_t N, const void* dst, int64_t dst_row_stride, uint32_t flags)

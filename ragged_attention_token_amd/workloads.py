@@ -198,3 +198,21 @@ def rows(w: Workload) -> np.ndarray:
 def split_qkv(rows_2d: np.ndarray, C: int):
     """Views of Q, K, V ([rows, C] each, row stride 3C) inside fused rows."""
     return rows_2d[:, 0:C], rows_2d[:, C:2 * C], rows_2d[:, 2 * C:3 * C]
+
+
+def second_stage_keep(w: Workload, kept: int, seed: int) -> np.ndarray:
+    """Keep bytes for a later pruning stage over w's packed rows (image by image
+    in order, each image's rows in ascending original position): every image
+    keeps its first packed row (CLS) and min(kept, L_b) - 1 of its other rows,
+    drawn uniformly without replacement (numpy PCG64, ``seed``).  uint8 [T]."""
+    rng = np.random.default_rng(seed)
+    k2 = np.zeros(w.T, dtype=np.uint8)
+    start = 0
+    for L in w.lengths.tolist():
+        if L > 0:
+            k2[start] = 1
+            m = min(kept, L) - 1
+            if m > 0:
+                k2[start + 1 + rng.choice(L - 1, size=m, replace=False)] = 1
+        start += L
+    return k2

@@ -71,6 +71,36 @@ def test_pack_rejects(lib, kwargs, status, needle):
     assert needle in binding.last_error()
 
 
+def repack(lib, keep=A, cu_in=A, g_in=A, B=2, maxr=40, total=80, src=A, ss=2304, rb=2304,
+           dst=A + 0x1000000, ds=2304, cu_out=A, g_out=A):
+    return lib.rag_repack(keep, cu_in, g_in, B, maxr, total, src, ss, rb, dst, ds, cu_out, g_out,
+                          None)
+
+
+@pytest.mark.parametrize("kwargs,status,needle", [
+    (dict(B=0), INVALID, "B=0"),
+    (dict(maxr=0), INVALID, "N=0"),
+    (dict(maxr=9000), UNSUPPORTED, "limits"),
+    (dict(total=-1), INVALID, "total_rows"),
+    (dict(keep=None), INVALID, "keep_packed"),
+    (dict(keep=A + 3), ALIGN, "keep_packed"),
+    (dict(cu_in=None), INVALID, "cu_in"),
+    (dict(g_in=None), INVALID, "gather_in"),
+    (dict(cu_out=None), INVALID, "cu_out"),
+    (dict(g_out=None), INVALID, "gather_out"),
+    (dict(rb=8), INVALID, "row_bytes"),
+    (dict(rb=2308), ALIGN, "row_bytes"),
+    (dict(src=None), INVALID, "src"),
+    (dict(ds=2300), INVALID, "dst row stride"),
+    (dict(dst=A + 8), ALIGN, "dst"),
+    (dict(dst=A), INVALID, "overlap"),
+    (dict(maxr=8192, ss=1 << 20), UNSUPPORTED, "2^31"),
+])
+def test_repack_rejects(lib, kwargs, status, needle):
+    assert repack(lib, **kwargs) == status
+    assert needle in binding.last_error()
+
+
 def attn(lib, q=A, k=A, v=A, qs=1152, ks=1152, vs=1152, dt=BF16, cu=A, B=4, maxlen=197, tr=788,
          H=6, hd=64, scale=0.125, o=A, os_=384, odt=F32):
     return lib.rag_attn(q, k, v, qs, ks, vs, dt, cu, B, maxlen, tr, H, hd, scale, o, os_, odt, None)

@@ -449,3 +449,87 @@ def test_attention_any_scale(scale):
         o16 = gpu_attn(g["packed"], g["cu"], w, torch.bfloat16)
         worst = _check_attn(w, ref, o32, o16, range(w.B))
         print("scale", scale, w.dtype, "max abs err", worst, flush=True)
+
+
+def _second_stage_keep(w, seed, density):
+    """A keep byte per packed row (a later pruning stage), CLS rows kept: the
+    input generator's draw at a kept count of about density * N."""
+    k = wl.second_stage_keep(w, max(1, int(round(density * w.N))), seed)
+    rng = np.random.default_rng(seed + 100)  # any nonzero byte keeps
+    return (k * rng.integers(1, 256, k.shape)).astype(np.uint8)
+
+
+def _gpu_repack(g, k2_np, w, max_rows_in):
+    rows = w.B * w.N
+    k2 = torch.zeros(rows, dtype=torch.uint8, device="cuda")
+    k2[:k2_np.shape[0]] = torch.from_numpy(k2_np).cuda()
+    dst = sentinel_like((rows, 3 * w.C), g["packed"].dtype)
+    cu_out = sentinel_like((w.B + 1,), torch.int32)
+    g_out = sentinel_like((rows,), torch.int32)
+    binding.rag_repack(k2, g["cu"], g["gather"], max_rows_in, g["packed"], dst, cu_out, g_out)
+    torch.cuda.synchronize()
+    return dst, cu_out, g_out
+
+
+@pytest.mark.parametrize("name,density", [("deits_b4_p800", 0.5), ("deitb_ragged_b64", 0.3),
+                                          ("empty_and_full", 0.7), ("f32_odd", 0.5),
+                                          ("n577_two", 0.4), ("tile_edges", 1.0)])
+def test_repack_bit_exact(name, density):
+    """A second pruning stage on the packed buffer: cu, composed gather index and
+    rows bit for bit the oracle's; rows and entries past T' untouched."""
+    w = FULL[name]()
+    print("repack case", name, flush=True)
+    packed_ref, cu_ref, gather_ref = _oracle_pack(w)
+    g = gpu_pack(w)
+    k2 = _second_stage_keep(w, 19, density)
+    want_rows, want_cu, want_g = oracle.repack(k2, cu_ref, gather_ref, packed_ref)
+    dst, cu_out, g_out = _gpu_repack(g, k2, w, int(w.lengths.max()) if w.T else 1)
+    T2 = int(want_cu[-1])
+    assert (cu_out.cpu().numpy() == want_cu).all()
+    assert (g_out.cpu().numpy()[:T2] == want_g).all()
+    assert (g_out.cpu().numpy()[T2:].view(np.uint32) == np.uint32(0xA5A5A5A5)).all()
+    d = as_numpy_rows(dst)
+    assert (d[:T2].view(np.uint8) == want_rows.view(np.uint8)).all()
+    assert (d[T2:].view(np.uint8) == SENTINEL_BYTE).all()
+
+
+def test_repack_equals_pack_of_composed_mask_full_size():
+    """deits at B = 256 without pruning, then a 60% second stage: the same bits
+    as packing the batch with the composed mask in one go."""
+    w = wl.deits(256, 0)
+    g = gpu_pack(w)
+    k2 = _second_stage_keep(w, 20, 0.6)
+    dst, cu_out, g_out = _gpu_repack(g, k2, w, w.N)
+    _, cu_ref, gather_ref = _oracle_pack(w)
+    k12 = np.zeros(w.B * w.N, dtype=np.uint8)
+    k12[gather_ref[k2 != 0]] = 1
+    w2 = wl.custom(B=w.B, N=w.N, H=w.H, lengths=np.count_nonzero(k12.reshape(w.B, w.N), axis=1),
+                   seed=0)
+    w2.keep = k12.reshape(w.B, w.N)
+    w2.qkv = w.qkv
+    g2 = gpu_pack(w2)
+    T2 = int(np.count_nonzero(k12))
+    assert torch.equal(cu_out, g2["cu"])
+    assert torch.equal(g_out[:T2], g2["gather"][:T2])
+    assert torch.equal(dst[:T2].view(torch.uint8), g2["packed"][:T2].view(torch.uint8))
+
+
+def test_repack_then_attention_and_unpack():
+    """The second stage feeds attention and unpack directly (gather_out holds
+    batch rows): the result equals the oracle on the composed mask."""
+    w = wl.deits(4, 500)
+    g = gpu_pack(w)
+    k2 = _second_stage_keep(w, 21, 0.5)
+    dst, cu_out, g_out = _gpu_repack(g, k2, w, int(w.lengths.max()))
+    o = gpu_attn(dst, cu_out, w, torch.float32, max_seqlen=int(w.lengths.max()))
+    packed_ref, cu_ref, gather_ref = _oracle_pack(w)
+    rows2, cu2, g2 = oracle.repack(k2, cu_ref, gather_ref, packed_ref)
+    q, k, v = wl.split_qkv(rows2, w.C)
+    want = oracle.attn(q, k, v, cu2, w.H, w.d, w.scale)
+    T2 = int(cu2[-1])
+    assert np.abs(o.cpu().numpy()[:T2].astype(np.float64) - want).max() <= ATOL
+    out = sentinel_like((w.B * w.N, w.C), torch.float32)
+    binding.rag_unpack(o, cu_out, g_out, out, N=w.N)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert (got[g2].view(np.uint8) == o.cpu().numpy()[:T2].view(np.uint8)).all()
