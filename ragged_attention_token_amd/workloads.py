@@ -216,3 +216,30 @@ def second_stage_keep(w: Workload, kept: int, seed: int) -> np.ndarray:
                 k2[start + 1 + rng.choice(L - 1, size=m, replace=False)] = 1
         start += L
     return k2
+
+
+def vit_block_params(C: int, mlp_ratio: int, seed: int) -> Dict[str, np.ndarray]:
+    """Random weights for one pre-norm ViT encoder block (numpy PCG64, ``seed``;
+    draw order as listed): matrices N(0, 0.02^2) rounded to bf16 (uint16 bit
+    patterns, row-major [in, out]); biases N(0, 0.02^2), LayerNorm gamma
+    1 + N(0, 0.1^2) and beta N(0, 0.1^2) as float32.  The scale follows ViT's
+    initialisation; gamma, beta and the biases are perturbed so that every
+    parameter shows in the output."""
+    rng = np.random.default_rng(seed)
+    hid = C * mlp_ratio
+    out: Dict[str, np.ndarray] = {}
+    for name, shape in (("w_qkv", (C, 3 * C)), ("w_proj", (C, C)), ("w_fc1", (C, hid)),
+                        ("w_fc2", (hid, C))):
+        out[name] = _to_bf16_bits((0.02 * rng.standard_normal(shape)).astype(np.float32))
+    for name, n in (("b_qkv", 3 * C), ("b_proj", C), ("b_fc1", hid), ("b_fc2", C)):
+        out[name] = (0.02 * rng.standard_normal(n)).astype(np.float32)
+    for ln in ("ln1", "ln2"):
+        out[ln + "_gamma"] = (1.0 + 0.1 * rng.standard_normal(C)).astype(np.float32)
+        out[ln + "_beta"] = (0.1 * rng.standard_normal(C)).astype(np.float32)
+    return out
+
+
+def hidden_rows(B: int, N: int, C: int, seed: int) -> np.ndarray:
+    """Token hidden states [B*N, C]: N(0, 1) draws rounded to bf16 (uint16)."""
+    rng = np.random.default_rng(seed)
+    return _to_bf16_bits(rng.standard_normal((B * N, C)).astype(np.float32))

@@ -379,3 +379,143 @@ def test_repack_brute_force_per_image():
             assert g_out[t + i] == gather_in[r]
             assert (out[t + i] == rows[r]).all()
         t += len(sel)
+
+
+# ---- the ViT block reference (end-to-end timing row) -----------------------
+from oracle import vit_block as vb  # noqa: E402
+
+
+def test_layernorm_golden():
+    g = _read_golden("layernorm_worked_example.txt")
+    x = np.array([[float(v) for v in g["x"][0]]])
+    want = np.array([float(v) for v in g["y"][0]])
+    got = vb.layernorm(x, np.ones(4), np.zeros(4), 0.0)[0]
+    assert np.abs(got - want).max() < 1e-15
+
+
+def test_gelu_forms_against_the_normal_cdf_table():
+    """erf form: x * Phi(x), with Phi from a printed normal table (Phi(1) =
+    0.8413447, Phi(2) = 0.9772499, Phi(-1) = 0.1586553); the tanh form stays
+    within 5e-4 of it everywhere and is not the same function (it falls short
+    of Phi by ~24% relative at x = -3.5)."""
+    table = {1.0: 0.8413447, 2.0: 0.9772499, -1.0: 0.1586553}
+    for xv, phi in table.items():
+        assert abs(vb.gelu(np.array([xv]), "erf")[0] - xv * phi) < 2e-7
+    xs = np.linspace(-8, 8, 4001)
+    e, t = vb.gelu(xs, "erf"), vb.gelu(xs, "tanh")
+    assert np.abs(e - t).max() < 5e-4
+    assert vb.gelu(np.array([0.0]), "tanh")[0] == 0.0
+    assert abs(vb.gelu(np.array([-3.5]), "tanh")[0] / vb.gelu(np.array([-3.5]), "erf")[0] - 0.757) < 0.01
+
+
+def test_block_attention_step_matches_the_c_oracle():
+    """The block's numpy attention against oracle.attn (C) on bf16-exact q|k|v
+    rows: two independent implementations of the same definition."""
+    w = wl.deits(3, 800)
+    rows = wl.rows(w)
+    packed, cu, _ = oracle.pack(w.keep, rows)
+    q, k, v = wl.split_qkv(packed, w.C)
+    want = oracle.attn(q, k, v, cu, w.H, w.d, w.scale)
+    got = vb.attention(vb.bf16_bits_to_f64(packed), cu, w.H, w.d, w.scale)
+    assert np.abs(got - want).max() < 1e-12
+
+
+def test_block_with_zero_weights_is_the_identity():
+    C = 128
+    P = wl.vit_block_params(C, 4, 0)
+    for k in P:
+        if k.startswith(("w_", "b_")):
+            P[k] = np.zeros_like(P[k])
+    x = wl.hidden_rows(2, 7, C, 1)
+    y = vb.block(x, P, np.array([0, 5, 14]), 2, 0.125)
+    assert (y == vb.bf16_bits_to_f64(x)).all()
+
+
+def _block_brute_force(x, P, cu, H, d, scale, eps, form):
+    """Pure-Python loops, tiny sizes: the block written element by element."""
+    T, C = len(x), len(x[0])
+
+    def ln(rows, g, b):
+        out = []
+        for r in rows:
+            mu = math.fsum(r) / C
+            var = math.fsum((v - mu) ** 2 for v in r) / C
+            out.append([(r[c] - mu) / math.sqrt(var + eps) * g[c] + b[c] for c in range(C)])
+        return out
+
+    def mm(A, Wt, bias):
+        return [[math.fsum(A[i][k] * Wt[k][j] for k in range(len(Wt))) + bias[j]
+                 for j in range(len(Wt[0]))] for i in range(len(A))]
+
+    def act(v):
+        if form == "erf":
+            return 0.5 * v * (1 + math.erf(v / math.sqrt(2)))
+        return 0.5 * v * (1 + math.tanh(math.sqrt(2 / math.pi) * (v + 0.044715 * v ** 3)))
+
+    xs = [list(r) for r in x]
+    h = ln(xs, P["ln1_gamma"], P["ln1_beta"])
+    qkv = mm(h, P["w_qkv"], P["b_qkv"])
+    a = [[0.0] * C for _ in range(T)]
+    for b in range(len(cu) - 1):
+        for hh in range(H):
+            for i in range(cu[b], cu[b + 1]):
+                s = [scale * math.fsum(qkv[i][hh * d + c] * qkv[j][C + hh * d + c] for c in range(d))
+                     for j in range(cu[b], cu[b + 1])]
+                mx = max(s)
+                e = [math.exp(v - mx) for v in s]
+                z = math.fsum(e)
+                for c in range(d):
+                    a[i][hh * d + c] = math.fsum(
+                        e[jj] / z * qkv[cu[b] + jj][2 * C + hh * d + c] for jj in range(len(e)))
+    pa = mm(a, P["w_proj"], P["b_proj"])
+    x1 = [[xs[i][c] + pa[i][c] for c in range(C)] for i in range(T)]
+    f1 = mm(ln(x1, P["ln2_gamma"], P["ln2_beta"]), P["w_fc1"], P["b_fc1"])
+    m = [[act(v) for v in r] for r in f1]
+    f2 = mm(m, P["w_fc2"], P["b_fc2"])
+    return np.array([[x1[i][c] + f2[i][c] for c in range(C)] for i in range(T)])
+
+
+@pytest.mark.parametrize("form", ["erf", "tanh"])
+def test_block_brute_force_tiny(form):
+    """C = 4 (two heads of width 2), images of 3, 1 and 2 rows; weights that are
+    not symmetric, so a transposed operand or a swapped q/k/v block shows."""
+    rng = np.random.default_rng(7)
+    C, H, d, hid = 4, 2, 2, 8
+    P = {"w_qkv": rng.standard_normal((C, 3 * C)), "w_proj": rng.standard_normal((C, C)),
+         "w_fc1": rng.standard_normal((C, hid)), "w_fc2": rng.standard_normal((hid, C)),
+         "b_qkv": rng.standard_normal(3 * C), "b_proj": rng.standard_normal(C),
+         "b_fc1": rng.standard_normal(hid), "b_fc2": rng.standard_normal(C),
+         "ln1_gamma": 1 + rng.standard_normal(C), "ln1_beta": rng.standard_normal(C),
+         "ln2_gamma": 1 + rng.standard_normal(C), "ln2_beta": rng.standard_normal(C)}
+    x = rng.standard_normal((6, C))
+    cu = [0, 3, 4, 6]
+    bits = lambda a: np.asarray(a, np.float32)  # noqa: E731
+    # the oracle takes bf16 bit patterns for x and matrices: round the draws
+    # to bf16 first so both sides see the same exact values
+    Pb = dict(P)
+    for k in ("w_qkv", "w_proj", "w_fc1", "w_fc2"):
+        Pb[k] = wl._to_bf16_bits(bits(P[k]))
+        P[k] = vb.bf16_bits_to_f64(Pb[k])
+    xb = wl._to_bf16_bits(bits(x))
+    xv = vb.bf16_bits_to_f64(xb)
+    for k in P:
+        if not k.startswith("w_"):
+            Pb[k] = bits(P[k])
+            P[k] = Pb[k].astype(np.float64)
+    got = vb.block(xb, Pb, np.array(cu), H, 0.7, eps=1e-5, gelu_form=form, d=d)
+    want = _block_brute_force(xv.tolist(), {k: (v.tolist() if hasattr(v, "tolist") else v)
+                                            for k, v in P.items()}, cu, H, d, 0.7, 1e-5, form)
+    assert np.abs(got - want).max() < 1e-11
+
+
+def test_block_images_are_independent():
+    """Rows of one image do not move when another image's rows change."""
+    C = 128
+    P = wl.vit_block_params(C, 2, 3)
+    x = wl.hidden_rows(1, 9, C, 4)
+    cu = np.array([0, 4, 9])
+    y1 = vb.block(x, P, cu, 2, 0.125)
+    x2 = x.copy()
+    x2[4:] = wl.hidden_rows(1, 5, C, 5)
+    y2 = vb.block(x2, P, cu, 2, 0.125)
+    assert (y1[:4] == y2[:4]).all() and not (y1[4:] == y2[4:]).all()

@@ -85,3 +85,63 @@ def test_pins_catch_planted_mistake(name):
         assert caught, "no pin caught mutant %s" % name
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
+
+
+# ---- the ViT block reference (Python): the same idea, one-token slips in a
+# copy of oracle/vit_block.py, loaded in place of the module while the block
+# pins run.
+import importlib.util  # noqa: E402
+import sys  # noqa: E402
+
+from oracle import vit_block  # noqa: E402
+
+BLOCK_SRC = vit_block.__file__
+BLOCK_MUTANTS = {
+    "ln_unbiased_variance": ("var = ((x - mean) ** 2).mean(axis=1, keepdims=True)",
+                             "var = ((x - mean) ** 2).sum(axis=1, keepdims=True) / (x.shape[1] - 1)"),
+    "ln_eps_outside_root": ("return (x - mean) / np.sqrt(var + eps) * gamma + beta",
+                            "return (x - mean) / (np.sqrt(var) + eps) * gamma + beta"),
+    "no_first_residual": ("x1 = x + a @ W[\"w_proj\"] + P[\"b_proj\"]", "x1 = a @ W[\"w_proj\"] + P[\"b_proj\"]"),
+    "k_from_v_block": ("k = qkv[s:e, C + h * d:C + (h + 1) * d]",
+                       "k = qkv[s:e, 2 * C + h * d:2 * C + (h + 1) * d]"),
+    "transposed_proj": ("x1 = x + a @ W[\"w_proj\"] + P[\"b_proj\"]", "x1 = x + a @ W[\"w_proj\"].T + P[\"b_proj\"]"),
+    "gelu_erf_scale": ("np.vectorize(math.erf)(x / math.sqrt(2.0))", "np.vectorize(math.erf)(x / 2.0)"),
+}
+BLOCK_PINS = [
+    pins.test_layernorm_golden,
+    pins.test_gelu_forms_against_the_normal_cdf_table,
+    pins.test_block_attention_step_matches_the_c_oracle,
+    pins.test_block_with_zero_weights_is_the_identity,
+    lambda: pins.test_block_brute_force_tiny("erf"),
+    lambda: pins.test_block_brute_force_tiny("tanh"),
+]
+
+
+@pytest.mark.parametrize("name", sorted(BLOCK_MUTANTS))
+def test_block_pins_catch_planted_mistake(name):
+    old, new = BLOCK_MUTANTS[name]
+    text = open(BLOCK_SRC).read()
+    assert text.count(old) == 1, "mutation site not found: %s" % name
+    tmp = tempfile.mkdtemp(prefix="block_mutant_")
+    try:
+        path = os.path.join(tmp, "vit_block_mutant.py")
+        with open(path, "w") as f:
+            f.write(text.replace(old, new))
+        spec = importlib.util.spec_from_file_location("vit_block_mutant", path)
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        saved = pins.vb
+        pins.vb = mod
+        caught = []
+        try:
+            for pin in BLOCK_PINS:
+                try:
+                    pin()
+                except (AssertionError, ValueError, IndexError):
+                    caught.append(getattr(pin, "__name__", "lambda"))
+        finally:
+            pins.vb = saved
+        assert caught, "no pin caught mutant %s" % name
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+        sys.modules.pop("vit_block_mutant", None)
