@@ -265,6 +265,57 @@ def measure_repack(steps):
             "timing": "%d launches captured in one graph, %d replays, HIP events" % (per_graph, reps)}
 
 
+def measure_block(steps):
+    """One DeiT-S encoder block (random weights, bf16) on the headline batch:
+    on the packed rows (T = B * 40, ragged attention) against the same block on
+    all B * N rows (padded attention with masked keys).  The analogue of the
+    pages' end-to-end comparison for one post-pruning block.  Device time per
+    forward from back-to-back calls between HIP events (host enqueue is faster
+    than the GPU work here)."""
+    import torch
+    from ragged_attention_token_amd import binding
+    from ragged_attention_token_amd import workloads as wl
+
+    w = wl.deits(256, 800)
+    C, H = w.C, w.H
+    P = wl.vit_block_params(C, 4, 1)
+    prm = {k: (torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).cuda() if k.startswith("w_")
+               else torch.from_numpy(v).cuda()) for k, v in P.items()}
+    blk = binding.Block(prm, H=H, scale=w.scale)
+    xb = wl.hidden_rows(w.B, w.N, C, 2)
+    x_all = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).cuda()
+    keep = torch.from_numpy(w.keep).cuda()
+    rows = w.B * w.N
+    xp = torch.empty_like(x_all)
+    cu = torch.zeros(w.B + 1, dtype=torch.int32, device="cuda")
+    gather = torch.zeros(rows, dtype=torch.int32, device="cuda")
+    binding.rag_pack(keep, x_all, xp, cu, gather)
+    T, L = w.T, int(w.lengths.max())
+    y_p, y_pad = torch.empty_like(x_all), torch.empty_like(x_all)
+
+    def timed(fn):
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+        k = max(20, min(200, steps // 10))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(k):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / k
+
+    packed_us = timed(lambda: blk.forward(xp, y_p, T, cu, L))
+    padded_us = timed(lambda: blk.forward_padded(x_all, y_pad, keep))
+    blk.close()
+    return {"workload": "DeiT-S block (C=384, H=6, MLP 4x, random bf16 weights), B=256: "
+                        "%d packed rows (80%% prune) vs %d padded rows" % (T, rows),
+            "packed_block_us": packed_us, "padded_block_us": padded_us,
+            "speedup": padded_us / packed_us,
+            "packed_tokens_per_s": T / packed_us * 1e6}
+
+
 def sweep(steps):
     """Prune-rate sweep on the DeiT-S shape: per-launch device time of each kernel
     and of a whole pass (three launches, and one graph launch)."""
@@ -389,6 +440,7 @@ def main():
         "dispatch_floor_us": floor,
     }
     res["repack"] = measure_repack(args.steps)
+    res["vit_block"] = measure_block(args.steps)
     if not args.no_sweep:
         res["sweep"] = sweep(args.steps)
     if not args.no_cpu:

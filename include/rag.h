@@ -43,6 +43,7 @@
 #ifndef RAG_H
 #define RAG_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -324,6 +325,68 @@ RAG_API rag_status rag_measure_dispatch(rag_pipeline* p, int32_t warmup, int32_t
  */
 #define RAG_STAGES_N 7
 RAG_API rag_status rag_measure_stages(rag_pipeline* p, int32_t iters, double* out_us, void* stream);
+
+/*
+ * ---- one ViT encoder block on packed rows (end-to-end timing) ----------------
+ *
+ * [abstract] reports end-to-end throughput of pruned DeiT models whose blocks
+ * run on the packed tokens; the pages fix the attention and the packing, not
+ * the rest of the block.  rag_block runs DeiT's pre-norm encoder block with
+ * the caller's (e.g. random) weights on [rows, C] bf16 token rows, C = H * 64:
+ *     h = LN1(x); qkv = h Wqkv + bqkv; a = attention(qkv);
+ *     x1 = x + a Wproj + bproj; m = GELU(LN2(x1) W1 + b1); y = x1 + m W2 + b2
+ * with this library's attention (ragged over cu_seqlens, or the padded form
+ * over keep) and LayerNorm, and hipBLASLt for the four matrix products (bf16
+ * inputs, fp32 accumulation; bias, GELU and residual applied in its epilogue;
+ * GELU is the library epilogue's).  Every intermediate is stored as bf16.
+ *
+ * Weights: bf16, row-major [in, out] (y = x W), 16-byte aligned; Wqkv's
+ * output columns are q | k | v, each head-major (head h = columns h*64 ..).
+ * Biases and LayerNorm gamma / beta: fp32.  workspace: device memory the
+ * library GEMMs may use (caller-owned; 32 MiB is ample), may be NULL with 0
+ * bytes.  The descriptor's pointers must stay valid while the block exists.
+ */
+typedef struct rag_block_desc {
+    int32_t H;          /* heads; C = H * 64, at most 2048 */
+    int32_t mlp_ratio;  /* MLP hidden width = mlp_ratio * C (DeiT: 4), 1 .. 8 */
+    float eps;          /* LayerNorm epsilon (DeiT: 1e-6), > 0 */
+    float scale;        /* attention scale (e.g. 1/sqrt(64)), finite */
+    const void* ln1_gamma;
+    const void* ln1_beta;
+    const void* w_qkv;  /* [C, 3C] */
+    const void* b_qkv;  /* [3C] */
+    const void* w_proj; /* [C, C] */
+    const void* b_proj; /* [C] */
+    const void* ln2_gamma;
+    const void* ln2_beta;
+    const void* w_fc1;  /* [C, mlp_ratio*C] */
+    const void* b_fc1;  /* [mlp_ratio*C] */
+    const void* w_fc2;  /* [mlp_ratio*C, C] */
+    const void* b_fc2;  /* [C] */
+    void* workspace;
+    size_t workspace_bytes;
+} rag_block_desc;
+
+typedef struct rag_block rag_block;
+
+/* Device scratch a forward pass over `rows` rows needs (0 for bad arguments). */
+RAG_API size_t rag_block_scratch_bytes(int32_t rows, int32_t H, int32_t mlp_ratio);
+/* Allocates host-side state (the GEMM library handle); no device memory. */
+RAG_API rag_status rag_block_create(const rag_block_desc* desc, rag_block** out);
+/* y = block(x) over `rows` packed rows (a host value: e.g. B times the kept
+ * count of a fixed-rate pruning stage); attention over cu_seqlens (int32[B+1],
+ * device) with max_seqlen as in rag_attn.  x, y: bf16 [rows, C] contiguous,
+ * 16-byte aligned.  scratch: >= rag_block_scratch_bytes(rows, ...) bytes.  The
+ * first call at a given `rows` also builds the GEMM plans (host work). */
+RAG_API rag_status rag_block_forward(rag_block* blk, const void* x, void* y, int32_t rows,
+                                     const int32_t* cu_seqlens, int32_t B, int32_t max_seqlen,
+                                     void* scratch, size_t scratch_bytes, void* stream);
+/* The same block on all B*N rows of the [B, N] layout with the padded
+ * attention (keys with keep == 0 masked): the comparator of the packed pass. */
+RAG_API rag_status rag_block_forward_padded(rag_block* blk, const void* x, void* y,
+                                            const uint8_t* keep, int32_t B, int32_t N,
+                                            void* scratch, size_t scratch_bytes, void* stream);
+RAG_API void rag_block_destroy(rag_block* blk);
 
 /* Message for the last non-OK status returned on the calling thread. */
 RAG_API const char* rag_last_error(void);

@@ -10,7 +10,7 @@ __all__ = ["binding", "workloads", "build"]
 
 def __getattr__(name):
     if name in ("rag_pack", "rag_repack", "rag_attn", "rag_unpack", "rag_attn_padded", "rag_attn_gathered",
-                "Pipeline", "RagError", "last_error"):
+                "Pipeline", "Block", "RagError", "last_error"):
         from . import binding
         return getattr(binding, name)
     raise AttributeError(name)

@@ -32,7 +32,8 @@ EXPORTS = ("rag_pack", "rag_repack", "rag_attn", "rag_unpack", "rag_attn_padded"
            "rag_pipeline_create", "rag_pipeline_launch", "rag_pipeline_launch_eager",
            "rag_pipeline_launch_fused", "rag_pipeline_destroy",
            "rag_measure_dispatch", "rag_measure_stages", "rag_last_error", "rag_status_string",
-           "rag_version")
+           "rag_version", "rag_block_scratch_bytes", "rag_block_create", "rag_block_forward",
+           "rag_block_forward_padded", "rag_block_destroy")
 
 _lib = None
 
@@ -58,6 +59,20 @@ class PipelineDesc(ctypes.Structure):
         ("o_packed", ctypes.c_void_p), ("o_packed_row_stride", ctypes.c_int64),
         ("dst", ctypes.c_void_p), ("dst_row_stride", ctypes.c_int64),
         ("unpack_flags", ctypes.c_uint32),
+    ]
+
+
+class BlockDesc(ctypes.Structure):
+    _fields_ = [
+        ("H", ctypes.c_int32), ("mlp_ratio", ctypes.c_int32),
+        ("eps", ctypes.c_float), ("scale", ctypes.c_float),
+        ("ln1_gamma", ctypes.c_void_p), ("ln1_beta", ctypes.c_void_p),
+        ("w_qkv", ctypes.c_void_p), ("b_qkv", ctypes.c_void_p),
+        ("w_proj", ctypes.c_void_p), ("b_proj", ctypes.c_void_p),
+        ("ln2_gamma", ctypes.c_void_p), ("ln2_beta", ctypes.c_void_p),
+        ("w_fc1", ctypes.c_void_p), ("b_fc1", ctypes.c_void_p),
+        ("w_fc2", ctypes.c_void_p), ("b_fc2", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
     ]
 
 
@@ -89,13 +104,21 @@ def load(path: str = LIB_PATH):
     lib.rag_pipeline_destroy.restype = None
     lib.rag_measure_dispatch.argtypes = [vp, i32, i32, ctypes.POINTER(ctypes.c_double), vp]
     lib.rag_measure_stages.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_double), vp]
+    lib.rag_block_scratch_bytes.argtypes = [i32, i32, i32]
+    lib.rag_block_scratch_bytes.restype = ctypes.c_size_t
+    lib.rag_block_create.argtypes = [ctypes.POINTER(BlockDesc), ctypes.POINTER(vp)]
+    lib.rag_block_forward.argtypes = [vp, vp, vp, i32, vp, i32, i32, vp, ctypes.c_size_t, vp]
+    lib.rag_block_forward_padded.argtypes = [vp, vp, vp, vp, i32, i32, vp, ctypes.c_size_t, vp]
+    lib.rag_block_destroy.argtypes = [vp]
+    lib.rag_block_destroy.restype = None
     lib.rag_last_error.restype = ctypes.c_char_p
     lib.rag_status_string.argtypes = [i32]
     lib.rag_status_string.restype = ctypes.c_char_p
     lib.rag_version.restype = i32
     for name in ("rag_pack", "rag_repack", "rag_attn", "rag_unpack", "rag_attn_padded", "rag_attn_gathered",
                  "rag_pipeline_create", "rag_pipeline_launch", "rag_pipeline_launch_eager",
-                 "rag_pipeline_launch_fused", "rag_measure_dispatch", "rag_measure_stages"):
+                 "rag_pipeline_launch_fused", "rag_measure_dispatch", "rag_measure_stages",
+                 "rag_block_create", "rag_block_forward", "rag_block_forward_padded"):
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -359,6 +382,82 @@ class Pipeline:
     def close(self) -> None:
         if getattr(self, "_h", None) is not None and self._h.value:
             load().rag_pipeline_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class Block:
+    """One DeiT encoder block on packed (or padded) bf16 token rows; see
+    rag_block_desc in include/rag.h.  `params` maps names to GPU tensors:
+    ln1_gamma, ln1_beta, ln2_gamma, ln2_beta, b_qkv, b_proj, b_fc1, b_fc2
+    (fp32) and w_qkv [C, 3C], w_proj [C, C], w_fc1 [C, hidden], w_fc2
+    [hidden, C] (bf16, row-major [in, out]).  The tensors and the workspace
+    are kept alive here."""
+
+    NAMES = ("ln1_gamma", "ln1_beta", "w_qkv", "b_qkv", "w_proj", "b_proj", "ln2_gamma",
+             "ln2_beta", "w_fc1", "b_fc1", "w_fc2", "b_fc2")
+
+    def __init__(self, params: dict, H: int, scale: float, mlp_ratio: int = 4, eps: float = 1e-6,
+                 workspace_bytes: int = 32 << 20):
+        self.params = {k: _gpu(params[k], k).contiguous() for k in self.NAMES}
+        self.H, self.mlp_ratio = int(H), int(mlp_ratio)
+        self.C = self.H * RAG_HEAD_DIM
+        self.workspace = torch.empty(max(workspace_bytes, 16), dtype=torch.uint8, device="cuda")
+        d = BlockDesc()
+        d.H, d.mlp_ratio, d.eps, d.scale = self.H, self.mlp_ratio, float(eps), float(scale)
+        for k in self.NAMES:
+            setattr(d, k, self.params[k].data_ptr())
+        d.workspace = self.workspace.data_ptr()
+        d.workspace_bytes = int(workspace_bytes)
+        self._desc = d
+        handle = ctypes.c_void_p()
+        _check(load().rag_block_create(ctypes.byref(d), ctypes.byref(handle)))
+        self._h = handle
+        self._scratch = None
+
+    def _scratch_for(self, rows: int) -> torch.Tensor:
+        need = load().rag_block_scratch_bytes(int(rows), self.H, self.mlp_ratio)
+        if self._scratch is None or self._scratch.numel() < need:
+            self._scratch = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+        return self._scratch
+
+    def _rows(self, x, y, rows):
+        for t, name in ((x, "x"), (y, "y")):
+            _gpu(t, name)
+            if t.dtype != torch.bfloat16 or not t.is_contiguous() or t.dim() != 2 \
+                    or t.shape[1] != self.C or t.shape[0] < rows:
+                raise ValueError("%s must be a contiguous bf16 [>= rows, C] tensor" % name)
+
+    def forward(self, x: torch.Tensor, y: torch.Tensor, rows: int, cu_seqlens: torch.Tensor,
+                max_seqlen: int, stream=None) -> None:
+        """y[:rows] = block(x[:rows]) with ragged attention over cu_seqlens."""
+        self._rows(x, y, rows)
+        _gpu(cu_seqlens, "cu_seqlens")
+        sc = self._scratch_for(rows)
+        _check(load().rag_block_forward(self._h, x.data_ptr(), y.data_ptr(), int(rows),
+                                        cu_seqlens.data_ptr(), cu_seqlens.numel() - 1,
+                                        int(max_seqlen), sc.data_ptr(), sc.numel(),
+                                        _stream(stream)))
+
+    def forward_padded(self, x: torch.Tensor, y: torch.Tensor, keep: torch.Tensor,
+                       stream=None) -> None:
+        """y = block(x) on all B*N rows, padded attention with masked keys."""
+        _gpu(keep, "keep")
+        B, N = keep.shape
+        self._rows(x, y, B * N)
+        sc = self._scratch_for(B * N)
+        _check(load().rag_block_forward_padded(self._h, x.data_ptr(), y.data_ptr(),
+                                               keep.data_ptr(), B, N, sc.data_ptr(), sc.numel(),
+                                               _stream(stream)))
+
+    def close(self) -> None:
+        if self._h:
+            load().rag_block_destroy(self._h)
             self._h = None
 
     def __del__(self):

@@ -44,6 +44,9 @@ rag_status validate_attn_gathered(const uint8_t* keep, int32_t B, int32_t N, int
                                   int32_t H, int32_t head_dim, float scale, const void* o,
                                   int64_t o_row_stride, int32_t out_dtype, uint32_t flags);
 rag_status validate_pipeline(const rag_pipeline_desc* d);
+rag_status validate_block_desc(const rag_block_desc* d);
+rag_status validate_block_call(const void* x, const void* y, int32_t rows, int32_t C,
+                               const void* scratch, size_t scratch_given, size_t scratch_needed);
 
 inline int dtype_bytes(int32_t dt) { return dt == RAG_DTYPE_F32 ? 4 : 2; }
 

@@ -263,8 +263,6 @@ rag_status validate_pipeline(const rag_pipeline_desc* d)
                                   d->unpack_flags);
 }
 
-}  // namespace rag
-
 extern "C" RAG_API const char* rag_last_error(void) { return rag::g_error; }
 
 extern "C" RAG_API const char* rag_status_string(rag_status s)
@@ -280,3 +278,44 @@ extern "C" RAG_API const char* rag_status_string(rag_status s)
 }
 
 extern "C" RAG_API int32_t rag_version(void) { return 100; }
+
+rag_status validate_block_desc(const rag_block_desc* d)
+{
+    if (!d) return set_error(RAG_ERR_INVALID_ARG, "desc is NULL");
+    if (d->H < 1 || d->H > 32) return set_error(RAG_ERR_UNSUPPORTED, "H=%d must lie in [1, 32]", d->H);
+    if (d->mlp_ratio < 1 || d->mlp_ratio > 8)
+        return set_error(RAG_ERR_UNSUPPORTED, "mlp_ratio=%d must lie in [1, 8]", d->mlp_ratio);
+    if (!(d->eps > 0.f) || !std::isfinite(d->eps))
+        return set_error(RAG_ERR_INVALID_ARG, "eps must be positive and finite");
+    if (!std::isfinite(d->scale)) return set_error(RAG_ERR_INVALID_ARG, "scale must be finite");
+    const void* ptrs[] = {d->ln1_gamma, d->ln1_beta, d->w_qkv, d->b_qkv, d->w_proj, d->b_proj,
+                          d->ln2_gamma, d->ln2_beta, d->w_fc1, d->b_fc1, d->w_fc2, d->b_fc2};
+    const char* names[] = {"ln1_gamma", "ln1_beta", "w_qkv", "b_qkv", "w_proj", "b_proj",
+                           "ln2_gamma", "ln2_beta", "w_fc1", "b_fc1", "w_fc2", "b_fc2"};
+    for (int i = 0; i < 12; ++i) {
+        if (!ptrs[i]) return set_error(RAG_ERR_INVALID_ARG, "%s is NULL", names[i]);
+        if (!aligned16(ptrs[i])) return set_error(RAG_ERR_ALIGNMENT, "%s must be 16-byte aligned", names[i]);
+    }
+    if (d->workspace_bytes && !d->workspace)
+        return set_error(RAG_ERR_INVALID_ARG, "workspace is NULL but workspace_bytes > 0");
+    if (d->workspace && !aligned16(d->workspace))
+        return set_error(RAG_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
+    return RAG_OK;
+}
+
+rag_status validate_block_call(const void* x, const void* y, int32_t rows, int32_t C,
+                               const void* scratch, size_t scratch_given, size_t scratch_needed)
+{
+    if (rows < 0) return set_error(RAG_ERR_INVALID_ARG, "rows=%d must be >= 0", rows);
+    if ((int64_t)rows * 9 * C >= ((int64_t)1 << 31))
+        return set_error(RAG_ERR_UNSUPPORTED, "rows=%d too large for 32-bit row offsets", rows);
+    if (!x || !y || !scratch) return set_error(RAG_ERR_INVALID_ARG, "x, y and scratch must not be NULL");
+    if (!aligned16(x) || !aligned16(y) || !aligned16(scratch))
+        return set_error(RAG_ERR_ALIGNMENT, "x, y and scratch must be 16-byte aligned");
+    if (scratch_given < scratch_needed)
+        return set_error(RAG_ERR_INVALID_ARG, "scratch of %zu bytes is smaller than the %zu needed",
+                         scratch_given, scratch_needed);
+    return RAG_OK;
+}
+
+}  // namespace rag
