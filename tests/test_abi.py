@@ -191,3 +191,41 @@ def test_attn_gathered_rejects(lib):
     assert call(q=A + 4) == ALIGN
     assert call(scale=float("nan")) == INVALID
     assert lib.rag_pipeline_launch_fused(None, None) == INVALID
+
+
+def _block_desc(**kw):
+    d = binding.BlockDesc()
+    d.H, d.mlp_ratio, d.eps, d.scale = 6, 4, 1e-6, 0.125
+    for i, name in enumerate(binding.Block.NAMES):
+        setattr(d, name, A + 0x1000 * i)
+    d.workspace, d.workspace_bytes = A + 0x100000, 1 << 20
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+@pytest.mark.parametrize("kwargs,status,needle", [
+    (dict(H=0), UNSUPPORTED, "H=0"),
+    (dict(H=33), UNSUPPORTED, "H=33"),
+    (dict(mlp_ratio=9), UNSUPPORTED, "mlp_ratio"),
+    (dict(eps=0.0), INVALID, "eps"),
+    (dict(scale=float("inf")), INVALID, "scale"),
+    (dict(w_qkv=None), INVALID, "w_qkv"),
+    (dict(b_fc2=A + 4), ALIGN, "b_fc2"),
+    (dict(workspace=None), INVALID, "workspace"),
+])
+def test_block_create_rejects(lib, kwargs, status, needle):
+    h = ctypes.c_void_p()
+    d = _block_desc(**kwargs)
+    assert lib.rag_block_create(ctypes.byref(d), ctypes.byref(h)) == status
+    assert needle in binding.last_error()
+    assert not h.value
+
+
+def test_block_calls_reject_without_a_block(lib):
+    assert lib.rag_block_create(None, None) == INVALID
+    assert lib.rag_block_forward(None, A, A, 10, A, 1, 10, A, 1 << 20, None) == INVALID
+    assert lib.rag_block_forward_padded(None, A, A, A, 1, 10, A, 1 << 20, None) == INVALID
+    lib.rag_block_destroy(None)  # a no-op
+    assert lib.rag_block_scratch_bytes(-1, 6, 4) == 0
+    assert lib.rag_block_scratch_bytes(10, 6, 4) == 10 * (6 * 384 + 4 * 384) * 2
