@@ -342,6 +342,35 @@ def sweep(steps):
     return out
 
 
+def other_shapes(steps):
+    """The DeiT-B shapes: highly ragged lengths at N = 197 (B = 64) and the 384x384
+    input (N = 577, B = 32, about half the tokens kept): per-launch device time of
+    each kernel, the passes, and the padded comparator."""
+    import torch
+    from ragged_attention_token_amd import workloads as wl
+
+    out = {}
+    for w in (wl.deitb_ragged(64), wl.deitb384(32)):
+        bf = Bufs(w)
+        bf.pipe.launch()
+        torch.cuda.synchronize()
+        m = bf.pipe.measure_stages(max(50, min(steps, 400)))
+        alg = algorithmic(w, 2)
+        rec = {"B": w.B, "N": w.N, "H": w.H, "T": w.T, "max_seqlen": bf.max_seqlen,
+               "pack_us": m["pack"], "attn_us": m["attn"], "unpack_us": m["unpack"],
+               "padded_attn_us": m["padded"], "pipeline_us": m["eager_pass"],
+               "fused_pass_us": m["fused_pass"],
+               "attn_hbm_frac": alg["attn"] / m["attn"] * 1e-3 / HBM_PEAK_GBS,
+               "attn_mfma_frac": alg["attn_flops"] / m["attn"] * 1e-6 / BF16_PEAK_TFLOPS,
+               "padded_mfma_frac": alg["padded_flops"] / m["padded"] * 1e-6 / BF16_PEAK_TFLOPS}
+        rec["ragged_pipeline_vs_padded_attn"] = m["padded"] / m["eager_pass"]
+        out[w.name] = rec
+        print("%s: attn %.2f us, pipeline %.2f us, padded %.2f us" %
+              (w.name, m["attn"], m["eager_pass"], m["padded"]), file=sys.stderr, flush=True)
+        del bf
+    return out
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -441,6 +470,7 @@ def main():
     }
     res["repack"] = measure_repack(args.steps)
     res["vit_block"] = measure_block(args.steps)
+    res["deitb_shapes"] = other_shapes(args.steps)
     if not args.no_sweep:
         res["sweep"] = sweep(args.steps)
     if not args.no_cpu:
