@@ -213,8 +213,7 @@ def _cpu_model():
 
 
 def measure_repack(steps):
-    """A second pruning stage on a packed batch (SURVEY-style progressive
-    pruning): DeiT-S at B = 256 packed at 50% prune (99 kept per image), then
+    """A second pruning stage on a packed batch (progressive pruning): DeiT-S at B = 256 packed at 50% prune (99 kept per image), then
     re-packed to 40 per image (the headline's kept count) with rag_repack.
     Device time per launch from a captured run of back-to-back launches (no host
     work between them), and the launch's algorithmic bytes."""
@@ -339,6 +338,63 @@ def sweep(steps):
             print("sweep B=%d p=%03d: attn %.2f us, pipeline %.2f us" %
                   (B, p, rec["attn_us"], rec["pipeline_us"]), file=sys.stderr, flush=True)
             del bf
+    return out
+
+
+def graph_us(call, steps, per_graph=50):
+    """Device microseconds per call: `per_graph` back-to-back calls captured in
+    one graph, replayed, timed with events on the capturing stream."""
+    import torch
+
+    call()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(per_graph):
+            call()
+    graph.replay()
+    torch.cuda.synchronize()
+    reps = max(4, min(40, steps // per_graph))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * per_graph)
+
+
+def tile_list_comparison(steps):
+    """rag_attn (grid with one slot per (head, image[, query split])) against
+    rag_attn_tiled (the device-built tile list) on the ragged and long-sequence
+    shapes and on uniform lengths; the outputs are checked equal bit for bit."""
+    import torch
+    from ragged_attention_token_amd import binding
+    from ragged_attention_token_amd import workloads as wl
+
+    out = {}
+    for w in (wl.deitb_ragged(64), wl.deitb384(32), wl.deits(256, 0), wl.deits(256, 800),
+              wl.deits(4, 0), wl.deits(1, 500)):
+        bf = Bufs(w)
+        bf.pack()
+        C, p = w.C, bf.packed
+        o_t = torch.empty_like(bf.o_packed)
+
+        def attn(o, tiled):
+            binding.rag_attn(p[:, :C], p[:, C:2 * C], p[:, 2 * C:], bf.cu, bf.max_seqlen, o, H=w.H,
+                             scale=w.scale, tiled=tiled)
+
+        attn(bf.o_packed, False)
+        attn(o_t, True)
+        torch.cuda.synchronize()
+        assert torch.equal(bf.o_packed[:w.T].view(torch.uint8), o_t[:w.T].view(torch.uint8))
+        grid = graph_us(lambda: attn(bf.o_packed, False), steps)
+        tiled = graph_us(lambda: attn(o_t, True), steps)
+        out[w.name] = {"B": w.B, "N": w.N, "H": w.H, "T": w.T, "max_seqlen": bf.max_seqlen,
+                       "rag_attn_us": grid, "rag_attn_tiled_us": tiled, "tiled_vs_grid": grid / tiled}
+        print("%s: rag_attn %.2f us, rag_attn_tiled %.2f us" % (w.name, grid, tiled), file=sys.stderr,
+              flush=True)
+        del bf
     return out
 
 
@@ -471,6 +527,7 @@ def main():
     res["repack"] = measure_repack(args.steps)
     res["vit_block"] = measure_block(args.steps)
     res["deitb_shapes"] = other_shapes(args.steps)
+    res["tile_list"] = tile_list_comparison(args.steps)
     if not args.no_sweep:
         res["sweep"] = sweep(args.steps)
     if not args.no_cpu:

@@ -188,6 +188,28 @@ RAG_API rag_status rag_attn(const void* q, const void* k, const void* v, int64_t
                             void* o, int64_t o_row_stride, rag_dtype out_dtype, void* stream);
 
 /*
+ * rag_attn_tiled -- rag_attn launched over a device-built tile list
+ * ([abstract]: attention on ragged post-pruning lengths; the work list is this
+ * library's design).
+ *
+ *   Same arguments, result and error behaviour as rag_attn, and the same
+ *   values bit for bit.  Instead of a grid with one slot per (head, image,
+ *   query tile) -- where every image gets as many slots as the longest one and
+ *   a short image's extra slots exit at once -- the launch is a 1-D grid whose
+ *   workgroups each derive one work item (an (image, head) pair, or one 64-row
+ *   query tile of it) from cu_seqlens on the device: items of images with more
+ *   64-key tiles come first, and all items of one pair run on one XCD.
+ *   Limits: B <= 1024, H <= 64 and max_seqlen <= 960 (RAG_ERR_UNSUPPORTED
+ *   otherwise, before any launch).
+ */
+RAG_API rag_status rag_attn_tiled(const void* q, const void* k, const void* v,
+                                  int64_t q_row_stride, int64_t k_row_stride, int64_t v_row_stride,
+                                  rag_dtype in_dtype, const int32_t* cu_seqlens, int32_t B,
+                                  int32_t max_seqlen, int32_t total_rows, int32_t H,
+                                  int32_t head_dim, float scale, void* o, int64_t o_row_stride,
+                                  rag_dtype out_dtype, void* stream);
+
+/*
  * rag_unpack -- scatter packed rows back to their batch positions
  * ([blog-method], write-back via cu_seqlens).
  *

@@ -9,7 +9,7 @@ __all__ = ["binding", "workloads", "build"]
 
 
 def __getattr__(name):
-    if name in ("rag_pack", "rag_repack", "rag_attn", "rag_unpack", "rag_attn_padded", "rag_attn_gathered",
+    if name in ("rag_pack", "rag_repack", "rag_attn", "rag_attn_tiled", "rag_unpack", "rag_attn_padded", "rag_attn_gathered",
                 "Pipeline", "Block", "RagError", "last_error"):
         from . import binding
         return getattr(binding, name)

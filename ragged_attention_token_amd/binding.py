@@ -28,7 +28,7 @@ RAG_FLOOR_N = 27
 RAG_STAGES_N = 7
 
 #: Every symbol include/rag.h declares.
-EXPORTS = ("rag_pack", "rag_repack", "rag_attn", "rag_unpack", "rag_attn_padded", "rag_attn_gathered",
+EXPORTS = ("rag_pack", "rag_repack", "rag_attn", "rag_attn_tiled", "rag_unpack", "rag_attn_padded", "rag_attn_gathered",
            "rag_pipeline_create", "rag_pipeline_launch", "rag_pipeline_launch_eager",
            "rag_pipeline_launch_fused", "rag_pipeline_destroy",
            "rag_measure_dispatch", "rag_measure_stages", "rag_last_error", "rag_status_string",
@@ -90,6 +90,7 @@ def load(path: str = LIB_PATH):
     lib.rag_pack.argtypes = [vp, i32, i32, vp, i64, i32, vp, i64, vp, vp, vp, vp]
     lib.rag_attn.argtypes = [vp, vp, vp, i64, i64, i64, i32, vp, i32, i32, i32, i32, i32, f32, vp,
                              i64, i32, vp]
+    lib.rag_attn_tiled.argtypes = lib.rag_attn.argtypes
     lib.rag_unpack.argtypes = [vp, i64, i32, vp, vp, i32, i32, vp, i64, u32, vp]
     lib.rag_repack.argtypes = [vp, vp, vp, i32, i32, i32, vp, i64, i32, vp, i64, vp, vp, vp]
     lib.rag_attn_padded.argtypes = [vp, vp, vp, i64, i64, i64, i32, vp, i32, i32, i32, i32, f32,
@@ -115,7 +116,7 @@ def load(path: str = LIB_PATH):
     lib.rag_status_string.argtypes = [i32]
     lib.rag_status_string.restype = ctypes.c_char_p
     lib.rag_version.restype = i32
-    for name in ("rag_pack", "rag_repack", "rag_attn", "rag_unpack", "rag_attn_padded", "rag_attn_gathered",
+    for name in ("rag_pack", "rag_repack", "rag_attn", "rag_attn_tiled", "rag_unpack", "rag_attn_padded", "rag_attn_gathered",
                  "rag_pipeline_create", "rag_pipeline_launch", "rag_pipeline_launch_eager",
                  "rag_pipeline_launch_fused", "rag_measure_dispatch", "rag_measure_stages",
                  "rag_block_create", "rag_block_forward", "rag_block_forward_padded"):
@@ -230,9 +231,10 @@ def rag_repack(keep_packed: torch.Tensor, cu_in: torch.Tensor, gather_in: torch.
 
 def rag_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
              max_seqlen: int, o: torch.Tensor, H: int, scale: float, head_dim: int = RAG_HEAD_DIM,
-             total_rows: Optional[int] = None, stream=None) -> None:
+             total_rows: Optional[int] = None, stream=None, tiled: bool = False) -> None:
     """q, k, v, o: [rows, >= H*head_dim] (row stride free, rows contiguous inside);
-    cu_seqlens int32 [B+1] on the GPU; max_seqlen a host upper bound."""
+    cu_seqlens int32 [B+1] on the GPU; max_seqlen a host upper bound.  tiled:
+    call rag_attn_tiled (the same result over the device-built tile list)."""
     qp, qs = _rows(q, "q")
     kp, ks = _rows(k, "k")
     vp, vs = _rows(v, "v")
@@ -247,9 +249,15 @@ def rag_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torc
     if tr > rows:
         raise ValueError("total_rows larger than the buffers")
     B = cu_seqlens.numel() - 1
-    _check(load().rag_attn(qp, kp, vp, qs, ks, vs, _dtype_code(q), cu_seqlens.data_ptr(), B,
-                           int(max_seqlen), tr, int(H), int(head_dim), float(scale), op, os_,
-                           _dtype_code(o), _stream(stream)))
+    fn = load().rag_attn_tiled if tiled else load().rag_attn
+    _check(fn(qp, kp, vp, qs, ks, vs, _dtype_code(q), cu_seqlens.data_ptr(), B, int(max_seqlen), tr,
+              int(H), int(head_dim), float(scale), op, os_, _dtype_code(o), _stream(stream)))
+
+
+def rag_attn_tiled(q, k, v, cu_seqlens, max_seqlen, o, H, scale, head_dim=RAG_HEAD_DIM,
+                   total_rows=None, stream=None) -> None:
+    """rag_attn over the device-built tile list (B <= 1024, max_seqlen <= 960)."""
+    rag_attn(q, k, v, cu_seqlens, max_seqlen, o, H, scale, head_dim, total_rows, stream, tiled=True)
 
 
 def rag_unpack(packed: torch.Tensor, cu_seqlens: torch.Tensor, gather_idx: torch.Tensor,

@@ -77,6 +77,7 @@ struct AttnParams {
     const uint8_t* keep;     // padded and gathered
     int32_t B, N, H, total_rows, max_len, n_qtiles, zero_dropped;
     int32_t lds_rows;        // LDS-resident kernel: K / V rows held, max_len rounded up to 32
+    int32_t tl_kt;           // tile-list launch: key tiles of the longest image (else 0)
     float scale_log2;        // scale * log2(e)
 };
 
@@ -269,6 +270,161 @@ __device__ __forceinline__ float online_inv(const Online& st)
     return l > 0.f ? 1.f / l : 0.f;
 }
 
+// ---- tile list of the ragged layout ---------------------------------------
+//
+// A tile-list launch covers the work items of a ragged batch with a 1-D grid
+// in which no slot belongs to a query tile that a short image lacks, and in
+// which the longest images come first ("Dispatch-Aware Ragged Attention for
+// Pruned Vision Transformers", abstract: the kernel runs on ragged
+// post-pruning lengths).  An item is one (image, head) pair, whole, or one
+// 64-row query tile of it (four 16-row blocks).  Each workgroup derives its
+// item from cu_seqlens alone (wave 0 does, and hands it to the other waves
+// through LDS; no atomics, nothing written by an earlier launch):
+//   * an image of L rows has nkt = ceil(L / 64) key tiles (0 when empty) and
+//     n = 1 item (whole pairs) or n = nkt items (query tiles);
+//   * items are ordered by nkt, largest first;
+//   * the pairs of one nkt class are dealt round-robin to the eight XCDs
+//     (workgroup w runs on XCD w mod 8) and all items of a pair go to its XCD,
+//     so the pair's K and V rows are fetched into one L2.
+// The grid is an upper bound the host computes from B, H and max_seqlen;
+// workgroups past the items of their XCD return at once (they come last).
+// Limits (checked by the host): B <= 1024 (lane l holds the key-tile counts of
+// images 64 i + l, 4 bits each, i < 16) and max_seqlen <= 960 (nkt <= 15).
+struct Item {
+    int b, h, q0, q1, L;  // query blocks [q0, q1)
+    int64_t row0;
+};
+
+// a / d and a % d for 0 <= a < 2^24, 1 <= d < 2^24 (wave-uniform values): a
+// float reciprocal estimate, then one correction step each way.
+__device__ __forceinline__ int udiv_small(int a, int d, int& rem)
+{
+    int q = (int)((float)a * __builtin_amdgcn_rcpf((float)d));
+    int r = a - q * d;
+    if (r < 0) { --q; r += d; }
+    if (r >= d) { ++q; r -= d; }
+    rem = r;
+    return q;
+}
+
+template <bool WHOLE>
+__device__ __forceinline__ bool tile_item(const AttnParams& p, Item& it)
+{
+    const int lane = threadIdx.x & 63;
+    const int nch = (p.B + 63) >> 6;
+    const auto rc = make_rsrc(p.cu, (uint32_t)(p.B + 1) * 4u);  // cu[b], b > B reads 0
+    auto seq_len = [&](int s, int e) {
+        s = min(max(s, 0), p.total_rows);
+        e = min(max(e, s), p.total_rows);
+        return min(e - s, p.max_len);
+    };
+    // the chunks' offsets are requested at once (straight-line code: no load
+    // waits for another): 4 chunks when B <= 256, else 16; chunks past B read
+    // zeros, i.e. empty images
+    int cs[16], ce[16];
+    auto load_chunks = [&](auto nc_tag) {
+        constexpr int NC = decltype(nc_tag)::value;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t off = 4u * (uint32_t)(64 * i + lane);
+            cs[i] = i < NC ? (int)__builtin_amdgcn_raw_buffer_load_b32(rc, off, 0, 0) : 0;
+            ce[i] = i < NC ? (int)__builtin_amdgcn_raw_buffer_load_b32(rc, off + 4u, 0, 0) : 0;
+        }
+    };
+    if (nch <= 4) load_chunks(std::integral_constant<int, 4>{});
+    else load_chunks(std::integral_constant<int, 16>{});
+    uint64_t kt4 = 0;  // key-tile count of image 64 i + lane in bits [4i, 4i + 4)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) kt4 |= (uint64_t)((seq_len(cs[i], ce[i]) + 63) >> 6) << (4 * i);
+    auto class_mask = [&](int i, int k) -> uint64_t {
+        return __ballot((int)((kt4 >> (4 * i)) & 15u) == k);
+    };
+
+    // the nkt class of this workgroup's item, and its place among the XCD's
+    // items of that class
+    const int x = blockIdx.x & 7;
+    int pos = blockIdx.x >> 3;
+    int k = p.tl_kt, G = 0;
+    for (; k >= 1; --k) {
+        G = 0;
+        for (int i = 0; i < nch; ++i) G += __popcll(class_mask(i, k));
+        const int pairs = G * p.H;
+        const int mine = pairs > x ? (pairs - x + 7) >> 3 : 0;  // pairs x, x + 8, ...
+        const int items = WHOLE ? mine : mine * k;
+        if (pos < items) break;
+        pos -= items;
+    }
+    if (k < 1) return false;
+    int part = 0, r;
+    const int pi = WHOLE ? pos : udiv_small(pos, k, part);
+    it.h = udiv_small(x + 8 * pi, G, r);  // pair x + 8 pi = h G + r: the r-th image of the class
+    int b = 0, s = 0, e = 0;
+    bool found = false;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {  // (constant i: the offsets stay in registers)
+        if (i < nch && !found) {
+            const uint64_t msk = class_mask(i, k);
+            const int c = __popcll(msk);
+            if (r < c) {
+                const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(msk >> 32),
+                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)msk, 0u));
+                const int l = __builtin_ctzll(__ballot(((msk >> lane) & 1u) && below == (uint32_t)r));
+                b = 64 * i + l;
+                s = __builtin_amdgcn_readlane(cs[i], l);  // the image's offsets, already loaded
+                e = __builtin_amdgcn_readlane(ce[i], l);
+                found = true;
+            }
+            r -= c;
+        }
+    }
+    it.b = b;
+    it.row0 = min(max(s, 0), p.total_rows);
+    it.L = seq_len(s, e);
+    const int nqb = (it.L + 15) >> 4;
+    it.q0 = WHOLE ? 0 : 4 * part;
+    it.q1 = WHOLE ? nqb : min(4 * part + 4, nqb);
+    return true;
+}
+
+// The workgroup's item: wave 0 derives it, the others read it from LDS (the
+// decode's loads and scalar steps are paid once per workgroup).  Returns false
+// for a workgroup past its XCD's items (uniform over the workgroup).
+template <bool WHOLE>
+__device__ __forceinline__ bool workgroup_item(const AttnParams& p, Item& it)
+{
+    __shared__ int s_item[7];
+    if (threadIdx.x < 64) {
+        Item w;
+        const bool ok = tile_item<WHOLE>(p, w);
+        if (threadIdx.x == 0) {
+            s_item[0] = ok ? w.b : -1;
+            s_item[1] = w.h;
+            s_item[2] = w.q0;
+            s_item[3] = w.q1;
+            s_item[4] = w.L;
+            s_item[5] = (int)w.row0;  // row0 <= total_rows < 2^31
+        }
+    }
+    __syncthreads();
+    it.b = s_item[0];
+    it.h = s_item[1];
+    it.q0 = s_item[2];
+    it.q1 = s_item[3];
+    it.L = s_item[4];
+    it.row0 = s_item[5];
+    return it.b >= 0;
+}
+
+// Grid of a tile-list launch: on each XCD at most ceil(B H n_max / 8) + sum_k n_k
+// items (n_k = 1 for whole pairs, k for query tiles; n_max = n_kt_max).
+int tile_list_grid(int B, int H, int kt_max, bool whole)
+{
+    const int64_t n_max = whole ? 1 : kt_max;
+    int64_t per_xcd = ((int64_t)B * H * n_max + 7) / 8;
+    per_xcd += whole ? kt_max : kt_max * (kt_max + 1) / 2;
+    return (int)(8 * per_xcd);
+}
+
 // Gathered layout with RAG_UNPACK_ZERO_DROPPED: head h of every dropped row of
 // the image is set to zero (one workgroup per (image, head) does it).
 template <bool OUT_F32>
@@ -286,7 +442,7 @@ __device__ void zero_dropped_head(const AttnParams& p, int64_t row0, int h)
     }
 }
 
-template <bool IN_F32, bool OUT_F32, int LAYOUT>
+template <bool IN_F32, bool OUT_F32, int LAYOUT, bool TILES>
 __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
 {
     constexpr bool PADDED = LAYOUT == kPadded;
@@ -306,16 +462,28 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
     extern __shared__ int s_pos[];  // gathered: the image's kept positions by rank (N ints)
     __shared__ int s_wsum[16];  // keep ranking: up to 4 planes x 4 waves
 
-    // ---- which (head, image, q-tile): a 3-D grid with the q-tile slowest, so
-    // that the first q-tile of every (image, head) -- the only one most pruned
-    // sequences have -- is dispatched before any tile that will exit at once.
-    const int h = blockIdx.x;
-    const int b = blockIdx.y;
+    // ---- which (head, image, query blocks): TILES, the tile list's item (four
+    // query blocks at most); otherwise a 3-D grid (head, image, q-tile of four
+    // blocks) with the q-tile slowest, so that the first q-tile of every
+    // (image, head) -- the only one most pruned sequences have -- is dispatched
+    // before any tile that will exit at once.
+    int h = blockIdx.x;
+    int b = blockIdx.y;
     const int qt = blockIdx.z;
 
     int64_t row0;
-    int L;
-    if constexpr (PADDED) {
+    int L, qlo, qhi;
+    if constexpr (TILES) {
+        static_assert(LAYOUT == kRagged, "the tile list is built from cu_seqlens");
+        Item it;
+        if (!workgroup_item<false>(p, it)) return;  // uniform over the workgroup
+        h = it.h;
+        b = it.b;
+        row0 = it.row0;
+        L = it.L;
+        qlo = it.q0;
+        qhi = it.q1;
+    } else if constexpr (PADDED) {
         row0 = (int64_t)b * p.N;
         L = p.N;
     } else if constexpr (GATHERED) {
@@ -330,12 +498,16 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
         row0 = s;
         L = min(e - s, p.max_len);
     }
-    const int q0 = qt * kBM;
-    if (q0 >= L) return;
+    if constexpr (!TILES) {
+        qlo = qt * (kBM / 16);
+        qhi = (L + 15) >> 4;
+    }
+    if (qlo >= qhi) return;
+    const int qrow = 16 * qlo;  // first query row of the workgroup
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r16 = lane & 15, g = lane >> 4;
-    const bool wave_active = q0 + wave * 16 < L;
+    const bool wave_active = qlo + wave < qhi;
     const int64_t hoff = (int64_t)h * kD;
 
     // Buffer resources covering this head's rows of the image: rows row0 ..
@@ -359,7 +531,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
     // Q^T as the B operand: lane holds query row r16, d = 8g..8g+7 and 32+8g..
     bf16x8 qh0, qh1, ql0 = {}, ql1 = {};
     {
-        const uint32_t off = row_off(q0 + wave * 16 + r16, qsb) + 8 * g * ES;
+        const uint32_t off = row_off(qrow + wave * 16 + r16, qsb) + 8 * g * ES;
         load8<IN_F32>(rq, off, qh0, ql0);
         load8<IN_F32>(rq, off + 32 * ES, qh1, ql1);
     }
@@ -492,7 +664,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
         const int piece = lane + 64 * j;
         const int r = piece / CHUNKS, cix = piece % CHUNKS;
         const u32x4 val = *reinterpret_cast<const u32x4*>(so + r * OUT_ROW + 16 * cix);
-        __builtin_amdgcn_raw_buffer_store_b128(val, ro, row_off(q0 + wave * 16 + r, osb) + 16 * cix, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(val, ro, row_off(qrow + wave * 16 + r, osb) + 16 * cix, 0, 0);
     }
 }
 
@@ -534,7 +706,9 @@ __device__ __forceinline__ bf16x4 ld_tr4(const char* lds_addr)
     return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)lds_addr));
 }
 
-template <bool OUT_F32, int LAYOUT, bool MULTI>
+// TL: 0 = grid of (head, image, query split); tile list of 1 = whole pairs,
+// 2 = 64-row query tiles.
+template <bool OUT_F32, int LAYOUT, bool MULTI, int TL>
 __global__ __launch_bounds__(64 * kMaxWaves) void attn_lds_kernel(AttnParams p)
 {
     constexpr bool PADDED = LAYOUT == kPadded;
@@ -543,7 +717,10 @@ __global__ __launch_bounds__(64 * kMaxWaves) void attn_lds_kernel(AttnParams p)
     extern __shared__ __attribute__((aligned(16))) char lds[];
     __shared__ int s_wsum[4 * kMaxWaves];  // keep ranking: up to 4 planes x W waves
 
-    const int h = blockIdx.x, b = blockIdx.y, qs = blockIdx.z;
+    constexpr bool TILES = TL != 0;
+    static_assert(!TILES || LAYOUT == kRagged, "the tile list is built from cu_seqlens");
+    int h = blockIdx.x, b = blockIdx.y;
+    const int qs = blockIdx.z;
     const int nw = blockDim.x >> 6;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r16 = lane & 15, g = lane >> 4;
@@ -557,8 +734,17 @@ __global__ __launch_bounds__(64 * kMaxWaves) void attn_lds_kernel(AttnParams p)
     uint8_t* s_keep = reinterpret_cast<uint8_t*>(lds + 2 * R * kRowBytes);
 
     int64_t row0;
-    int L;
-    if constexpr (PADDED) {
+    int L, qlo = qs * nw, qhi;  // this workgroup's query blocks: qlo + wave (+ k * qstride) < qhi
+    if constexpr (TILES) {
+        Item it;
+        if (!workgroup_item<TL == 1>(p, it)) return;  // uniform over the workgroup
+        h = it.h;
+        b = it.b;
+        row0 = it.row0;
+        L = it.L;
+        qlo = it.q0;
+        qhi = it.q1;
+    } else if constexpr (PADDED) {
         row0 = (int64_t)b * p.N;
         L = p.N;
         const int nkeep = (p.N + 63) & ~63;
@@ -575,8 +761,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void attn_lds_kernel(AttnParams p)
         row0 = s;
         L = min(e - s, p.max_len);
     }
-    const int nqb = (L + 15) >> 4;  // 16-row query blocks
-    if (qs * nw >= nqb) return;     // uniform over the workgroup
+    if constexpr (!TILES) qhi = (L + 15) >> 4;  // 16-row query blocks
+    if (qlo >= qhi) return;                      // uniform over the workgroup
 
     const int64_t hoff = (int64_t)h * kD;
     const int span = GATHERED ? p.N : L;
@@ -617,7 +803,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void attn_lds_kernel(AttnParams p)
     // Q^T as the B operand of S^T = K Q^T: lane holds query row r16 of the
     // block, d = 8g..8g+7 and 32+8g..32+8g+7.  The wave's blocks are
     // qs * W + wave + k * gridDim.z * W: one of them, or (MULTI) one or more.
-    int qb = qs * nw + wave;
+    int qb = qlo + wave;
     const int qstride = gridDim.z * nw;
     bf16x8 qa0, qa1;
     auto load_q = [&](int blk) {
@@ -625,10 +811,10 @@ __global__ __launch_bounds__(64 * kMaxWaves) void attn_lds_kernel(AttnParams p)
         qa0 = __builtin_bit_cast(bf16x8, ld16(rq, off));
         qa1 = __builtin_bit_cast(bf16x8, ld16(rq, off + 64));
     };
-    if (qb < nqb) load_q(qb);
+    if (qb < qhi) load_q(qb);
     __builtin_amdgcn_s_waitcnt(0);  // every load of this wave has landed (LDS included)
     __syncthreads();
-    if (qb >= nqb) return;
+    if (qb >= qhi) return;
 
     // Per-lane LDS offsets inside a 16-row block.
     //  K (A operand of S^T): row r16, chunks g and g + 4 of the row.
@@ -712,7 +898,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void attn_lds_kernel(AttnParams p)
         }
         if constexpr (!MULTI) break;  // (single-block launches: one block per wave)
         qb += qstride;
-        if (qb >= nqb) break;
+        if (qb >= qhi) break;
         load_q(qb);
     }
 }
@@ -736,11 +922,17 @@ void launch_lds_layout(const AttnParams& p, int layout, dim3 grid, dim3 block, s
                        hipStream_t st)
 {
     if (layout == kPadded)
-        hipLaunchKernelGGL((attn_lds_kernel<OUT_F32, kPadded, MULTI>), grid, block, lds_bytes, st, p);
+        hipLaunchKernelGGL((attn_lds_kernel<OUT_F32, kPadded, MULTI, 0>), grid, block, lds_bytes, st, p);
     else if (layout == kGathered)
-        hipLaunchKernelGGL((attn_lds_kernel<OUT_F32, kGathered, MULTI>), grid, block, lds_bytes, st, p);
-    else
-        hipLaunchKernelGGL((attn_lds_kernel<OUT_F32, kRagged, MULTI>), grid, block, lds_bytes, st, p);
+        hipLaunchKernelGGL((attn_lds_kernel<OUT_F32, kGathered, MULTI, 0>), grid, block, lds_bytes, st, p);
+    else if (p.tl_kt == 0)
+        hipLaunchKernelGGL((attn_lds_kernel<OUT_F32, kRagged, MULTI, 0>), grid, block, lds_bytes, st, p);
+    else if (grid.z == 1)  // tile list, many pairs: whole (image, head) pairs
+        hipLaunchKernelGGL((attn_lds_kernel<OUT_F32, kRagged, MULTI, 1>),
+                           dim3(tile_list_grid(p.B, p.H, p.tl_kt, true)), block, lds_bytes, st, p);
+    else  // tile list, few pairs: the query splits are 64-row query tiles
+        hipLaunchKernelGGL((attn_lds_kernel<OUT_F32, kRagged, false, 2>),
+                           dim3(tile_list_grid(p.B, p.H, p.tl_kt, false)), block, lds_bytes, st, p);
 }
 
 template <bool OUT_F32>
@@ -751,15 +943,19 @@ void launch_lds_variant(AttnParams p, int layout, size_t lds_bytes, hipStream_t 
     // two per wave beyond (so that two workgroups fit a CU and one's K / V load
     // overlaps the other's compute).  With few pairs the blocks are split over
     // gridDim.z workgroups of at most 4 waves, one block each, so that more CUs
-    // share the work.
+    // share the work.  A tile-list launch (p.tl_kt > 0, ragged layout) keeps
+    // these workgroup shapes, its items being the whole pairs, or the 64-row
+    // query tiles (4 blocks on 4 waves) with few pairs.
     const int nqb = (p.max_len + 15) / 16;
+    const bool many = (int64_t)p.B * p.H >= 256;
     int waves;
-    if ((int64_t)p.B * p.H >= 256)  // one block per wave up to 8, else two
+    if (many)  // one block per wave up to 8, else two
         waves = nqb <= 8 ? nqb : (nqb + 1) / 2;
     else
         waves = min(nqb, 4);
-    const int splits = (int64_t)p.B * p.H >= 256 ? 1 : (nqb + waves - 1) / waves;
+    const int splits = many ? 1 : (nqb + waves - 1) / waves;
     p.lds_rows = (p.max_len + kLdsRowAlign - 1) & ~(kLdsRowAlign - 1);
+    if (p.tl_kt > 0 && !many) waves = 4;
     const dim3 grid(p.H, p.B, splits), block(64 * waves);
     if (waves * splits >= nqb)
         launch_lds_layout<OUT_F32, false>(p, layout, grid, block, lds_bytes, st);
@@ -770,14 +966,19 @@ void launch_lds_variant(AttnParams p, int layout, size_t lds_bytes, hipStream_t 
 template <bool IN_F32, bool OUT_F32>
 void launch_variant(const AttnParams& p, int layout, hipStream_t st)
 {
+    if (p.tl_kt > 0) {  // the tile list's items: one 64-row q-tile's worth of blocks
+        const dim3 grid(tile_list_grid(p.B, p.H, p.tl_kt, false)), block(kThreads);
+        hipLaunchKernelGGL((attn_kernel<IN_F32, OUT_F32, kRagged, true>), grid, block, 0, st, p);
+        return;
+    }
     const dim3 grid(p.H, p.B, p.n_qtiles), block(kThreads);
     if (layout == kPadded)
-        hipLaunchKernelGGL((attn_kernel<IN_F32, OUT_F32, kPadded>), grid, block, 0, st, p);
+        hipLaunchKernelGGL((attn_kernel<IN_F32, OUT_F32, kPadded, false>), grid, block, 0, st, p);
     else if (layout == kGathered)
-        hipLaunchKernelGGL((attn_kernel<IN_F32, OUT_F32, kGathered>), grid, block,
+        hipLaunchKernelGGL((attn_kernel<IN_F32, OUT_F32, kGathered, false>), grid, block,
                            sizeof(int) * (size_t)p.N, st, p);
     else
-        hipLaunchKernelGGL((attn_kernel<IN_F32, OUT_F32, kRagged>), grid, block, 0, st, p);
+        hipLaunchKernelGGL((attn_kernel<IN_F32, OUT_F32, kRagged, false>), grid, block, 0, st, p);
 }
 
 }  // namespace
@@ -808,6 +1009,7 @@ int launch_attn(const void* q, const void* k, const void* v, int64_t q_row_strid
     p.n_qtiles = (p.max_len + kBM - 1) / kBM;
     p.zero_dropped = (flags & RAG_UNPACK_ZERO_DROPPED) ? 1 : 0;
     p.lds_rows = 0;
+    p.tl_kt = (layout == kRagged && (flags & kAttnTileList)) ? (p.max_len + 63) / 64 : 0;
     p.scale_log2 = scale * 1.4426950408889634f;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool in_f32 = in_dtype == RAG_DTYPE_F32, out_f32 = out_dtype == RAG_DTYPE_F32;

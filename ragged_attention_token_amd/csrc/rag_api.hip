@@ -64,6 +64,26 @@ extern "C" RAG_API rag_status rag_attn(const void* q, const void* k, const void*
                       "rag_attn launch");
 }
 
+extern "C" RAG_API rag_status rag_attn_tiled(const void* q, const void* k, const void* v,
+                                             int64_t q_row_stride, int64_t k_row_stride,
+                                             int64_t v_row_stride, rag_dtype in_dtype,
+                                             const int32_t* cu_seqlens, int32_t B, int32_t max_seqlen,
+                                             int32_t total_rows, int32_t H, int32_t head_dim,
+                                             float scale, void* o, int64_t o_row_stride,
+                                             rag_dtype out_dtype, void* stream)
+{
+    rag_status s = rag::validate_attn(q, k, v, q_row_stride, k_row_stride, v_row_stride, in_dtype,
+                                      cu_seqlens, B, max_seqlen, total_rows, H, head_dim, scale, o,
+                                      o_row_stride, out_dtype);
+    if (s != RAG_OK) return s;
+    if ((s = rag::validate_tile_list(B, H, max_seqlen)) != RAG_OK) return s;
+    return hip_status(rag::launch_attn(q, k, v, q_row_stride, k_row_stride, v_row_stride, in_dtype,
+                                       cu_seqlens, nullptr, B, 0, max_seqlen, total_rows, H, scale,
+                                       o, o_row_stride, out_dtype, rag::kLayoutRagged,
+                                       rag::kAttnTileList, stream),
+                      "rag_attn_tiled launch");
+}
+
 extern "C" RAG_API rag_status rag_unpack(const void* packed, int64_t packed_row_stride,
                                          int32_t row_bytes, const int32_t* cu_seqlens,
                                          const int32_t* gather_idx, int32_t B, int32_t N,

@@ -32,6 +32,8 @@ rag_status validate_attn(const void* q, const void* k, const void* v, int64_t q_
                          const int32_t* cu_seqlens, int32_t B, int32_t max_seqlen,
                          int32_t total_rows, int32_t H, int32_t head_dim, float scale,
                          const void* o, int64_t o_row_stride, int32_t out_dtype);
+// rag_attn_tiled's extra limits (B, H, max_seqlen of the tile list).
+rag_status validate_tile_list(int32_t B, int32_t H, int32_t max_seqlen);
 rag_status validate_attn_padded(const void* q, const void* k, const void* v,
                                 int64_t q_row_stride, int64_t k_row_stride, int64_t v_row_stride,
                                 int32_t in_dtype, const uint8_t* keep, int32_t B, int32_t N,
@@ -72,6 +74,13 @@ int launch_unpack(const void* packed, int64_t packed_row_stride, int32_t row_byt
 // from the keep row, output written to those rows (flags: zero-dropped).
 // max_seqlen bounds the rows per image for layouts 0 and 2 (ignored for 1).
 enum { kLayoutRagged = 0, kLayoutPadded = 1, kLayoutGathered = 2 };
+// flags bit (library-internal, ragged layout): launch over the device-built
+// tile list (B <= kTileListMaxB, H <= kTileListMaxH, max_seqlen <=
+// kTileListMaxLen: the decode's item indices stay below 2^17).
+constexpr uint32_t kAttnTileList = 1u << 16;
+constexpr int kTileListMaxB = 1024;
+constexpr int kTileListMaxH = 64;
+constexpr int kTileListMaxLen = 960;
 int launch_attn(const void* q, const void* k, const void* v, int64_t q_row_stride,
                 int64_t k_row_stride, int64_t v_row_stride, int32_t in_dtype,
                 const int32_t* cu_seqlens, const uint8_t* keep, int32_t B, int32_t N,

@@ -193,6 +193,18 @@ rag_status validate_attn(const void* q, const void* k, const void* v, int64_t q_
                       out_dtype);
 }
 
+rag_status validate_tile_list(int32_t B, int32_t H, int32_t max_seqlen)
+{
+    if (H > kTileListMaxH)
+        return set_error(RAG_ERR_UNSUPPORTED, "tile list: H=%d exceeds %d", H, kTileListMaxH);
+    if (B > kTileListMaxB)
+        return set_error(RAG_ERR_UNSUPPORTED, "tile list: B=%d exceeds %d", B, kTileListMaxB);
+    if (max_seqlen > kTileListMaxLen)
+        return set_error(RAG_ERR_UNSUPPORTED, "tile list: max_seqlen=%d exceeds %d", max_seqlen,
+                         kTileListMaxLen);
+    return RAG_OK;
+}
+
 rag_status validate_attn_padded(const void* q, const void* k, const void* v,
                                 int64_t q_row_stride, int64_t k_row_stride, int64_t v_row_stride,
                                 int32_t in_dtype, const uint8_t* keep, int32_t B, int32_t N,

@@ -50,11 +50,12 @@ def gpu_pack(w: wl.Workload, want_max=True):
     return dict(keep=keep, src=src, packed=packed, cu=cu, gather=gather, max=mx)
 
 
-def gpu_attn(packed: torch.Tensor, cu: torch.Tensor, w: wl.Workload, out_dtype, max_seqlen=None):
+def gpu_attn(packed: torch.Tensor, cu: torch.Tensor, w: wl.Workload, out_dtype, max_seqlen=None,
+             tiled=False):
     C = w.C
     q, k, v = packed[:, 0:C], packed[:, C:2 * C], packed[:, 2 * C:3 * C]
     o = sentinel_like((packed.shape[0], C), out_dtype)
-    binding.rag_attn(q, k, v, cu, max_seqlen or w.N, o, H=w.H, scale=w.scale)
+    binding.rag_attn(q, k, v, cu, max_seqlen or w.N, o, H=w.H, scale=w.scale, tiled=tiled)
     torch.cuda.synchronize()
     return o
 

@@ -102,8 +102,9 @@ def test_repack_rejects(lib, kwargs, status, needle):
 
 
 def attn(lib, q=A, k=A, v=A, qs=1152, ks=1152, vs=1152, dt=BF16, cu=A, B=4, maxlen=197, tr=788,
-         H=6, hd=64, scale=0.125, o=A, os_=384, odt=F32):
-    return lib.rag_attn(q, k, v, qs, ks, vs, dt, cu, B, maxlen, tr, H, hd, scale, o, os_, odt, None)
+         H=6, hd=64, scale=0.125, o=A, os_=384, odt=F32, fn="rag_attn"):
+    return getattr(lib, fn)(q, k, v, qs, ks, vs, dt, cu, B, maxlen, tr, H, hd, scale, o, os_, odt,
+                            None)
 
 
 @pytest.mark.parametrize("kwargs,status,needle", [
@@ -126,7 +127,19 @@ def attn(lib, q=A, k=A, v=A, qs=1152, ks=1152, vs=1152, dt=BF16, cu=A, B=4, maxl
     (dict(maxlen=8192, qs=192000, ks=192000, vs=192000, os_=192000), UNSUPPORTED, "2^31"),
 ])
 def test_attn_rejects(lib, kwargs, status, needle):
-    assert attn(lib, **kwargs) == status
+    for fn in ("rag_attn", "rag_attn_tiled"):
+        assert attn(lib, fn=fn, **kwargs) == status
+        assert needle in binding.last_error()
+
+
+@pytest.mark.parametrize("kwargs,needle", [(dict(B=1025, tr=1025 * 197), "B=1025"),
+                                           (dict(H=65, os_=65 * 64, qs=3 * 65 * 64, ks=3 * 65 * 64,
+                                                 vs=3 * 65 * 64), "H=65"),
+                                           (dict(maxlen=961), "max_seqlen=961")])
+def test_attn_tiled_limits(lib, kwargs, needle):
+    """The tile list's own limits; rag_attn takes the same calls (no GPU work
+    happens here: the checks fail first, or the call is not made)."""
+    assert attn(lib, fn="rag_attn_tiled", **kwargs) == UNSUPPORTED
     assert needle in binding.last_error()
 
 
