@@ -160,6 +160,7 @@ constexpr float kLazyLog2 = 8.f;
 
 struct Online {
     float m;        // reference maximum of c * s for the lane's query row
+    float neg_m;    // the exponent offset: -m, or 0 while m is -inf (no key yet)
     f32x4 acc[4];   // O^T: acc[db][i] = O[query r16][16 db + 4 g + i] (unnormalised)
     f32x4 lsum;     // row sums of P (all four elements equal)
 };
@@ -167,6 +168,7 @@ struct Online {
 __device__ __forceinline__ void online_init(Online& st)
 {
     st.m = -INFINITY;
+    st.neg_m = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) st.acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     st.lsum = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -213,26 +215,29 @@ __device__ __forceinline__ void online_probs(f32x4 (&s)[4], int nk, const uint8_
             }
         }
     }
+    // this lane's maximum; the row's (over the four lanes of the query row) is
+    // only formed when the reference is set or moved: some lane exceeds
+    // m + kLazyLog2 exactly when the row maximum does (c > 0 keeps the order)
     float mloc = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]), fmaxf(fmaxf(s[0][3], s[1][0]), s[1][1]));
     mloc = fmaxf(mloc, fmaxf(fmaxf(fmaxf(s[1][2], s[1][3]), s[2][0]), fmaxf(fmaxf(s[2][1], s[2][2]), s[2][3])));
     mloc = fmaxf(mloc, fmaxf(fmaxf(s[3][0], s[3][1]), fmaxf(s[3][2], s[3][3])));
-    mloc = row_max(mloc) * c;
     if (first) {
-        st.m = mloc;
-    } else if (__ballot(mloc > st.m + kLazyLog2)) {  // uniform over the wave
-        const float m_new = fmaxf(st.m, mloc);
+        st.m = row_max(mloc) * c;
+        st.neg_m = (st.m == -INFINITY) ? 0.f : -st.m;
+    } else if (__ballot(mloc * c > st.m + kLazyLog2)) {  // uniform over the wave
+        const float m_new = fmaxf(st.m, row_max(mloc) * c);
         const float alpha = fast_exp2(st.m - m_new);
 #pragma unroll
         for (int db = 0; db < 4; ++db) st.acc[db] *= alpha;
         st.lsum *= alpha;
         st.m = m_new;
+        st.neg_m = (m_new == -INFINITY) ? 0.f : -m_new;
     }
-    const float m_use = (st.m == -INFINITY) ? 0.f : st.m;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
         if (FULL || 16 * kb < nk) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) s[kb][i] = fast_exp2(__builtin_fmaf(s[kb][i], c, -m_use));
+            for (int i = 0; i < 4; ++i) s[kb][i] = fast_exp2(__builtin_fmaf(s[kb][i], c, st.neg_m));
         } else {
             s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
