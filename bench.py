@@ -364,6 +364,120 @@ def graph_us(call, steps, per_graph=50):
     return e0.elapsed_time(e1) * 1e3 / (reps * per_graph)
 
 
+def _pct(xs):
+    xs = np.sort(np.asarray(xs, dtype=np.float64))
+    return {"p10": float(np.percentile(xs, 10)), "p50": float(np.percentile(xs, 50)),
+            "p90": float(np.percentile(xs, 90)), "n": int(xs.size)}
+
+
+def stage_samples(bf, hot_samples=100, cold_samples=30, per_graph=20):
+    """Per-launch device time of pack, attention and unpack as distributions.
+
+    hot: `hot_samples` samples, each one replay of a graph of `per_graph`
+    back-to-back launches between two events (the same graph replayed just
+    before, untimed, keeps the GPU busy while the host enqueues, so no host gap
+    is timed); per-launch time = elapsed / per_graph.
+    cold: `cold_samples` samples of ONE direct launch between two events, each
+    after 512 MiB of scratch traffic outside the timed region (about 100 us of
+    GPU work, during which the host enqueues the events and the launch, so no
+    host gap is timed either), which evicts the L2s and the 256 MB MALL so that
+    the stage reads its inputs from HBM:
+      cold_write_us: the scratch is written (what a preceding layer leaves: the
+        caches full of dirty lines, written back as the stage evicts them);
+      cold_read_us: the scratch is read (clean lines: HBM reads only)."""
+    import torch
+
+    stages = {"pack": bf.pack, "attn": bf.attn, "unpack": bf.unpack}
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(1, dtype=torch.int64, device="cuda")
+    out = {}
+    for name, fn in stages.items():
+        fn()
+        torch.cuda.synchronize()
+        g_many = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_many):
+            for _ in range(per_graph):
+                fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(max(hot_samples, cold_samples))]
+        for i in range(hot_samples):
+            g_many.replay()
+            ev[i][0].record()
+            g_many.replay()
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        rec = {"hot_us": _pct([a.elapsed_time(b) * 1e3 / per_graph for a, b in ev[:hot_samples]])}
+        for kind in ("write", "read"):
+            xs = []
+            for i in range(cold_samples):
+                if kind == "write":
+                    scratch.fill_(i & 0xFF)
+                else:
+                    torch.sum(scratch.view(torch.int64), dim=0, keepdim=True, out=sink)
+                ev[i][0].record()
+                fn()
+                ev[i][1].record()
+                torch.cuda.synchronize()
+                xs.append(ev[i][0].elapsed_time(ev[i][1]) * 1e3)
+            rec["cold_%s_us" % kind] = _pct(xs)
+        out[name] = rec
+        del g_many
+    del scratch
+    return out
+
+
+def timing_distributions(w_main):
+    """stage_samples on the headline workload and on the DeiT-B and B = 256, p = 0
+    shapes."""
+    from ragged_attention_token_amd import workloads as wl
+
+    out = {}
+    for w in (w_main, wl.deitb_ragged(64), wl.deitb384(32), wl.deits(256, 0)):
+        bf = Bufs(w)
+        out[w.name] = stage_samples(bf)
+        del bf
+    return out
+
+
+def python_binding_floor(iters=1000):
+    """rag_attn at minimal work (B = 1, L = 1) called through the Python binding,
+    then a device synchronize: wall-clock p10/p50/p90, to set against the C++
+    round trip of the same call (the difference is the binding's overhead)."""
+    import torch
+    from ragged_attention_token_amd import workloads as wl
+
+    bf = Bufs(wl.custom(B=1, N=197, H=6, lengths=[1], seed=0, name="floor_l1"))
+    bf.pack()
+    torch.cuda.synchronize()
+    for _ in range(100):
+        bf.attn()
+        torch.cuda.synchronize()
+    xs = []
+    for _ in range(iters):
+        t0 = time.perf_counter()
+        bf.attn()
+        torch.cuda.synchronize()
+        xs.append((time.perf_counter() - t0) * 1e6)
+    return _pct(xs)
+
+
+def copy_reference(w, steps):
+    """A plain device-to-device copy of the bytes pack moves (its kept rows read
+    and written once, T x 3C elements), timed like the kernels: the practical
+    floor of a copy of that size on this GPU, for reading pack's roofline
+    fraction.  Captured as 50 back-to-back copies in one graph."""
+    import torch
+
+    n = w.T * 3 * w.C * w.elem_bytes // 2
+    a = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    b = torch.empty_like(a)
+    a.view(torch.int16).random_()
+    us = graph_us(lambda: b.copy_(a), steps)
+    nbytes = 2 * n * 2
+    return {"bytes_read_plus_written": nbytes, "us": us, "achieved_GBs": nbytes / us * 1e-3,
+            "hbm_frac": nbytes / us * 1e-3 / HBM_PEAK_GBS}
+
+
 def tile_list_comparison(steps):
     """rag_attn (grid with one slot per (head, image[, query split])) against
     rag_attn_tiled (the device-built tile list) on the ragged and long-sequence
@@ -524,6 +638,9 @@ def main():
         "fused_tokens_per_s": w.T / st["fused_pass"] * 1e6,
         "dispatch_floor_us": floor,
     }
+    res["copy_reference"] = copy_reference(w, args.steps)
+    res["dispatch_floor_us"]["B1_L1"]["attn_roundtrip_python"] = python_binding_floor()
+    res["timing_distributions"] = timing_distributions(w)
     res["repack"] = measure_repack(args.steps)
     res["vit_block"] = measure_block(args.steps)
     res["deitb_shapes"] = other_shapes(args.steps)
