@@ -13,8 +13,8 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests are collected everywhere but only run where a GPU is present; the
-    # driver selects them with -m gpu on the GPU machine.
+    # GPU tests are collected everywhere but only run where a GPU is present
+    # (select them with -m gpu).
     try:
         import torch
         # device_count() does not initialise the HIP runtime
