@@ -68,6 +68,9 @@ def _bind(path: str):
     lib.oracle_attn.argtypes = [vp, vp, vp, i64, i64, i64, i32, vp, i32, i32, i32, dbl, vp,
                                 i64, vp, vp]
     lib.oracle_attn.restype = ctypes.c_int
+    lib.oracle_attn_rows.argtypes = [vp, vp, vp, i64, i64, i64, i32, vp, i32, i32, i32, dbl, vp,
+                                     i32, vp, i64, vp, vp]
+    lib.oracle_attn_rows.restype = ctypes.c_int
     lib.oracle_attn_padded.argtypes = [vp, vp, vp, i64, i64, i64, i32, vp, i32, i32, i32,
                                        i32, dbl, vp, i64, vp, vp]
     lib.oracle_attn_padded.restype = ctypes.c_int
@@ -197,6 +200,38 @@ def attn(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_seqlens: np.ndarray, H:
                              _ptr(r_buf))
     if rc != 0:
         raise ValueError("oracle_attn rejected its arguments")
+    return o
+
+
+def attn_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_seqlens: np.ndarray, H: int, d: int,
+              scale: float, rows) -> np.ndarray:
+    """attn() for the listed packed query rows only: fp64 [len(rows), H*d], row r
+    of the result being attn(...)[rows[r]] (the same arithmetic)."""
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    B = cu.shape[0] - 1
+    code = _dtype_code(q)
+    arrs = []
+    for a in (q, k, v):
+        if _dtype_code(a) != code:
+            raise TypeError("q, k, v dtypes differ")
+        a2 = a.reshape(a.shape[0], -1)
+        if a2.strides[1] != a2.itemsize:
+            a2 = np.ascontiguousarray(a2)
+        arrs.append(a2)
+    lens = np.diff(cu)
+    if (lens < 0).any() or cu[0] != 0:
+        raise ValueError("cu_seqlens must start at 0 and not decrease")
+    r = np.ascontiguousarray(rows, dtype=np.int64)
+    Lmax = int(lens.max()) if B else 0
+    o = np.zeros((r.shape[0], H * d), dtype=np.float64)
+    s_buf = np.zeros(max(Lmax, 1), dtype=np.float64)
+    r_buf = np.zeros(max(Lmax, 1), dtype=np.int64)
+    qs, ks, vs = (a.strides[0] // a.itemsize for a in arrs)
+    rc = _load().oracle_attn_rows(_ptr(arrs[0]), _ptr(arrs[1]), _ptr(arrs[2]), qs, ks, vs, code,
+                                  _ptr(cu), B, H, d, float(scale), _ptr(r), int(r.shape[0]), _ptr(o),
+                                  H * d, _ptr(s_buf), _ptr(r_buf))
+    if rc != 0:
+        raise ValueError("oracle_attn_rows rejected its arguments")
     return o
 
 

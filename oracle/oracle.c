@@ -223,6 +223,38 @@ int oracle_attn(const void* q, const void* k, const void* v, int64_t q_stride,
 }
 
 /*
+ * The ragged attention of selected query rows only (the same definition as
+ * oracle_attn, for the outputs of a batch too large to compute whole):
+ * rows[r] is a packed row index; its image b is the one with cu[b] <= row <
+ * cu[b+1] (cu non-decreasing).  o[r, h*d .. h*d+d-1] gets
+ * O[row, h].  Returns 0, or -1 on a bad argument (a row outside [0, cu[B])).
+ */
+int oracle_attn_rows(const void* q, const void* k, const void* v, int64_t q_stride,
+                     int64_t k_stride, int64_t v_stride, int32_t dtype, const int32_t* cu_seqlens,
+                     int32_t B, int32_t H, int32_t d, double scale, const int64_t* rows,
+                     int32_t nrows, double* o, int64_t o_stride, double* s_buf, int64_t* rows_buf)
+{
+    if (dtype != ORACLE_DTYPE_F32 && dtype != ORACLE_DTYPE_BF16)
+        return -1;
+    for (int32_t r = 0; r < nrows; ++r) {
+        const int64_t row = rows[r];
+        if (row < 0 || row >= cu_seqlens[B])
+            return -1;
+        int32_t b = 0;  /* the image holding the row */
+        while (!(cu_seqlens[b] <= row && row < cu_seqlens[b + 1]))
+            ++b;
+        const int64_t first = cu_seqlens[b];
+        const int32_t L = cu_seqlens[b + 1] - cu_seqlens[b];
+        for (int32_t j = 0; j < L; ++j)
+            rows_buf[j] = first + j;
+        for (int32_t h = 0; h < H; ++h)
+            attend_one_row(q, k, v, dtype, row, rows_buf, NULL, L, q_stride, k_stride, v_stride,
+                           h * d, d, scale, s_buf, o + (int64_t)r * o_stride + (int64_t)h * d);
+    }
+    return 0;
+}
+
+/*
  * Padded attention ([blog-problem]): every image keeps all N positions; key n of
  * image b takes part only if keep[b][n] != 0; every query position n (kept or
  * not) gets an output row.  Rows are b*N + n.  Kept query rows equal the

@@ -250,6 +250,30 @@ def test_attn_matches_torch_sdpa_fp64(dtype):
     assert np.abs(got - want).max() < 1e-12
 
 
+def test_attn_rows_match_torch_sdpa_on_sampled_rows():
+    """attn_rows (the sampled-row form used at sizes too large to compute whole)
+    against torch's fp64 SDPA on the rows it is asked for: first and last rows
+    of images, rows of images that follow empty ones, and random rows, in any
+    order and with repeats."""
+    rng = np.random.default_rng(19)
+    lengths = [5, 0, 0, 40, 1, 0, 17]
+    x, cu = _rand_case(rng, lengths, H=2, d=64, dtype="bf16")
+    want = _sdpa_ref(x[:, 0], x[:, 1], x[:, 2], cu, 2, 64, 0.3)
+    T = int(cu[-1])
+    rows = [0, 4, 5, 44, 45, 46, 62, T - 1] + rng.integers(0, T, size=12).tolist() + [5, 0]
+    got = oracle.attn_rows(x[:, 0], x[:, 1], x[:, 2], cu, H=2, d=64, scale=0.3, rows=rows)
+    assert got.shape == (len(rows), 128)
+    assert np.abs(got - want[rows]).max() < 1e-12
+
+
+def test_attn_rows_rejects_rows_outside_the_batch():
+    rng = np.random.default_rng(20)
+    x, cu = _rand_case(rng, [3, 2], H=1, d=64, dtype="f32")
+    for bad in ([5], [-1]):
+        with pytest.raises(ValueError):
+            oracle.attn_rows(x[:, 0], x[:, 1], x[:, 2], cu, H=1, d=64, scale=0.1, rows=bad)
+
+
 def test_attn_on_tiny_workload_matches_sdpa():
     w = wl.tiny()
     rows = wl.rows(w)

@@ -38,6 +38,10 @@ MUTANTS = {
     "repack_skips_image_start": ("for (int64_t t = cu_in[b]; t < cu_in[b + 1]; ++t) {",
                                  "for (int64_t t = cu_in[b] + 1; t < cu_in[b + 1]; ++t) {"),
     "repack_keep_is_one": ("            if (keep[t] != 0) {", "            if (keep[t] == 1) {"),
+    "rows_image_lookup_off_by_one": ("        while (!(cu_seqlens[b] <= row && row < cu_seqlens[b + 1]))",
+                                     "        while (!(cu_seqlens[b] <= row && row <= cu_seqlens[b + 1]))"),
+    "rows_keys_from_row_on": ("            rows_buf[j] = first + j;",
+                              "            rows_buf[j] = row + j;"),
 }
 
 PINS = [
@@ -56,6 +60,7 @@ PINS = [
     lambda: pins.test_repack_equals_pack_of_the_composed_mask(0, 0.5, 0.5),
     pins.test_repack_keep_all_is_identity_and_keep_none_is_empty,
     pins.test_repack_brute_force_per_image,
+    pins.test_attn_rows_match_torch_sdpa_on_sampled_rows,
 ]
 
 
