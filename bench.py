@@ -407,6 +407,17 @@ def stage_samples(bf, hot_samples=100, cold_samples=30, per_graph=20):
             ev[i][1].record()
         torch.cuda.synchronize()
         rec = {"hot_us": _pct([a.elapsed_time(b) * 1e3 / per_graph for a, b in ev[:hot_samples]])}
+        # one launch at a time, caches hot: the graph replay before it keeps the
+        # GPU busy while the events and the launch are enqueued
+        xs = []
+        for i in range(hot_samples):
+            g_many.replay()
+            ev[i][0].record()
+            fn()
+            ev[i][1].record()
+            torch.cuda.synchronize()
+            xs.append(ev[i][0].elapsed_time(ev[i][1]) * 1e3)
+        rec["hot_single_us"] = _pct(xs)
         for kind in ("write", "read"):
             xs = []
             for i in range(cold_samples):
