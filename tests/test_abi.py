@@ -39,6 +39,16 @@ def test_header_declares_the_boundary():
     assert sorted(binding.EXPORTS) == syms
 
 
+def test_binding_constants_match_the_header():
+    text = open(HEADER).read()
+    for name in ("RAG_STAGES_N", "RAG_FLOOR_N", "RAG_MAX_N", "RAG_MAX_B", "RAG_HEAD_DIM",
+                 "RAG_UNPACK_ZERO_DROPPED"):
+        m = re.search(r"#define\s+%s\s+(\S+)" % name, text)
+        assert m, name
+        if hasattr(binding, name):
+            assert int(m.group(1).rstrip("uU"), 0) == getattr(binding, name), name
+
+
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_symbols():
         assert hasattr(lib, name), name
