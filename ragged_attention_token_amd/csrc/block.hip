@@ -36,61 +36,85 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 using rag::dev::u32x4;
 
-constexpr int kLnMaxChunks = 4;  // 8-element chunks per lane: C <= 64 * 8 * 4 = 2048
+constexpr int kLnRowsPerWave = 2;
 
 // LayerNorm over rows of C bf16 values (C a multiple of 8, at most 2048):
 // y = (x - mean) / sqrt(var + eps) * gamma + beta, mean and (biased) variance
-// in fp32 over the row, y rounded to bf16.  One wave per row, 4 rows per
-// workgroup; a lane holds up to kLnMaxChunks 16-byte chunks of its row.
+// in fp32 over the row, y rounded to bf16.  Each wave normalises
+// kLnRowsPerWave rows, 4 waves per workgroup; a lane holds NCH 16-byte chunks
+// of each row (NCH = ceil(C / 512)), and every row's loads are issued before
+// the first reduction.
+template <int NCH>
 __global__ __launch_bounds__(256) void layernorm_kernel(const __bf16* x, __bf16* y, int rows, int C,
                                                         const float* gamma, const float* beta,
                                                         float eps)
 {
+    constexpr int R = kLnRowsPerWave;
     const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= rows) return;
+    const int row0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * R;
+    if (row0 >= rows) return;
     const int nchunk = C / 8;
-    const auto rx = rag::dev::make_rsrc(x + (int64_t)row * C, (uint32_t)C * 2u);
-    float v[kLnMaxChunks][8];
-    float sum = 0.f;
+    float v[R][NCH][8];
 #pragma unroll
-    for (int j = 0; j < kLnMaxChunks; ++j) {
-        const int ch = lane + 64 * j;
-        const bf16x8 w = __builtin_bit_cast(bf16x8, rag::dev::ld16(rx, 16u * (uint32_t)ch));
+    for (int r = 0; r < R; ++r) {
+        // rows past the end read zeros (and are not written)
+        const auto rx = rag::dev::make_rsrc(x + (int64_t)(row0 + r) * C,
+                                            row0 + r < rows ? (uint32_t)C * 2u : 0u);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            v[j][e] = ch < nchunk ? static_cast<float>(w[e]) : 0.f;
-            sum += v[j][e];
+        for (int j = 0; j < NCH; ++j) {
+            const int ch = lane + 64 * j;
+            const bf16x8 w = __builtin_bit_cast(bf16x8, rag::dev::ld16(rx, 16u * (uint32_t)ch));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[r][j][e] = ch < nchunk ? static_cast<float>(w[e]) : 0.f;
         }
     }
+    float mean[R], rstd[R];
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
-    const float mean = sum / (float)C;
-    float sq = 0.f;
+    for (int r = 0; r < R; ++r) {
+        float sum = 0.f;
 #pragma unroll
-    for (int j = 0; j < kLnMaxChunks; ++j) {
-        const bool in = lane + 64 * j < nchunk;
+        for (int j = 0; j < NCH; ++j)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float d = v[j][e] - mean;
-            sq += in ? d * d : 0.f;
-        }
+            for (int e = 0; e < 8; ++e) sum += v[r][j][e];
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+        mean[r] = sum / (float)C;
     }
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) sq += __shfl_xor(sq, off);
-    const float rstd = 1.f / sqrtf(sq / (float)C + eps);
-    const auto ry = rag::dev::make_rsrc(y + (int64_t)row * C, (uint32_t)C * 2u);
+    for (int r = 0; r < R; ++r) {
+        float sq = 0.f;
 #pragma unroll
-    for (int j = 0; j < kLnMaxChunks; ++j) {
+        for (int j = 0; j < NCH; ++j) {
+            const bool in = lane + 64 * j < nchunk;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float d = v[r][j][e] - mean[r];
+                sq += in ? d * d : 0.f;
+            }
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) sq += __shfl_xor(sq, off);
+        rstd[r] = 1.f / sqrtf(sq / (float)C + eps);
+    }
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
         const int ch = lane + 64 * j;
         if (ch >= nchunk) continue;
-        bf16x8 o;
+        const auto* g4 = reinterpret_cast<const f32x4*>(gamma + 8 * ch);
+        const auto* b4 = reinterpret_cast<const f32x4*>(beta + 8 * ch);
+        const f32x4 ga = g4[0], gb = g4[1], ba = b4[0], bb = b4[1];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int c = 8 * ch + e;
-            o[e] = static_cast<__bf16>((v[j][e] - mean) * rstd * gamma[c] + beta[c]);
+        for (int r = 0; r < R; ++r) {
+            if (row0 + r >= rows) continue;
+            bf16x8 o;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float gm = e < 4 ? ga[e] : gb[e - 4], bt = e < 4 ? ba[e] : bb[e - 4];
+                o[e] = static_cast<__bf16>((v[r][j][e] - mean[r]) * rstd[r] * gm + bt);
+            }
+            const auto ry = rag::dev::make_rsrc(y + (int64_t)(row0 + r) * C, (uint32_t)C * 2u);
+            rag::dev::st16(__builtin_bit_cast(u32x4, o), ry, 16u * (uint32_t)ch);
         }
-        rag::dev::st16(__builtin_bit_cast(u32x4, o), ry, 16u * (uint32_t)ch);
     }
 }
 
@@ -218,9 +242,18 @@ rag_status run_layernorm(const void* x, void* y, int rows, int C, const void* ga
                          hipStream_t st)
 {
     if (rows == 0) return RAG_OK;
-    hipLaunchKernelGGL(layernorm_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, static_cast<const __bf16*>(x),
-                       static_cast<__bf16*>(y), rows, C, static_cast<const float*>(gamma),
-                       static_cast<const float*>(beta), eps);
+    const int per_group = 4 * kLnRowsPerWave;
+    const dim3 grid((rows + per_group - 1) / per_group), block(256);
+    const auto* xb = static_cast<const __bf16*>(x);
+    auto* yb = static_cast<__bf16*>(y);
+    const auto* gm = static_cast<const float*>(gamma);
+    const auto* bt = static_cast<const float*>(beta);
+    if (C <= 512)
+        hipLaunchKernelGGL(layernorm_kernel<1>, grid, block, 0, st, xb, yb, rows, C, gm, bt, eps);
+    else if (C <= 1024)
+        hipLaunchKernelGGL(layernorm_kernel<2>, grid, block, 0, st, xb, yb, rows, C, gm, bt, eps);
+    else
+        hipLaunchKernelGGL(layernorm_kernel<4>, grid, block, 0, st, xb, yb, rows, C, gm, bt, eps);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? RAG_OK : set_error(RAG_ERR_HIP, "layernorm launch: %s", hipGetErrorString(e));
 }
