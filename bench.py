@@ -264,18 +264,18 @@ def measure_repack(steps):
             "timing": "%d launches captured in one graph, %d replays, HIP events" % (per_graph, reps)}
 
 
-def measure_block(steps):
-    """One DeiT-S encoder block (random weights, bf16) on the headline batch:
-    on the packed rows (T = B * 40, ragged attention) against the same block on
-    all B * N rows (padded attention with masked keys).  The analogue of the
-    pages' end-to-end comparison for one post-pruning block.  Device time per
-    forward from back-to-back calls between HIP events (host enqueue is faster
-    than the GPU work here)."""
+def measure_block(steps, w=None, label=None):
+    """One encoder block (random weights, bf16) on a pruned batch: on the packed
+    rows (ragged attention) against the same block on all B * N rows (padded
+    attention with masked keys).  The analogue of the pages' end-to-end
+    comparison for one post-pruning block.  Device time per forward from
+    back-to-back calls between HIP events (host enqueue is faster than the GPU
+    work here).  Default: DeiT-S at B = 256, 80% prune."""
     import torch
     from ragged_attention_token_amd import binding
     from ragged_attention_token_amd import workloads as wl
 
-    w = wl.deits(256, 800)
+    w = w or wl.deits(256, 800)
     C, H = w.C, w.H
     P = wl.vit_block_params(C, 4, 1)
     prm = {k: (torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).cuda() if k.startswith("w_")
@@ -308,11 +308,10 @@ def measure_block(steps):
     packed_us = timed(lambda: blk.forward(xp, y_p, T, cu, L))
     padded_us = timed(lambda: blk.forward_padded(x_all, y_pad, keep))
     blk.close()
-    return {"workload": "DeiT-S block (C=384, H=6, MLP 4x, random bf16 weights), B=256: "
-                        "%d packed rows (80%% prune) vs %d padded rows" % (T, rows),
-            "packed_block_us": packed_us, "padded_block_us": padded_us,
-            "speedup": padded_us / packed_us,
-            "packed_tokens_per_s": T / packed_us * 1e6}
+    label = label or ("DeiT-S block (C=384, H=6, MLP 4x, random bf16 weights), B=256: "
+                      "%d packed rows (80%% prune) vs %d padded rows" % (T, rows))
+    return {"workload": label, "packed_block_us": packed_us, "padded_block_us": padded_us,
+            "speedup": padded_us / packed_us, "packed_tokens_per_s": T / packed_us * 1e6}
 
 
 def sweep(steps):
@@ -654,6 +653,10 @@ def main():
     res["timing_distributions"] = timing_distributions(w)
     res["repack"] = measure_repack(args.steps)
     res["vit_block"] = measure_block(args.steps)
+    w384 = wl.deitb384(32)
+    res["vit_block_384"] = measure_block(
+        args.steps, w384, "DeiT-B block at 384x384 (N=577, C=768, H=12, MLP 4x, random bf16 "
+        "weights), B=32, keep 0.5 +- 0.1: %d packed rows vs %d padded rows" % (w384.T, w384.B * w384.N))
     res["deitb_shapes"] = other_shapes(args.steps)
     res["tile_list"] = tile_list_comparison(args.steps)
     if not args.no_sweep:
