@@ -62,7 +62,8 @@ typedef enum rag_status {
     RAG_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, stride too small, ... */
     RAG_ERR_UNSUPPORTED = 2, /* head_dim != 64, unknown dtype or flag, size over a limit */
     RAG_ERR_ALIGNMENT = 3,   /* pointer, stride or row size not a multiple of 16 bytes */
-    RAG_ERR_HIP = 4          /* the HIP runtime reported an error (text in rag_last_error) */
+    RAG_ERR_HIP = 4,         /* the HIP runtime reported an error (text in rag_last_error) */
+    RAG_ERR_NO_MEMORY = 5    /* a host-side allocation of the library failed */
 } rag_status;
 
 /* Element types. */

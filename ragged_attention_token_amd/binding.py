@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "librag.so")
 
 RAG_OK = 0
 STATUS = {0: "RAG_OK", 1: "RAG_ERR_INVALID_ARG", 2: "RAG_ERR_UNSUPPORTED", 3: "RAG_ERR_ALIGNMENT",
-          4: "RAG_ERR_HIP"}
+          4: "RAG_ERR_HIP", 5: "RAG_ERR_NO_MEMORY"}
 RAG_DTYPE_F32 = 0
 RAG_DTYPE_BF16 = 1
 RAG_UNPACK_ZERO_DROPPED = 1

@@ -221,7 +221,7 @@ rag_status get_plan(rag_block* blk, int kind, int M, GemmPlan** out)
         *out = &ins.first->second;
     } catch (...) {
         destroy_plan(g);
-        return set_error(RAG_ERR_INVALID_ARG, "out of host memory");
+        return set_error(RAG_ERR_NO_MEMORY, "out of host memory");
     }
     return RAG_OK;
 }
@@ -304,7 +304,7 @@ extern "C" RAG_API rag_status rag_block_create(const rag_block_desc* desc, rag_b
     rag_status s = rag::validate_block_desc(desc);
     if (s != RAG_OK) return s;
     rag_block* blk = new (std::nothrow) rag_block();
-    if (!blk) return set_error(RAG_ERR_INVALID_ARG, "out of host memory");
+    if (!blk) return set_error(RAG_ERR_NO_MEMORY, "out of host memory");
     blk->d = *desc;
     blk->C = desc->H * RAG_HEAD_DIM;
     blk->hidden = blk->C * desc->mlp_ratio;

@@ -208,7 +208,7 @@ extern "C" RAG_API rag_status rag_pipeline_create(const rag_pipeline_desc* desc,
     rag_status s = rag::validate_pipeline(desc);
     if (s != RAG_OK) return s;
     rag_pipeline* p = new (std::nothrow) rag_pipeline;
-    if (!p) return set_error(RAG_ERR_INVALID_ARG, "out of host memory");
+    if (!p) return set_error(RAG_ERR_NO_MEMORY, "out of host memory");
     p->d = *desc;
     hipStream_t cs = nullptr;
     s = hip_status((int)hipStreamCreateWithFlags(&cs, hipStreamNonBlocking), "capture stream");
@@ -284,8 +284,12 @@ template <typename F>
 rag_status time_calls(F launch, hipStream_t st, int warmup, int iters, double* rt, double* enq)
 {
     std::vector<double> a, b;
-    a.reserve(iters);
-    b.reserve(iters);
+    try {  // (no exception crosses the C ABI; push_back below never reallocates)
+        a.reserve(iters);
+        b.reserve(iters);
+    } catch (const std::bad_alloc&) {
+        return set_error(RAG_ERR_NO_MEMORY, "out of host memory");
+    }
     for (int i = 0; i < warmup + iters; ++i) {
         const Clock::time_point t0 = Clock::now();
         rag_status s = launch();

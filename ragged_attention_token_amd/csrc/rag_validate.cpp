@@ -285,6 +285,7 @@ extern "C" RAG_API const char* rag_status_string(rag_status s)
     case RAG_ERR_UNSUPPORTED: return "RAG_ERR_UNSUPPORTED";
     case RAG_ERR_ALIGNMENT: return "RAG_ERR_ALIGNMENT";
     case RAG_ERR_HIP: return "RAG_ERR_HIP";
+    case RAG_ERR_NO_MEMORY: return "RAG_ERR_NO_MEMORY";
     }
     return "RAG_ERR_UNKNOWN";
 }

@@ -54,6 +54,8 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, name), name
     assert lib.rag_version() >= 100
     assert lib.rag_status_string(3) == b"RAG_ERR_ALIGNMENT"
+    for code, name in binding.STATUS.items():
+        assert lib.rag_status_string(code) == name.encode()
 
 
 def pack(lib, keep=A, B=2, N=197, src=A, ss=2304, rb=2304, packed=A, ps=2304, cu=A, g=A, m=None):
