@@ -533,3 +533,35 @@ def test_repack_then_attention_and_unpack():
     torch.cuda.synchronize()
     got = out.cpu().numpy()
     assert (got[g2].view(np.uint8) == o.cpu().numpy()[:T2].view(np.uint8)).all()
+
+
+@pytest.mark.parametrize("max_seqlen,dtype", [(100, "bf16"), (300, "bf16"), (100, "f32")])
+def test_attention_on_separate_strided_buffers(max_seqlen, dtype):
+    """q, k, v and o as four separate allocations, each with its own padded row
+    stride (rows wider than H*64, o's row stride different again): the same
+    result as the fused packed view, bit for bit, and the oracle's values.
+    max_seqlen 100 takes the LDS-resident kernel for bf16, 300 the 64-key
+    tile kernel (fp32 input always does)."""
+    N = max_seqlen
+    w = wl.custom(B=3, N=N, H=2, lengths=[N, N // 3, 0], dtype=dtype, seed=41)
+    ref = _oracle_pack(w)
+    g = gpu_pack(w)
+    T, C = w.T, w.C
+    fused = gpu_attn(g["packed"], g["cu"], w, torch.float32, max_seqlen=max_seqlen)
+    pk = g["packed"][:T]
+    pads = {"q": 64, "k": 128, "v": 8}
+    bufs = {}
+    for i, name in enumerate(("q", "k", "v")):
+        wide = torch.zeros(T, C + pads[name], dtype=pk.dtype, device="cuda")
+        wide[:, :C] = pk[:, i * C:(i + 1) * C]
+        bufs[name] = wide[:, :C]
+    o_wide = sentinel_like((T, C + 24), torch.float32)
+    binding.rag_attn(bufs["q"], bufs["k"], bufs["v"], g["cu"], max_seqlen, o_wide[:, :C], H=w.H,
+                     scale=w.scale)
+    torch.cuda.synchronize()
+    got = o_wide[:, :C].cpu().numpy()
+    assert (got.view(np.uint32) == fused[:T].cpu().numpy().view(np.uint32)).all()
+    assert (as_numpy_rows(o_wide)[:, C:].view(np.uint8) == SENTINEL_BYTE).all(), "pad columns written"
+    for b, want in _oracle_attn_images(w, ref, range(w.B)).items():
+        s, e = int(ref[1][b]), int(ref[1][b + 1])
+        assert np.abs(got[s:e].astype(np.float64) - want).max() <= ATOL
