@@ -328,9 +328,11 @@ RAG_API void rag_pipeline_destroy(rag_pipeline* p);
  *   [18..20] rag_attn_padded on the desc's src/keep (output into dst): launch + sync
  *   [21..23] the pass as one rag_attn_gathered launch: launch + sync
  *   [24..26] rag_attn_gathered: host enqueue only
+ *   [27..29] an empty kernel taking one pointer argument: host enqueue only
+ *            (beside [3..5], the runtime's cost of passing kernel arguments)
  * `out_us` must hold RAG_FLOOR_N doubles.  Runs work on `stream`.
  */
-#define RAG_FLOOR_N 27
+#define RAG_FLOOR_N 30
 RAG_API rag_status rag_measure_dispatch(rag_pipeline* p, int32_t warmup, int32_t iters,
                                         double* out_us, void* stream);
 

@@ -24,7 +24,7 @@ RAG_DTYPE_F32 = 0
 RAG_DTYPE_BF16 = 1
 RAG_UNPACK_ZERO_DROPPED = 1
 RAG_HEAD_DIM = 64
-RAG_FLOOR_N = 27
+RAG_FLOOR_N = 30
 RAG_STAGES_N = 7
 
 #: Every symbol include/rag.h declares.
@@ -374,7 +374,7 @@ class Pipeline:
         _check(load().rag_measure_dispatch(self._h, int(warmup), int(iters), out, _stream(stream)))
         keys = ["empty_roundtrip", "empty_enqueue", "attn_roundtrip", "attn_enqueue",
                 "eager3_roundtrip", "graph_roundtrip", "padded_roundtrip", "fused_roundtrip",
-                "fused_enqueue"]
+                "fused_enqueue", "empty_arg_enqueue"]
         res = {}
         for i, k in enumerate(keys):
             res[k] = {"p10": out[3 * i], "p50": out[3 * i + 1], "p90": out[3 * i + 2]}

@@ -29,6 +29,7 @@ rag_status hip_status(int err, const char* what)
 }
 
 __global__ void empty_kernel() {}
+__global__ void empty_kernel_arg(const void*) {}
 
 }  // namespace
 
@@ -353,6 +354,12 @@ extern "C" RAG_API rag_status rag_measure_dispatch(rag_pipeline* p, int32_t warm
     if ((s = time_calls(graph, st, warmup, iters, out_us + 15, nullptr)) != RAG_OK) return s;
     if ((s = time_calls(padded, st, warmup, iters, out_us + 18, nullptr)) != RAG_OK) return s;
     if ((s = time_calls(fused, st, warmup, iters, out_us + 21, out_us + 24)) != RAG_OK) return s;
+    auto empty_arg = [&]() {
+        hipLaunchKernelGGL(empty_kernel_arg, dim3(1), dim3(64), 0, st, static_cast<const void*>(d.keep));
+        return hip_status((int)hipGetLastError(), "empty kernel with an argument");
+    };
+    double unused_rt[3];
+    if ((s = time_calls(empty_arg, st, warmup, iters, unused_rt, out_us + 27)) != RAG_OK) return s;
     return RAG_OK;
 }
 
