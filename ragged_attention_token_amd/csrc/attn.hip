@@ -294,14 +294,16 @@ __device__ __forceinline__ float online_inv(const Online& st)
 // The grid is an upper bound the host computes from B, H and max_seqlen;
 // workgroups past the items of their XCD return at once (they come last).
 // Limits (checked by the host): B <= 1024 (lane l holds the key-tile counts of
-// images 64 i + l, 4 bits each, i < 16) and max_seqlen <= 960 (nkt <= 15).
+// images 64 i + l, 4 bits each, i < 16), max_seqlen <= 960 (nkt <= 15) and
+// H <= 64 (every item index stays below 2^17, see udiv_small).
 struct Item {
     int b, h, q0, q1, L;  // query blocks [q0, q1)
     int64_t row0;
 };
 
-// a / d and a % d for 0 <= a < 2^24, 1 <= d < 2^24 (wave-uniform values): a
-// float reciprocal estimate, then one correction step each way.
+// a / d and a % d for 0 <= a < 2^20 and d >= 1 (wave-uniform values): the
+// float estimate a * rcp(d) is within a * 2^-22 < 1/4 of a / d, so after
+// truncation one correction step each way gives the exact quotient.
 __device__ __forceinline__ int udiv_small(int a, int d, int& rem)
 {
     int q = (int)((float)a * __builtin_amdgcn_rcpf((float)d));
@@ -397,9 +399,9 @@ __device__ __forceinline__ bool tile_item(const AttnParams& p, Item& it)
 template <bool WHOLE>
 __device__ __forceinline__ bool workgroup_item(const AttnParams& p, Item& it)
 {
-    __shared__ int s_item[7];
+    __shared__ int s_item[6];
     if (threadIdx.x < 64) {
-        Item w;
+        Item w{};
         const bool ok = tile_item<WHOLE>(p, w);
         if (threadIdx.x == 0) {
             s_item[0] = ok ? w.b : -1;
