@@ -202,6 +202,44 @@ def cpu_baseline(w, seconds):
             "host_cpu": _cpu_model(), "host_threads_available": len(os.sched_getaffinity(0))}
 
 
+def cpu_baseline_threads(w, seconds, threads):
+    """The same oracle passes on `threads` host threads at once: the batch is
+    split into contiguous image ranges and each thread runs the oracle's pack,
+    attention and unpack on its range (the oracle's C routines release the
+    interpreter lock, so the ranges run in parallel).  Images are independent
+    in every stage, so this is the whole workload's work, split by image."""
+    import oracle
+    from concurrent.futures import ThreadPoolExecutor
+    from ragged_attention_token_amd import workloads as wl
+
+    rows = wl.rows(w)
+    bounds = np.linspace(0, w.B, threads + 1).astype(int)
+    chunks = [(int(a), int(b)) for a, b in zip(bounds[:-1], bounds[1:]) if b > a]
+    dst0 = np.zeros((w.B * w.N, w.C), dtype=np.float64)
+
+    def one(ch):
+        b0, b1 = ch
+        packed, cu, gather = oracle.pack(w.keep[b0:b1], rows[b0 * w.N:b1 * w.N])
+        q, k, v = wl.split_qkv(packed, w.C)
+        o = oracle.attn(q, k, v, cu, w.H, w.d, w.scale)
+        oracle.unpack(o, cu, gather, dst0[b0 * w.N:b1 * w.N])
+        return int(cu[-1])
+
+    reps, t_total = 0, 0.0
+    with ThreadPoolExecutor(max_workers=len(chunks)) as ex:
+        while reps == 0 or (t_total < seconds and reps < 200):
+            t0 = time.perf_counter()
+            assert sum(ex.map(one, chunks)) == w.T
+            t_total += time.perf_counter() - t0
+            reps += 1
+    return {"value": w.T * reps / t_total, "unit": "packed tokens/s", "cores": len(chunks),
+            "kind": "oracle",
+            "sample": "whole workload (%s, T=%d), %d pass(es) of fp64 pack+attention+unpack in "
+                      "%.1f s, the images split over %d host threads" % (w.name, w.T, reps, t_total,
+                                                                        len(chunks)),
+            "seconds_per_pass": t_total / reps}
+
+
 def _cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -677,6 +715,9 @@ def main():
     if not args.no_cpu:
         print("timing the CPU oracle (<= %.0f s)" % args.cpu_seconds, file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        # the machine's CPU share for one GPU is 16 threads
+        nthr = max(1, min(16, len(os.sched_getaffinity(0))))
+        res["cpu_baseline_threads"] = cpu_baseline_threads(w, args.cpu_seconds / 2, nthr)
     print(json.dumps(res))
 
 
