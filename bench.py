@@ -354,7 +354,8 @@ def measure_block(steps, w=None, label=None):
 
 def sweep(steps):
     """Prune-rate sweep on the DeiT-S shape: per-launch device time of each kernel
-    and of a whole pass (three launches, and one graph launch)."""
+    and of a whole pass (three launches, and one graph launch), and the host
+    round trip (launch + synchronize) of each at that point."""
     import torch
     from ragged_attention_token_amd import workloads as wl
 
@@ -371,6 +372,11 @@ def sweep(steps):
                    "padded_attn_us": m["padded"], "pipeline_us": m["eager_pass"],
                    "graph_pipeline_us": m["graph_pass"], "fused_pass_us": m["fused_pass"]}
             rec["ragged_pipeline_vs_padded_attn"] = rec["padded_attn_us"] / rec["pipeline_us"]
+            # the point's dispatch-inclusive latency: host launch call(s) + stream
+            # synchronize, p50 over 200 round trips from C++
+            fl = bf.pipe.measure_dispatch(warmup=20, iters=200)
+            rec["roundtrip_us"] = {k: fl[k + "_roundtrip"]["p50"]
+                                   for k in ("attn", "eager3", "graph", "padded", "fused")}
             out["B%d_p%03d" % (B, p)] = rec
             print("sweep B=%d p=%03d: attn %.2f us, pipeline %.2f us" %
                   (B, p, rec["attn_us"], rec["pipeline_us"]), file=sys.stderr, flush=True)
