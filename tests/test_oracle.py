@@ -172,6 +172,23 @@ def test_attn_constant_v_and_identical_keys():
     assert np.abs(o2 - x[:, 2].astype(np.float64).mean(axis=0)).max() < 1e-12
 
 
+def test_attn_probability_rows_sum_to_one():
+    """With V the identity (one-hot rows, d >= L) the output row is the row of
+    attention weights itself: non-negative, summing to 1, zero past column L."""
+    rng = np.random.default_rng(11)
+    L, d = 6, 8
+    x, cu = _rand_case(rng, [L], H=1, d=d)
+    v = np.zeros((L, d), dtype=np.float32)
+    v[np.arange(L), np.arange(L)] = 1.0
+    p = oracle.attn(x[:, 0], x[:, 1], v, cu, H=1, d=d, scale=0.9)
+    assert (p >= 0).all()
+    assert np.abs(p[:, :L].sum(axis=1) - 1.0).max() < 1e-12
+    assert (p[:, L:] == 0).all()
+    # the largest weight of each row sits on its largest score
+    q, k = _decode(x[:, 0]), _decode(x[:, 1])
+    assert (p[:, :L].argmax(axis=1) == (q @ k.T).argmax(axis=1)).all()
+
+
 def test_attn_permutation_equivariant_within_image():
     rng = np.random.default_rng(6)
     x, cu = _rand_case(rng, [7, 5], H=2, d=8)
