@@ -132,7 +132,9 @@ def repack(keep_packed: np.ndarray, cu_in: np.ndarray, gather_in: np.ndarray,
         raise ValueError("cu_in must start at 0 and not decrease")
     keep = np.ascontiguousarray(keep_packed, dtype=np.uint8)
     g = np.ascontiguousarray(gather_in, dtype=np.int32)
-    src = np.ascontiguousarray(packed_rows).reshape(packed_rows.shape[0], -1)
+    src = np.ascontiguousarray(packed_rows)
+    # (an explicit row width: reshape cannot infer it from zero rows)
+    src = src.reshape(src.shape[0], int(np.prod(src.shape[1:], dtype=np.int64)))
     if keep.shape[0] < T or g.shape[0] < T or src.shape[0] < T:
         raise ValueError("keep / gather / rows shorter than cu_in[B]")
     row_bytes = src.shape[1] * src.itemsize

@@ -61,6 +61,16 @@ def _attn(packed, cu, w, out_dtype, bound, tiled=False):
 @pytest.mark.parametrize("seed", range(CASES))
 def test_random_case(seed):
     w, out_dtype, bound = _draw(seed)
+    _check_case(w, out_dtype, bound, seed)
+
+
+def test_every_image_empty():
+    """T = 0: nothing is packed, attended or written, through every entry point."""
+    w = wl.custom(B=5, N=65, H=2, lengths=[0] * 5, seed=77)
+    _check_case(w, torch.bfloat16, 1, 77)
+
+
+def _check_case(w, out_dtype, bound, seed):
     print("seed", seed, "B", w.B, "N", w.N, "H", w.H, "T", w.T, w.dtype, out_dtype, "bound", bound,
           flush=True)
     rows = wl.rows(w)

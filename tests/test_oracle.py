@@ -401,6 +401,9 @@ def test_repack_keep_all_is_identity_and_keep_none_is_empty():
     assert (cu2 == cu1).all() and (g2 == g1).all() and (p2 == p1).all()
     p3, cu3, g3 = oracle.repack(np.zeros(p1.shape[0], np.uint8), cu1, g1, p1)
     assert p3.shape[0] == 0 and (cu3 == 0).all() and g3.shape[0] == 0
+    # an empty packed batch (every image dropped) re-packs to an empty batch
+    p4, cu4, g4 = oracle.repack(np.zeros(0, np.uint8), cu3, g3, p3)
+    assert p4.shape == (0, p1.shape[1]) and (cu4 == 0).all() and g4.shape[0] == 0
 
 
 def test_repack_brute_force_per_image():
