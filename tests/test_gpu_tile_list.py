@@ -140,3 +140,50 @@ def test_tile_list_largest_batch():
     images = sorted(set(rng.choice(1024, size=12, replace=False).tolist())
                     | {0, 1023, int(np.argmax(w.lengths))})
     print("max abs err", _check_oracle(w, ref, o32, images), flush=True)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_tile_list_random_shapes(seed):
+    """Seeded random shapes inside the tile list's limits (B <= 1024, N <= 960,
+    H <= 12, B N <= 40000): the tiled launch equals the grid launch bit for bit,
+    rows past T and past the max_seqlen bound stay unwritten, and sampled images
+    (fp32 output) are within the bar of the oracle."""
+    rng = np.random.default_rng(50000 + seed)
+    N = int(rng.integers(1, 961))
+    B = int(rng.integers(1, min(1024, max(1, 40000 // N)) + 1))
+    H = int(rng.integers(1, 13))
+    kind = rng.integers(0, 4)
+    if kind == 0:
+        lengths = rng.integers(0, N + 1, size=B)
+    elif kind == 1:
+        lengths = np.full(B, int(rng.integers(0, N + 1)))
+    elif kind == 2:
+        lengths = rng.choice([0, 1, N], size=B)
+    else:
+        lengths = np.minimum(N, rng.geometric(0.02, size=B))
+    dtype = "f32" if rng.random() < 0.15 else "bf16"
+    w = wl.custom(B=B, N=N, H=H, lengths=lengths, dtype=dtype, seed=60000 + seed)
+    mx = int(w.lengths.max()) if w.T else 1
+    bound = mx if rng.random() < 0.8 else int(rng.integers(1, mx + 1))
+    od = torch.float32 if rng.random() < 0.5 else torch.bfloat16
+    print("seed", seed, "B", B, "N", N, "H", H, "T", w.T, dtype, od, "bound", bound, flush=True)
+    g = gpu_pack(w, want_max=False)
+    T = w.T
+    a = as_numpy_rows(gpu_attn(g["packed"], g["cu"], w, od, max_seqlen=bound))
+    b = as_numpy_rows(gpu_attn(g["packed"], g["cu"], w, od, max_seqlen=bound, tiled=True))
+    assert (a.view(np.uint8) == b.view(np.uint8)).all(), "tile list != grid"
+    assert (a[T:].view(np.uint8) == SENTINEL_BYTE).all(), "rows past T written"
+    if T == 0:
+        return
+    o32 = a if od == torch.float32 else as_numpy_rows(
+        gpu_attn(g["packed"], g["cu"], w, torch.float32, max_seqlen=bound, tiled=True))
+    packed_ref, cu_ref, _ = oracle.pack(w.keep, wl.rows(w))
+    for im in rng.choice(B, size=min(B, 4), replace=False):
+        s, e = int(cu_ref[im]), int(cu_ref[im + 1])
+        L = min(e - s, bound)
+        if L == 0:
+            continue
+        q, k, v = wl.split_qkv(packed_ref[s:s + L], w.C)
+        want = oracle.attn(q, k, v, np.array([0, L], np.int32), w.H, w.d, w.scale)
+        assert np.abs(o32[s:s + L].astype(np.float64) - want).max() <= ATOL, int(im)
+        assert (a[s + L:e].view(np.uint8) == SENTINEL_BYTE).all(), "rows past the bound written"
