@@ -883,9 +883,21 @@ __global__ __launch_bounds__(64 * kMaxWaves) void attn_lds_kernel(AttnParams p)
                 }
             }
         };
-        int kt = 0;
-        for (; kt + kBN <= L; kt += kBN) tile(std::true_type{}, kt);
-        if (kt < L) tile(std::false_type{}, kt);
+        if constexpr (MULTI) {
+            // long sequences: the full tiles unrolled (at most kLdsMaxRows / kBN
+            // of them), so that every LDS offset is an immediate and no address
+            // arithmetic runs per tile (fewer VALU instructions and registers;
+            // the short-sequence launches keep the loop's smaller code)
+#pragma unroll
+            for (int t = 0; t < kLdsMaxRows / kBN; ++t)
+                if ((t + 1) * kBN <= L) tile(std::true_type{}, t * kBN);
+            const int kt = L & ~(kBN - 1);  // the partial last tile, if any
+            if (kt < L) tile(std::false_type{}, kt);
+        } else {
+            int kt = 0;
+            for (; kt + kBN <= L; kt += kBN) tile(std::true_type{}, kt);
+            if (kt < L) tile(std::false_type{}, kt);
+        }
 
         // ---- epilogue: O = acc / l; lane holds O[16 qb + r16][16 db + 4g + i] ----
         const float inv = online_inv(st);
