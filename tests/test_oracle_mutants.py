@@ -53,6 +53,7 @@ PINS = [
     pins.test_attn_length_one_returns_v_row,
     pins.test_attn_zero_query_or_zero_scale_gives_mean_of_v,
     pins.test_attn_constant_v_and_identical_keys,
+    pins.test_attn_probability_rows_sum_to_one,
     pins.test_attn_bounded_by_v_and_no_leakage,
     lambda: pins.test_attn_brute_force_tiny([4, 1, 5], 2, 8),
     lambda: pins.test_attn_matches_torch_sdpa_fp64("bf16"),
