@@ -1,0 +1,90 @@
+"""The entry points run on the stream the caller gives them.
+
+On a side stream, a long matrix product is queued first and the input rows are
+written after it; pack, attention and unpack (and the pipeline's three-launch
+pass) are then enqueued on the same stream with no synchronisation in between.
+Work that ran on another stream would start before the rows exist and read
+uninitialised memory; on the caller's stream it waits for them, and the results
+match the oracle (pack bit for bit, attention within 2e-3)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import as_numpy_rows, sentinel_like, to_gpu_rows
+from ragged_attention_token_amd import binding
+from ragged_attention_token_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+ATOL = 2e-3
+
+
+def _delay(n=4096):
+    """About a millisecond of GPU work on the current stream."""
+    a = torch.ones(n, n, device="cuda", dtype=torch.float32)
+    for _ in range(4):
+        a = a @ a * (1.0 / n)
+    return a
+
+
+def _expected(w):
+    packed_ref, cu_ref, gather_ref = oracle.pack(w.keep, wl.rows(w))
+    q, k, v = wl.split_qkv(packed_ref, w.C)
+    return packed_ref, cu_ref, gather_ref, oracle.attn(q, k, v, cu_ref, w.H, w.d, w.scale)
+
+
+def test_entry_points_follow_the_callers_stream():
+    w = wl.custom(B=6, N=197, H=3, lengths=[40, 197, 0, 1, 77, 130], seed=61)
+    packed_ref, cu_ref, gather_ref, o_ref = _expected(w)
+    T, C = w.T, w.C
+    src_host = to_gpu_rows(w)
+    keep = torch.from_numpy(w.keep).cuda()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        src = torch.empty_like(src_host)
+        packed = sentinel_like((w.B * w.N, 3 * C), src.dtype)
+        cu = sentinel_like((w.B + 1,), torch.int32)
+        gather = sentinel_like((w.B * w.N,), torch.int32)
+        o = sentinel_like((w.B * w.N, C), torch.float32)
+        dst = torch.zeros(w.B * w.N, C, dtype=torch.float32, device="cuda")
+        _delay()
+        src.copy_(src_host)  # the rows exist only after the delay, on stream s
+        binding.rag_pack(keep, src, packed, cu, gather)
+        binding.rag_attn(packed[:, :C], packed[:, C:2 * C], packed[:, 2 * C:], cu, w.N, o, H=w.H,
+                         scale=w.scale)
+        binding.rag_unpack(o, cu, gather, dst, N=w.N)
+    s.synchronize()
+    assert (cu.cpu().numpy() == cu_ref).all()
+    assert (gather.cpu().numpy()[:T] == gather_ref).all()
+    assert (as_numpy_rows(packed)[:T].view(np.uint8) == packed_ref.view(np.uint8)).all()
+    got = dst.cpu().numpy().astype(np.float64)[gather_ref]
+    assert np.abs(got - o_ref).max() <= ATOL
+
+
+def test_pipeline_pass_follows_the_given_stream():
+    w = wl.deits(4, 800)
+    packed_ref, cu_ref, gather_ref, o_ref = _expected(w)
+    C = w.C
+    src_host = to_gpu_rows(w)
+    keep = torch.from_numpy(w.keep).cuda()
+    src = torch.empty_like(src_host)
+    packed = torch.empty(w.B * w.N, 3 * C, dtype=src.dtype, device="cuda")
+    cu = torch.zeros(w.B + 1, dtype=torch.int32, device="cuda")
+    gather = torch.zeros(w.B * w.N, dtype=torch.int32, device="cuda")
+    o = torch.empty(w.B * w.N, C, dtype=torch.float32, device="cuda")
+    dst = torch.zeros(w.B * w.N, C, dtype=torch.float32, device="cuda")
+    pipe = binding.Pipeline(keep, src, packed, cu, gather, o, dst, H=w.H, scale=w.scale,
+                            max_seqlen=int(w.lengths.max()))
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        _delay()
+        src.copy_(src_host)
+    pipe.launch_eager(stream=s)
+    s.synchronize()
+    assert (cu.cpu().numpy() == cu_ref).all()
+    got = dst.cpu().numpy().astype(np.float64)[gather_ref]
+    assert np.abs(got - o_ref).max() <= ATOL
+    pipe.close()
