@@ -1,4 +1,5 @@
-"""The entry points run on the stream the caller gives them.
+"""The entry points run on the stream the caller gives them, and can be captured
+in a graph.
 
 On a side stream, a long matrix product is queued first and the input rows are
 written after it; pack, attention and unpack (and the pipeline's three-launch
@@ -88,3 +89,51 @@ def test_pipeline_pass_follows_the_given_stream():
     got = dst.cpu().numpy().astype(np.float64)[gather_ref]
     assert np.abs(got - o_ref).max() <= ATOL
     pipe.close()
+
+
+def test_entry_points_captured_in_a_graph_replay_correctly():
+    """rag_pack, rag_attn and rag_unpack captured in one CUDA graph (as a caller
+    would, with torch.cuda.graph), replayed three times with new input rows and
+    a new keep mask copied in between, eager work and synchronisations between
+    the replays; every replay matches the oracle for its own inputs."""
+    B, N, H = 5, 197, 2
+    cases = [wl.custom(B=B, N=N, H=H, lengths=lens, seed=70 + i)
+             for i, lens in enumerate(([40, 0, 197, 3, 90], [197, 197, 1, 0, 64], [0, 0, 0, 5, 40]))]
+    C = cases[0].C
+    src = torch.empty_like(to_gpu_rows(cases[0]))
+    keep = torch.zeros(B, N, dtype=torch.uint8, device="cuda")
+    packed = torch.empty(B * N, 3 * C, dtype=src.dtype, device="cuda")
+    cu = torch.zeros(B + 1, dtype=torch.int32, device="cuda")
+    gather = torch.zeros(B * N, dtype=torch.int32, device="cuda")
+    o = torch.empty(B * N, C, dtype=torch.float32, device="cuda")
+    dst = torch.zeros(B * N, C, dtype=torch.float32, device="cuda")
+
+    def run():
+        binding.rag_pack(keep, src, packed, cu, gather)
+        binding.rag_attn(packed[:, :C], packed[:, C:2 * C], packed[:, 2 * C:], cu, N, o, H=H,
+                         scale=cases[0].scale)
+        binding.rag_unpack(o, cu, gather, dst, N=N)
+
+    src.copy_(to_gpu_rows(cases[0]))
+    keep.copy_(torch.from_numpy(cases[0].keep))
+    run()  # eager once before capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for w in cases:
+        src.copy_(to_gpu_rows(w))
+        keep.copy_(torch.from_numpy(w.keep))
+        dst.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        packed_ref, cu_ref, gather_ref, o_ref = _expected(w)
+        assert (cu.cpu().numpy() == cu_ref).all()
+        T = w.T
+        assert (gather.cpu().numpy()[:T] == gather_ref).all()
+        if T:
+            got = dst.cpu().numpy().astype(np.float64)[gather_ref]
+            assert np.abs(got - o_ref).max() <= ATOL
+        dropped = np.setdiff1d(np.arange(B * N), gather_ref)
+        assert (dst.cpu().numpy()[dropped] == 0).all()
