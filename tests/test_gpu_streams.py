@@ -137,3 +137,36 @@ def test_entry_points_captured_in_a_graph_replay_correctly():
             assert np.abs(got - o_ref).max() <= ATOL
         dropped = np.setdiff1d(np.arange(B * N), gather_ref)
         assert (dst.cpu().numpy()[dropped] == 0).all()
+
+
+def test_two_streams_at_once_share_nothing():
+    """Two different batches through pack, attention and unpack on two streams
+    with no ordering between them: each matches the oracle for its own batch
+    (the library keeps no state between calls)."""
+    ws = [wl.custom(B=7, N=197, H=3, lengths=[40, 197, 0, 1, 77, 130, 12], seed=81),
+          wl.custom(B=3, N=577, H=2, lengths=[577, 300, 2], seed=82)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for w in ws:
+        C = w.C
+        outs.append(dict(src=to_gpu_rows(w), keep=torch.from_numpy(w.keep).cuda(),
+                         packed=torch.empty(w.B * w.N, 3 * C, dtype=torch.bfloat16, device="cuda"),
+                         cu=torch.zeros(w.B + 1, dtype=torch.int32, device="cuda"),
+                         gather=torch.zeros(w.B * w.N, dtype=torch.int32, device="cuda"),
+                         o=torch.empty(w.B * w.N, C, dtype=torch.float32, device="cuda"),
+                         dst=torch.zeros(w.B * w.N, C, dtype=torch.float32, device="cuda")))
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for w, b, s in zip(ws, outs, streams):
+            C = w.C
+            with torch.cuda.stream(s):
+                binding.rag_pack(b["keep"], b["src"], b["packed"], b["cu"], b["gather"])
+                binding.rag_attn(b["packed"][:, :C], b["packed"][:, C:2 * C], b["packed"][:, 2 * C:],
+                                 b["cu"], w.N, b["o"], H=w.H, scale=w.scale)
+                binding.rag_unpack(b["o"], b["cu"], b["gather"], b["dst"], N=w.N)
+    torch.cuda.synchronize()
+    for w, b in zip(ws, outs):
+        packed_ref, cu_ref, gather_ref, o_ref = _expected(w)
+        assert (b["cu"].cpu().numpy() == cu_ref).all()
+        got = b["dst"].cpu().numpy().astype(np.float64)[gather_ref]
+        assert np.abs(got - o_ref).max() <= ATOL
