@@ -154,23 +154,61 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError("dtype must be float32 or bfloat16, got %s" % t.dtype)
 
 
-def _rows(t: torch.Tensor, name: str):
-    """(pointer, row stride in elements) of a tensor whose first axis is rows and
-    whose remaining axes are contiguous."""
-    _gpu(t, name)
-    if t.dim() < 2:
-        raise ValueError("%s must have a row axis and a column axis" % name)
-    inner = t[0] if t.shape[0] > 0 else t.new_empty(t.shape[1:])
-    if t.shape[0] > 0 and not inner.is_contiguous():
-        raise ValueError("%s: elements within a row must be contiguous" % name)
-    return t.data_ptr(), t.stride(0)
-
-
 def _row_bytes(t: torch.Tensor) -> int:
+    """Bytes of one row: the elements of every axis after the first."""
     n = 1
     for s in t.shape[1:]:
         n *= s
     return n * t.element_size()
+
+
+def _inner_contiguous(t: torch.Tensor) -> bool:
+    """Whether the axes after the first are laid out contiguously (read from the
+    strides, without building a view)."""
+    expect = 1
+    for size, stride in zip(reversed(t.shape[1:]), reversed(t.stride()[1:])):
+        if size != 1 and stride != expect:
+            return False
+        expect *= size
+    return True
+
+
+def _check_rows(t: torch.Tensor, name: str, min_row_bytes: int = 0) -> None:
+    """A tensor whose first axis is rows and whose remaining axes are contiguous,
+    each row holding at least `min_row_bytes` bytes.  The kernels read or write
+    that many bytes from the start of every row, and the C ABI sees only a
+    pointer and a stride, so the width is checked here: a narrower view (e.g.
+    the last columns of a wider buffer) would let the kernels touch the
+    neighbouring columns or run past the end of the allocation."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor on the GPU" % name)
+    if t.dim() < 2:
+        raise ValueError("%s must have a row axis and a column axis" % name)
+    if not _inner_contiguous(t):
+        raise ValueError("%s: elements within a row must be contiguous" % name)
+    if _row_bytes(t) < min_row_bytes:
+        raise ValueError("%s rows hold %d bytes; the call reads or writes %d bytes of each row"
+                         % (name, _row_bytes(t), min_row_bytes))
+
+
+def _rows(t: torch.Tensor, name: str, min_row_bytes: int = 0):
+    """(pointer, row stride in elements) of a row tensor on the GPU (checked as
+    in _check_rows)."""
+    _check_rows(t, name, min_row_bytes)
+    _gpu(t, name)
+    return t.data_ptr(), t.stride(0)
+
+
+def _qkvo(q, k, v, o, H, head_dim):
+    """Pointers and row strides of attention's q, k, v, o: each row must hold
+    the H * head_dim elements the kernels read (q, k, v) or write (o)."""
+    named = ((q, "q"), (k, "k"), (v, "v"), (o, "o"))
+    for t, name in named:  # every width before any device check
+        _check_rows(t, name, int(H) * int(head_dim) * getattr(t, "element_size", lambda: 0)())
+    out = []
+    for t, name in named:
+        out.extend(_rows(t, name))
+    return out
 
 
 def rag_pack(keep: torch.Tensor, src: torch.Tensor, packed: torch.Tensor, cu_seqlens: torch.Tensor,
@@ -178,12 +216,16 @@ def rag_pack(keep: torch.Tensor, src: torch.Tensor, packed: torch.Tensor, cu_seq
              row_bytes: Optional[int] = None, stream=None) -> None:
     """keep [B,N] uint8; src rows [B*N, ...]; packed rows [>= B*N, ...];
     cu_seqlens int32 [B+1]; gather_idx int32 [>= B*N]; max_seqlen_dev int32 [1]."""
-    _gpu(keep, "keep")
-    if keep.dtype != torch.uint8 or keep.dim() != 2 or not keep.is_contiguous():
+    if not isinstance(keep, torch.Tensor) or keep.dtype != torch.uint8 or keep.dim() != 2 \
+            or not keep.is_contiguous():
         raise ValueError("keep must be a contiguous uint8 [B, N] tensor")
     B, N = keep.shape
+    rb = _row_bytes(src) if row_bytes is None else int(row_bytes)
+    _check_rows(src, "src", rb)
+    _check_rows(packed, "packed", rb)
     sp, ss = _rows(src, "src")
     pp, ps = _rows(packed, "packed")
+    _gpu(keep, "keep")
     for t, name in ((cu_seqlens, "cu_seqlens"), (gather_idx, "gather_idx")):
         _gpu(t, name)
         if t.dtype != torch.int32:
@@ -191,7 +233,6 @@ def rag_pack(keep: torch.Tensor, src: torch.Tensor, packed: torch.Tensor, cu_seq
     if src.shape[0] < B * N or packed.shape[0] < B * N or gather_idx.numel() < B * N \
             or cu_seqlens.numel() < B + 1:
         raise ValueError("buffers smaller than the B*N capacity")
-    rb = _row_bytes(src) if row_bytes is None else int(row_bytes)
     mp = None
     if max_seqlen_dev is not None:
         _gpu(max_seqlen_dev, "max_seqlen_dev")
@@ -207,22 +248,25 @@ def rag_repack(keep_packed: torch.Tensor, cu_in: torch.Tensor, gather_in: torch.
     """A later pruning stage on packed rows: keep_packed uint8 [>= rows] (one
     byte per input row); cu_in int32 [B+1]; gather_in int32 [>= rows]; src /
     dst rows [rows, ...]; cu_out int32 [B+1]; gather_out int32 [>= rows]."""
-    _gpu(keep_packed, "keep_packed")
-    if keep_packed.dtype != torch.uint8 or not keep_packed.is_contiguous():
+    if not isinstance(keep_packed, torch.Tensor) or keep_packed.dtype != torch.uint8 \
+            or not keep_packed.is_contiguous():
         raise ValueError("keep_packed must be a contiguous uint8 tensor")
+    rb = _row_bytes(src) if row_bytes is None else int(row_bytes)
+    _check_rows(src, "src", rb)
+    _check_rows(dst, "dst", rb)
+    sp, ss = _rows(src, "src")
+    dp, ds = _rows(dst, "dst")
+    _gpu(keep_packed, "keep_packed")
     for t, name in ((cu_in, "cu_in"), (gather_in, "gather_in"), (cu_out, "cu_out"),
                     (gather_out, "gather_out")):
         _gpu(t, name)
         if t.dtype != torch.int32:
             raise TypeError("%s must be int32" % name)
     B = cu_in.numel() - 1
-    sp, ss = _rows(src, "src")
-    dp, ds = _rows(dst, "dst")
     rows = src.shape[0]
     if keep_packed.numel() < rows or gather_in.numel() < rows or dst.shape[0] < rows \
             or gather_out.numel() < rows or cu_out.numel() < B + 1:
         raise ValueError("buffers smaller than src's rows")
-    rb = _row_bytes(src) if row_bytes is None else int(row_bytes)
     _check(load().rag_repack(keep_packed.data_ptr(), cu_in.data_ptr(), gather_in.data_ptr(), B,
                              int(max_rows_in), rows, sp, ss * src.element_size(), rb, dp,
                              ds * dst.element_size(), cu_out.data_ptr(), gather_out.data_ptr(),
@@ -235,10 +279,7 @@ def rag_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torc
     """q, k, v, o: [rows, >= H*head_dim] (row stride free, rows contiguous inside);
     cu_seqlens int32 [B+1] on the GPU; max_seqlen a host upper bound.  tiled:
     call rag_attn_tiled (the same result over the device-built tile list)."""
-    qp, qs = _rows(q, "q")
-    kp, ks = _rows(k, "k")
-    vp, vs = _rows(v, "v")
-    op, os_ = _rows(o, "o")
+    qp, qs, kp, ks, vp, vs, op, os_ = _qkvo(q, k, v, o, H, head_dim)
     _gpu(cu_seqlens, "cu_seqlens")
     if cu_seqlens.dtype != torch.int32:
         raise TypeError("cu_seqlens must be int32")
@@ -264,6 +305,9 @@ def rag_unpack(packed: torch.Tensor, cu_seqlens: torch.Tensor, gather_idx: torch
                dst: torch.Tensor, N: int, flags: int = 0, row_bytes: Optional[int] = None,
                stream=None) -> None:
     """packed rows [>= B*N, ...] -> dst rows [B*N, ...]."""
+    rb = _row_bytes(dst) if row_bytes is None else int(row_bytes)
+    _check_rows(packed, "packed", rb)
+    _check_rows(dst, "dst", rb)
     pp, ps = _rows(packed, "packed")
     dp, ds = _rows(dst, "dst")
     for t, name in ((cu_seqlens, "cu_seqlens"), (gather_idx, "gather_idx")):
@@ -273,7 +317,6 @@ def rag_unpack(packed: torch.Tensor, cu_seqlens: torch.Tensor, gather_idx: torch
     B = cu_seqlens.numel() - 1
     if dst.shape[0] < B * N or packed.shape[0] < B * N or gather_idx.numel() < B * N:
         raise ValueError("buffers smaller than the B*N capacity")
-    rb = _row_bytes(dst) if row_bytes is None else int(row_bytes)
     _check(load().rag_unpack(pp, ps * packed.element_size(), rb, cu_seqlens.data_ptr(),
                              gather_idx.data_ptr(), B, int(N), dp, ds * dst.element_size(),
                              int(flags), _stream(stream)))
@@ -283,10 +326,7 @@ def rag_attn_padded(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, keep: tor
                     o: torch.Tensor, H: int, scale: float, head_dim: int = RAG_HEAD_DIM,
                     stream=None) -> None:
     """Padded comparator: q/k/v/o rows b*N + n of the [B, N] layout."""
-    qp, qs = _rows(q, "q")
-    kp, ks = _rows(k, "k")
-    vp, vs = _rows(v, "v")
-    op, os_ = _rows(o, "o")
+    qp, qs, kp, ks, vp, vs, op, os_ = _qkvo(q, k, v, o, H, head_dim)
     _gpu(keep, "keep")
     if keep.dtype != torch.uint8 or keep.dim() != 2 or not keep.is_contiguous():
         raise ValueError("keep must be a contiguous uint8 [B, N] tensor")
@@ -304,10 +344,7 @@ def rag_attn_gathered(keep: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: t
     """Pack + attend + unpack in one launch: q/k/v/o rows b*N + n of the [B, N]
     layout; attention over each image's kept rows, written to those rows of o.
     max_seqlen: host bound of the kept count per image (0 = N)."""
-    qp, qs = _rows(q, "q")
-    kp, ks = _rows(k, "k")
-    vp, vs = _rows(v, "v")
-    op, os_ = _rows(o, "o")
+    qp, qs, kp, ks, vp, vs, op, os_ = _qkvo(q, k, v, o, H, head_dim)
     _gpu(keep, "keep")
     if keep.dtype != torch.uint8 or keep.dim() != 2 or not keep.is_contiguous():
         raise ValueError("keep must be a contiguous uint8 [B, N] tensor")
@@ -330,9 +367,13 @@ class Pipeline:
     def __init__(self, keep, src, packed, cu_seqlens, gather_idx, o_packed, dst, H, scale,
                  max_seqlen: int = 0, max_seqlen_dev=None, unpack_flags: int = 0):
         B, N = keep.shape
-        for t, name in ((keep, "keep"), (src, "src"), (packed, "packed"),
-                        (cu_seqlens, "cu_seqlens"), (gather_idx, "gather_idx"),
-                        (o_packed, "o_packed"), (dst, "dst")):
+        C = int(H) * RAG_HEAD_DIM
+        # row widths the three kernels touch: fused q|k|v rows of src / packed,
+        # output rows of o_packed / dst
+        for t, name, elems in ((src, "src", 3 * C), (packed, "packed", 3 * C),
+                               (o_packed, "o_packed", C), (dst, "dst", C)):
+            _check_rows(t, name, elems * getattr(t, "element_size", lambda: 0)())
+        for t, name in ((keep, "keep"), (cu_seqlens, "cu_seqlens"), (gather_idx, "gather_idx")):
             _gpu(t, name)
         if src.dtype != packed.dtype or o_packed.dtype != dst.dtype:
             raise TypeError("src/packed and o_packed/dst must share dtypes")

@@ -202,6 +202,50 @@ def test_binding_refuses_cpu_tensors():
         binding.rag_pack(keep, keep, keep, keep, keep)
 
 
+def test_binding_rejects_rows_narrower_than_the_kernels_touch():
+    """The C ABI sees a pointer and a row stride only, so a view narrower than
+    the bytes a kernel reads or writes per row (e.g. the last columns of a
+    wider buffer) must be refused by the binding, before anything is launched.
+    CPU tensors suffice: the width is checked before the device is."""
+    import torch
+    H, C = 6, 384
+    bf = torch.bfloat16
+    wide = torch.zeros(8, 3 * C, dtype=bf)
+    q, k, v = wide[:, :C], wide[:, C:2 * C], wide[:, 2 * C:]
+    narrow = wide[:, 2 * C + 64:]            # C - 64 columns: 64 short of a head set
+    o = torch.zeros(8, C, dtype=torch.float32)
+    o_narrow = torch.zeros(8, 2 * C, dtype=torch.float32)[:, C + 8:]
+    cu = torch.zeros(3, dtype=torch.int32)
+    keep = torch.ones(2, 4, dtype=torch.uint8)
+    for call in (lambda: binding.rag_attn(q, k, v, cu, 4, o_narrow, H=H, scale=0.125),
+                 lambda: binding.rag_attn(narrow, k, v, cu, 4, o, H=H, scale=0.125),
+                 lambda: binding.rag_attn(q, narrow, v, cu, 4, o, H=H, scale=0.125, tiled=True),
+                 lambda: binding.rag_attn(q, k, narrow, cu, 4, o, H=H, scale=0.125),
+                 lambda: binding.rag_attn_padded(q, k, narrow, keep, o, H=H, scale=0.125),
+                 lambda: binding.rag_attn_gathered(keep, q, k, v, o_narrow, H=H, scale=0.125)):
+        with pytest.raises(ValueError, match="rows hold"):
+            call()
+    # pack / re-pack / unpack: the destination must hold the source's row bytes,
+    # and an explicit row_bytes must fit both
+    src = torch.zeros(8, 3 * C, dtype=bf)
+    g = torch.zeros(8, dtype=torch.int32)
+    with pytest.raises(ValueError, match="packed rows hold"):
+        binding.rag_pack(keep, src, src[:, 8:], cu, g)
+    with pytest.raises(ValueError, match="src rows hold"):
+        binding.rag_pack(keep, src, src.clone(), cu, g, row_bytes=3 * C * 2 + 16)
+    with pytest.raises(ValueError, match="dst rows hold"):
+        binding.rag_repack(keep.view(-1), cu, g, 4, src, src[:, 8:], cu, g)
+    with pytest.raises(ValueError, match="packed rows hold"):
+        binding.rag_unpack(o_narrow, cu, g, o, N=4)
+    # the pipeline: fused q|k|v rows for src and packed, H*64 for o_packed and dst
+    for args in ((src[:, 8:], src, o, o), (src, src, o, o_narrow), (src, src, o_narrow, o)):
+        with pytest.raises(ValueError, match="rows hold"):
+            binding.Pipeline(keep, args[0], args[1], cu, g, args[2], args[3], H=H, scale=0.125)
+    # full-width CPU tensors get past the width checks and are refused as not on the GPU
+    with pytest.raises(TypeError, match="on the GPU"):
+        binding.rag_attn(q, k, v, cu, 4, o, H=H, scale=0.125)
+
+
 def test_attn_gathered_rejects(lib):
     def call(keep=A, B=4, N=197, q=A, qs=1152, dt=BF16, H=6, hd=64, scale=0.125, o=A, os_=384,
              odt=F32, flags=0, max_seqlen=0):
