@@ -18,8 +18,15 @@ in the order it is defined:
     y   = x1 + m W2 + b2
 
 Everything is fp64; bf16 inputs (bit patterns as uint16) are decoded exactly.
-numpy's matmul serves as the matrix product.  GELU is given by name: "erf"
-(x * Phi(x)) or "tanh" (the tanh approximation of the same).
+numpy's matmul serves as the matrix product.  GELU is DeiT's: the exact form
+x * Phi(x) with Phi the standard normal CDF ("erf"); the tanh approximation of
+the same ("tanh") is kept only as a named alternative that the pins tell
+apart from it.
+
+The composition (pre-norm order, which tensor each residual adds to, the
+q | k | v column blocks and their head split) is pinned against torch's own
+fp64 nn.TransformerEncoderLayer(norm_first=True, activation="gelu") in the
+tests, an implementation this module shares nothing with.
 """
 from __future__ import annotations
 
@@ -69,7 +76,7 @@ def attention(qkv: np.ndarray, cu_seqlens: np.ndarray, H: int, d: int, scale: fl
 
 
 def block(x_bits: np.ndarray, params: dict, cu_seqlens: np.ndarray, H: int, scale: float,
-          eps: float = 1e-6, gelu_form: str = "tanh", d: int = 64) -> np.ndarray:
+          eps: float = 1e-6, gelu_form: str = "erf", d: int = 64) -> np.ndarray:
     """y = block(x) over packed rows.  x_bits: uint16 bf16 patterns [T, C];
     params: w_* as uint16 bf16 patterns [in, out], b_* / ln*_gamma / ln*_beta
     as float32.  Returns fp64 [T, C]."""
@@ -82,5 +89,6 @@ def block(x_bits: np.ndarray, params: dict, cu_seqlens: np.ndarray, H: int, scal
     qkv = h @ W["w_qkv"] + P["b_qkv"]
     a = attention(qkv, cu_seqlens, H, d, scale)
     x1 = x + a @ W["w_proj"] + P["b_proj"]
-    m = gelu(layernorm(x1, P["ln2_gamma"], P["ln2_beta"], eps) @ W["w_fc1"] + P["b_fc1"], gelu_form)
+    h2 = layernorm(x1, P["ln2_gamma"], P["ln2_beta"], eps)
+    m = gelu(h2 @ W["w_fc1"] + P["b_fc1"], gelu_form)
     return x1 + m @ W["w_fc2"] + P["b_fc2"]

@@ -552,6 +552,52 @@ def test_block_brute_force_tiny(form):
     assert np.abs(got - want).max() < 1e-11
 
 
+def test_block_matches_torch_transformer_encoder_layer_fp64():
+    """The block's composition against an implementation that shares nothing
+    with it: torch's nn.TransformerEncoderLayer in float64 on the CPU, built as
+    DeiT's pre-norm block (norm_first, exact GELU, LayerNorm eps 1e-6, MLP 4C,
+    no dropout) and given the same weights (torch's Linear stores [out, in]:
+    the transposes of the [in, out] matrices here; the attention's in-projection
+    rows are q | k | v, each split into heads of 64 columns).  Each image of the
+    packed batch is run through torch on its own, which is what the block's
+    attention over cu_seqlens means."""
+    import torch
+    H, d = 2, 64
+    C = H * d
+    P = wl.vit_block_params(C, 4, 21)
+    lengths = [5, 1, 9]
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    x = wl.hidden_rows(1, int(cu[-1]), C, 22)
+    got = vb.block(x, P, cu, H, 1.0 / math.sqrt(d))
+
+    layer = torch.nn.TransformerEncoderLayer(
+        d_model=C, nhead=H, dim_feedforward=4 * C, dropout=0.0, activation="gelu",
+        layer_norm_eps=1e-6, batch_first=True, norm_first=True, dtype=torch.float64)
+    f64 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64))  # noqa: E731
+    W = {k: vb.bf16_bits_to_f64(P[k]) for k in ("w_qkv", "w_proj", "w_fc1", "w_fc2")}
+    with torch.no_grad():
+        layer.self_attn.in_proj_weight.copy_(f64(W["w_qkv"].T))
+        layer.self_attn.in_proj_bias.copy_(f64(P["b_qkv"]))
+        layer.self_attn.out_proj.weight.copy_(f64(W["w_proj"].T))
+        layer.self_attn.out_proj.bias.copy_(f64(P["b_proj"]))
+        layer.linear1.weight.copy_(f64(W["w_fc1"].T))
+        layer.linear1.bias.copy_(f64(P["b_fc1"]))
+        layer.linear2.weight.copy_(f64(W["w_fc2"].T))
+        layer.linear2.bias.copy_(f64(P["b_fc2"]))
+        layer.norm1.weight.copy_(f64(P["ln1_gamma"]))
+        layer.norm1.bias.copy_(f64(P["ln1_beta"]))
+        layer.norm2.weight.copy_(f64(P["ln2_gamma"]))
+        layer.norm2.bias.copy_(f64(P["ln2_beta"]))
+        layer.eval()
+        xv = vb.bf16_bits_to_f64(x)
+        want = np.concatenate([layer(f64(xv[cu[b]:cu[b + 1]])[None])[0].numpy()
+                               for b in range(len(lengths))])
+    assert np.abs(got - want).max() < 1e-10, np.abs(got - want).max()
+    # the exact GELU is the one that matches: the tanh form lands visibly apart
+    other = vb.block(x, P, cu, H, 1.0 / math.sqrt(d), gelu_form="tanh")
+    assert np.abs(other - want).max() > 1e-6
+
+
 def test_block_images_are_independent():
     """Rows of one image do not move when another image's rows change."""
     C = 128

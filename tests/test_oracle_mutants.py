@@ -112,12 +112,17 @@ BLOCK_MUTANTS = {
                        "k = qkv[s:e, 2 * C + h * d:2 * C + (h + 1) * d]"),
     "transposed_proj": ("x1 = x + a @ W[\"w_proj\"] + P[\"b_proj\"]", "x1 = x + a @ W[\"w_proj\"].T + P[\"b_proj\"]"),
     "gelu_erf_scale": ("np.vectorize(math.erf)(x / math.sqrt(2.0))", "np.vectorize(math.erf)(x / 2.0)"),
+    "ln2_on_x": ("h2 = layernorm(x1, P[\"ln2_gamma\"]", "h2 = layernorm(x, P[\"ln2_gamma\"]"),
+    "second_residual_from_x": ("return x1 + m @ W[\"w_fc2\"] + P[\"b_fc2\"]",
+                               "return x + m @ W[\"w_fc2\"] + P[\"b_fc2\"]"),
+    "block_gelu_tanh": ("eps: float = 1e-6, gelu_form: str = \"erf\"", "eps: float = 1e-6, gelu_form: str = \"tanh\""),
 }
 BLOCK_PINS = [
     pins.test_layernorm_golden,
     pins.test_gelu_forms_against_the_normal_cdf_table,
     pins.test_block_attention_step_matches_the_c_oracle,
     pins.test_block_with_zero_weights_is_the_identity,
+    pins.test_block_matches_torch_transformer_encoder_layer_fp64,
     lambda: pins.test_block_brute_force_tiny("erf"),
     lambda: pins.test_block_brute_force_tiny("tanh"),
 ]
