@@ -49,6 +49,10 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--batch", type=int, default=256)
     ap.add_argument("--prune", type=int, default=800, help="prune rate in thousandths")
+    ap.add_argument("--workload", default="deits", choices=("deits", "deitb_ragged", "deitb384"),
+                    help="deits: DeiT-S at --batch/--prune (the headline); deitb_ragged: DeiT-B "
+                         "B=64 N=197 with lengths uniform in [20, 197]; deitb384: DeiT-B at 384x384 "
+                         "(N=577) B=32, keep 0.5 +- 0.1 (--kernels-only profiling of those shapes)")
     ap.add_argument("--graph", action="store_true", help="time steps as hipGraphLaunch")
     ap.add_argument("--kernels-only", action="store_true")
     ap.add_argument("--pmc-calib", action="store_true")
@@ -611,7 +615,16 @@ def main():
         return
     from ragged_attention_token_amd import workloads as wl
 
-    w = wl.deits(args.batch, args.prune)
+    if args.workload == "deitb_ragged":
+        w = wl.deitb_ragged(64)
+    elif args.workload == "deitb384":
+        w = wl.deitb384(32)
+    else:
+        w = wl.deits(args.batch, args.prune)
+    if args.workload != "deits" and not args.kernels_only:
+        print("--workload %s is a profiling mode: use it with --kernels-only" % args.workload,
+              file=sys.stderr)
+        sys.exit(2)
     bf = Bufs(w)
     print("workload %s B=%d N=%d H=%d T=%d" % (w.name, w.B, w.N, w.H, w.T), file=sys.stderr,
           flush=True)
