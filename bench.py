@@ -56,6 +56,9 @@ def parse_args():
     ap.add_argument("--graph", action="store_true", help="time steps as hipGraphLaunch")
     ap.add_argument("--kernels-only", action="store_true")
     ap.add_argument("--pmc-calib", action="store_true")
+    ap.add_argument("--block-only", action="store_true",
+                    help="only the encoder-block timings (DeiT-S B=256 80%% prune, DeiT-B 384x384), "
+                         "for profiling the block's kernels")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -320,8 +323,9 @@ def measure_block(steps, w=None, label=None):
     w = w or wl.deits(256, 800)
     C, H = w.C, w.H
     P = wl.vit_block_params(C, 4, 1)
-    prm = {k: (torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).cuda() if k.startswith("w_")
-               else torch.from_numpy(v).cuda()) for k, v in P.items()}
+    # matrices drawn [in, out], uploaded in the [out, in] layout the block takes
+    prm = {k: (torch.from_numpy(np.ascontiguousarray(v.T).view(np.int16)).view(torch.bfloat16).cuda()
+               if k.startswith("w_") else torch.from_numpy(v).cuda()) for k, v in P.items()}
     blk = binding.Block(prm, H=H, scale=w.scale)
     xb = wl.hidden_rows(w.B, w.N, C, 2)
     x_all = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).cuda()
@@ -612,6 +616,12 @@ def main():
         sys.exit(1)
     if args.pmc_calib:
         pmc_calib()
+        return
+    if args.block_only:
+        from ragged_attention_token_amd import workloads as wl
+        w384 = wl.deitb384(32)
+        print(json.dumps({"vit_block": measure_block(args.steps),
+                          "vit_block_384": measure_block(args.steps, w384, "DeiT-B block at 384x384")}))
         return
     from ragged_attention_token_amd import workloads as wl
 

@@ -358,18 +358,20 @@ RAG_API rag_status rag_measure_stages(rag_pipeline* p, int32_t iters, double* ou
  * run on the packed tokens; the pages fix the attention and the packing, not
  * the rest of the block.  rag_block runs DeiT's pre-norm encoder block with
  * the caller's (e.g. random) weights on [rows, C] bf16 token rows, C = H * 64:
- *     h = LN1(x); qkv = h Wqkv + bqkv; a = attention(qkv);
- *     x1 = x + a Wproj + bproj; m = GELU(LN2(x1) W1 + b1); y = x1 + m W2 + b2
- * with this library's attention (ragged over cu_seqlens, or the padded form
- * over keep) and LayerNorm, and hipBLASLt for the four matrix products (bf16
- * inputs, fp32 accumulation; bias, GELU and residual applied in its epilogue;
- * GELU is the library epilogue's).  Every intermediate is stored as bf16.
+ *     h = LN1(x); qkv = h Wqkv^T + bqkv; a = attention(qkv);
+ *     x1 = x + a Wproj^T + bproj; m = GELU(LN2(x1) W1^T + b1); y = x1 + m W2^T + b2
+ * with GELU the exact x * Phi(x) (Phi the standard normal CDF) and every step
+ * a kernel of this library: LayerNorm (biased variance, eps inside the root),
+ * the matrix products (bf16 inputs, fp32 accumulation, bias / GELU / residual
+ * applied before the one rounding to bf16), and the attention (ragged over
+ * cu_seqlens, or the padded form over keep).  Every intermediate is stored as
+ * bf16.
  *
- * Weights: bf16, row-major [in, out] (y = x W), 16-byte aligned; Wqkv's
- * output columns are q | k | v, each head-major (head h = columns h*64 ..).
- * Biases and LayerNorm gamma / beta: fp32.  workspace: device memory the
- * library GEMMs may use (caller-owned; 32 MiB is ample), may be NULL with 0
- * bytes.  The descriptor's pointers must stay valid while the block exists.
+ * Weights: bf16, row-major [out, in] -- the layout of a linear layer's weight
+ * (y = x W^T) -- 16-byte aligned; Wqkv's output rows are q | k | v, each
+ * head-major (head h = rows h*64 ..).  Biases and LayerNorm gamma / beta:
+ * fp32, 16-byte aligned.  The descriptor's pointers must stay valid while the
+ * block exists.
  */
 typedef struct rag_block_desc {
     int32_t H;          /* heads; C = H * 64, at most 2048 */
@@ -378,31 +380,32 @@ typedef struct rag_block_desc {
     float scale;        /* attention scale (e.g. 1/sqrt(64)), finite */
     const void* ln1_gamma;
     const void* ln1_beta;
-    const void* w_qkv;  /* [C, 3C] */
+    const void* w_qkv;  /* [3C, C] */
     const void* b_qkv;  /* [3C] */
     const void* w_proj; /* [C, C] */
     const void* b_proj; /* [C] */
     const void* ln2_gamma;
     const void* ln2_beta;
-    const void* w_fc1;  /* [C, mlp_ratio*C] */
+    const void* w_fc1;  /* [mlp_ratio*C, C] */
     const void* b_fc1;  /* [mlp_ratio*C] */
-    const void* w_fc2;  /* [mlp_ratio*C, C] */
+    const void* w_fc2;  /* [C, mlp_ratio*C] */
     const void* b_fc2;  /* [C] */
-    void* workspace;
-    size_t workspace_bytes;
 } rag_block_desc;
 
 typedef struct rag_block rag_block;
 
-/* Device scratch a forward pass over `rows` rows needs (0 for bad arguments). */
+/* Device scratch a forward pass over `rows` rows needs (0 for bad arguments):
+ * the bf16 intermediates, rows * (6C + mlp_ratio*C) * 2 bytes. */
 RAG_API size_t rag_block_scratch_bytes(int32_t rows, int32_t H, int32_t mlp_ratio);
-/* Allocates host-side state (the GEMM library handle); no device memory. */
+/* Checks the descriptor and keeps a copy; allocates only the small host-side
+ * object, no device memory. */
 RAG_API rag_status rag_block_create(const rag_block_desc* desc, rag_block** out);
 /* y = block(x) over `rows` packed rows (a host value: e.g. B times the kept
  * count of a fixed-rate pruning stage); attention over cu_seqlens (int32[B+1],
  * device) with max_seqlen as in rag_attn.  x, y: bf16 [rows, C] contiguous,
- * 16-byte aligned.  scratch: >= rag_block_scratch_bytes(rows, ...) bytes.  The
- * first call at a given `rows` also builds the GEMM plans (host work). */
+ * 16-byte aligned, not overlapping.  scratch: caller-owned device memory of
+ * >= rag_block_scratch_bytes(rows, ...) bytes, 16-byte aligned.  Seven kernel
+ * launches on `stream`; nothing is allocated or synchronised. */
 RAG_API rag_status rag_block_forward(rag_block* blk, const void* x, void* y, int32_t rows,
                                      const int32_t* cu_seqlens, int32_t B, int32_t max_seqlen,
                                      void* scratch, size_t scratch_bytes, void* stream);

@@ -72,7 +72,6 @@ class BlockDesc(ctypes.Structure):
         ("ln2_gamma", ctypes.c_void_p), ("ln2_beta", ctypes.c_void_p),
         ("w_fc1", ctypes.c_void_p), ("b_fc1", ctypes.c_void_p),
         ("w_fc2", ctypes.c_void_p), ("b_fc2", ctypes.c_void_p),
-        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
     ]
 
 
@@ -444,25 +443,31 @@ class Block:
     """One DeiT encoder block on packed (or padded) bf16 token rows; see
     rag_block_desc in include/rag.h.  `params` maps names to GPU tensors:
     ln1_gamma, ln1_beta, ln2_gamma, ln2_beta, b_qkv, b_proj, b_fc1, b_fc2
-    (fp32) and w_qkv [C, 3C], w_proj [C, C], w_fc1 [C, hidden], w_fc2
-    [hidden, C] (bf16, row-major [in, out]).  The tensors and the workspace
-    are kept alive here."""
+    (fp32) and w_qkv [3C, C], w_proj [C, C], w_fc1 [hidden, C], w_fc2
+    [C, hidden] (bf16, the [out, in] layout of a linear layer's weight).  The
+    tensors are kept alive here; their shapes are checked against H and
+    mlp_ratio, since the C ABI sees only pointers."""
 
     NAMES = ("ln1_gamma", "ln1_beta", "w_qkv", "b_qkv", "w_proj", "b_proj", "ln2_gamma",
              "ln2_beta", "w_fc1", "b_fc1", "w_fc2", "b_fc2")
 
-    def __init__(self, params: dict, H: int, scale: float, mlp_ratio: int = 4, eps: float = 1e-6,
-                 workspace_bytes: int = 32 << 20):
-        self.params = {k: _gpu(params[k], k).contiguous() for k in self.NAMES}
+    def __init__(self, params: dict, H: int, scale: float, mlp_ratio: int = 4, eps: float = 1e-6):
         self.H, self.mlp_ratio = int(H), int(mlp_ratio)
         self.C = self.H * RAG_HEAD_DIM
-        self.workspace = torch.empty(max(workspace_bytes, 16), dtype=torch.uint8, device="cuda")
+        C, hid = self.C, self.C * self.mlp_ratio
+        shapes = {"ln1_gamma": (C,), "ln1_beta": (C,), "ln2_gamma": (C,), "ln2_beta": (C,),
+                  "w_qkv": (3 * C, C), "b_qkv": (3 * C,), "w_proj": (C, C), "b_proj": (C,),
+                  "w_fc1": (hid, C), "b_fc1": (hid,), "w_fc2": (C, hid), "b_fc2": (C,)}
+        for k in self.NAMES:
+            t = params[k]
+            want = torch.bfloat16 if k.startswith("w_") else torch.float32
+            if not isinstance(t, torch.Tensor) or tuple(t.shape) != shapes[k] or t.dtype != want:
+                raise ValueError("%s must be a %s tensor of shape %s" % (k, want, shapes[k]))
+        self.params = {k: _gpu(params[k], k).contiguous() for k in self.NAMES}
         d = BlockDesc()
         d.H, d.mlp_ratio, d.eps, d.scale = self.H, self.mlp_ratio, float(eps), float(scale)
         for k in self.NAMES:
             setattr(d, k, self.params[k].data_ptr())
-        d.workspace = self.workspace.data_ptr()
-        d.workspace_bytes = int(workspace_bytes)
         self._desc = d
         handle = ctypes.c_void_p()
         _check(load().rag_block_create(ctypes.byref(d), ctypes.byref(handle)))

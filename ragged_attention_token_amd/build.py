@@ -75,9 +75,7 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp%d" % os.getpid()
     # --no-undefined: a kernel whose host stub clang failed to emit would
     # otherwise only surface when the library is loaded
-    cmd = [cc, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-Wl,--no-undefined", "-o", tmp] + objs + [
-        # the ViT block's plain matrix products
-        "-lhipblaslt"]
+    cmd = [cc, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-Wl,--no-undefined", "-o", tmp] + objs
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("link failed: %s\n%s" % (" ".join(cmd), res.stderr))

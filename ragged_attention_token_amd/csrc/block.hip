@@ -5,25 +5,22 @@
 // measures end-to-end throughput of pruned DeiT models whose blocks run on the
 // packed tokens; the pages fix the attention step (the ragged kernel) and the
 // packing, not the rest of the block.  The block here is the standard
-// pre-norm encoder block of DeiT (ViT) with random weights:
+// pre-norm encoder block of DeiT (ViT) with the caller's (e.g. random) weights:
 //     h  = LayerNorm1(x)
-//     qkv = h Wqkv + bqkv                  (columns q | k | v, head-major)
+//     qkv = h Wqkv^T + bqkv                (columns q | k | v, head-major)
 //     a  = attention(qkv)                  (ragged, or padded with masked keys)
-//     x1 = x + a Wproj + bproj
+//     x1 = x + a Wproj^T + bproj
 //     h2 = LayerNorm2(x1)
-//     m  = GELU(h2 W1 + b1)
-//     y  = x1 + m W2 + b2
-// Row-wise steps (LayerNorm) are HIP kernels here; the four matrix products
-// are plain library GEMMs (hipBLASLt, bf16 inputs, fp32 accumulation, bias /
-// GELU / residual in its epilogue); the attention is this library's kernel.
+//     m  = GELU(h2 W1^T + b1)              (the exact GELU, x * Phi(x))
+//     y  = x1 + m W2^T + b2
+// with weights in the [out, in] layout of a linear layer.  Every step is a
+// kernel of this library: the LayerNorm below, the GEMM of gemm.hip (bias,
+// GELU and residual fused into its epilogue) and the attention of attn.hip.
 // Every intermediate row is stored as bf16.
 #include <hip/hip_runtime.h>
-#include <hipblaslt/hipblaslt.h>
 
 #include <cstdint>
-#include <map>
 #include <new>
-#include <utility>
 
 #include "rag_device.h"
 #include "rag_internal.h"
@@ -118,124 +115,20 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const __bf16* x, __bf16*
     }
 }
 
-// One GEMM of the block: D[M, N] = act(X[M, K] W[K, N] + bias) + R (row-major
-// bf16 X, W, D, R; fp32 bias).  hipBLASLt is column-major, so the product is
-// run as D^T = W^T X^T: m = N, n = M, k = K with W, X, D as stored.
-struct GemmPlan {
-    hipblasLtMatmulDesc_t desc = nullptr;
-    hipblasLtMatrixLayout_t a = nullptr, b = nullptr, c = nullptr;
-    hipblasLtMatmulAlgo_t algo;
-    bool residual = false;
-};
-
-enum GemmKind { kQkv = 0, kProj = 1, kFc1 = 2, kFc2 = 3 };
-
 }  // namespace
 
 struct rag_block {
     rag_block_desc d;
     int32_t C = 0, hidden = 0;
-    hipblasLtHandle_t lt = nullptr;
-    std::map<std::pair<int, int>, GemmPlan> plans;  // (kind, rows)
 };
 
 namespace {
 
-void destroy_plan(GemmPlan& g)
+rag_status run_gemm(const void* X, const void* W, const void* bias, const void* R, void* D, int M, int N,
+                    int K, int epi, hipStream_t st)
 {
-    if (g.a) hipblasLtMatrixLayoutDestroy(g.a);
-    if (g.b) hipblasLtMatrixLayoutDestroy(g.b);
-    if (g.c) hipblasLtMatrixLayoutDestroy(g.c);
-    if (g.desc) hipblasLtMatmulDescDestroy(g.desc);
-    g = GemmPlan();
-}
-
-rag_status lt_status(hipblasStatus_t s, const char* what)
-{
-    if (s == HIPBLAS_STATUS_SUCCESS) return RAG_OK;
-    return set_error(RAG_ERR_HIP, "%s: hipBLASLt status %d", what, (int)s);
-}
-
-// The plan of GEMM `kind` at M rows, built on first use and kept.
-rag_status get_plan(rag_block* blk, int kind, int M, GemmPlan** out)
-{
-    auto it = blk->plans.find({kind, M});
-    if (it != blk->plans.end()) {
-        *out = &it->second;
-        return RAG_OK;
-    }
-    const int C = blk->C, Hd = blk->hidden;
-    int K = C, N = C;
-    const void* bias = nullptr;
-    hipblasLtEpilogue_t epi = HIPBLASLT_EPILOGUE_BIAS;
-    bool residual = false;
-    switch (kind) {
-    case kQkv: K = C; N = 3 * C; bias = blk->d.b_qkv; break;
-    case kProj: K = C; N = C; bias = blk->d.b_proj; residual = true; break;
-    case kFc1: K = C; N = Hd; bias = blk->d.b_fc1; epi = HIPBLASLT_EPILOGUE_GELU_BIAS; break;
-    default: K = Hd; N = C; bias = blk->d.b_fc2; residual = true; break;
-    }
-    GemmPlan g;
-    g.residual = residual;
-    rag_status s;
-    if ((s = lt_status(hipblasLtMatmulDescCreate(&g.desc, HIPBLAS_COMPUTE_32F, HIP_R_32F), "desc")) != RAG_OK)
-        return s;
-    const hipblasOperation_t op = HIPBLAS_OP_N;
-    const hipDataType bias_type = HIP_R_32F;
-    s = lt_status(hipblasLtMatmulDescSetAttribute(g.desc, HIPBLASLT_MATMUL_DESC_TRANSA, &op, sizeof op), "transa");
-    if (s == RAG_OK)
-        s = lt_status(hipblasLtMatmulDescSetAttribute(g.desc, HIPBLASLT_MATMUL_DESC_TRANSB, &op, sizeof op), "transb");
-    if (s == RAG_OK)
-        s = lt_status(hipblasLtMatmulDescSetAttribute(g.desc, HIPBLASLT_MATMUL_DESC_EPILOGUE, &epi, sizeof epi), "epilogue");
-    if (s == RAG_OK)
-        s = lt_status(hipblasLtMatmulDescSetAttribute(g.desc, HIPBLASLT_MATMUL_DESC_BIAS_POINTER, &bias, sizeof bias), "bias");
-    if (s == RAG_OK)
-        s = lt_status(hipblasLtMatmulDescSetAttribute(g.desc, HIPBLASLT_MATMUL_DESC_BIAS_DATA_TYPE, &bias_type,
-                                                      sizeof bias_type), "bias type");
-    if (s == RAG_OK) s = lt_status(hipblasLtMatrixLayoutCreate(&g.a, HIP_R_16BF, N, K, N), "layout W");
-    if (s == RAG_OK) s = lt_status(hipblasLtMatrixLayoutCreate(&g.b, HIP_R_16BF, K, M, K), "layout X");
-    if (s == RAG_OK) s = lt_status(hipblasLtMatrixLayoutCreate(&g.c, HIP_R_16BF, N, M, N), "layout D");
-    if (s == RAG_OK) {
-        hipblasLtMatmulPreference_t pref = nullptr;
-        s = lt_status(hipblasLtMatmulPreferenceCreate(&pref), "preference");
-        if (s == RAG_OK) {
-            const uint64_t ws = blk->d.workspace_bytes;
-            s = lt_status(hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &ws,
-                                                                sizeof ws), "workspace");
-            hipblasLtMatmulHeuristicResult_t res[1];
-            int found = 0;
-            if (s == RAG_OK)
-                s = lt_status(hipblasLtMatmulAlgoGetHeuristic(blk->lt, g.desc, g.a, g.b, g.c, g.c, pref, 1, res,
-                                                              &found), "heuristic");
-            if (s == RAG_OK && found < 1) s = set_error(RAG_ERR_UNSUPPORTED, "no GEMM algorithm for M=%d", M);
-            if (s == RAG_OK) g.algo = res[0].algo;
-            hipblasLtMatmulPreferenceDestroy(pref);
-        }
-    }
-    if (s != RAG_OK) {
-        destroy_plan(g);
-        return s;
-    }
-    try {
-        auto ins = blk->plans.emplace(std::make_pair(kind, M), g);
-        *out = &ins.first->second;
-    } catch (...) {
-        destroy_plan(g);
-        return set_error(RAG_ERR_NO_MEMORY, "out of host memory");
-    }
-    return RAG_OK;
-}
-
-rag_status run_gemm(rag_block* blk, int kind, int M, const void* W, const void* X, const void* R,
-                    void* D, hipStream_t st)
-{
-    GemmPlan* g = nullptr;
-    rag_status s = get_plan(blk, kind, M, &g);
-    if (s != RAG_OK) return s;
-    const float alpha = 1.f, beta = g->residual ? 1.f : 0.f;
-    return lt_status(hipblasLtMatmul(blk->lt, g->desc, &alpha, W, g->a, X, g->b, &beta, g->residual ? R : D,
-                                     g->c, D, g->c, &g->algo, blk->d.workspace, blk->d.workspace_bytes, st),
-                     "matmul");
+    const int e = rag::launch_gemm(X, W, static_cast<const float*>(bias), R, D, M, N, K, epi, st);
+    return e == (int)hipSuccess ? RAG_OK : set_error(RAG_ERR_HIP, "GEMM launch: %s", hipGetErrorString((hipError_t)e));
 }
 
 rag_status run_layernorm(const void* x, void* y, int rows, int C, const void* gamma, const void* beta, float eps,
@@ -277,15 +170,16 @@ rag_status forward(rag_block* blk, const void* x, void* y, int32_t rows, const i
     char* m = x1 + (size_t)rows * C * 2;
     const rag_block_desc& d = blk->d;
     rag_status s;
+    const int Hd = blk->hidden;
     if ((s = run_layernorm(x, h, rows, C, d.ln1_gamma, d.ln1_beta, d.eps, st)) != RAG_OK) return s;
-    if ((s = run_gemm(blk, kQkv, rows, d.w_qkv, h, nullptr, qkv, st)) != RAG_OK) return s;
+    if ((s = run_gemm(h, d.w_qkv, d.b_qkv, nullptr, qkv, rows, 3 * C, C, rag::kGemmBias, st)) != RAG_OK) return s;
     const int e = rag::launch_attn(qkv, qkv + C * 2, qkv + 2 * C * 2, 3 * C, 3 * C, 3 * C, RAG_DTYPE_BF16, cu, keep,
                                    B, N, max_seqlen, rows, d.H, d.scale, a, C, RAG_DTYPE_BF16, layout, 0u, st);
     if (e != (int)hipSuccess) return set_error(RAG_ERR_HIP, "block attention: %s", hipGetErrorString((hipError_t)e));
-    if ((s = run_gemm(blk, kProj, rows, d.w_proj, a, x, x1, st)) != RAG_OK) return s;
+    if ((s = run_gemm(a, d.w_proj, d.b_proj, x, x1, rows, C, C, rag::kGemmResidual, st)) != RAG_OK) return s;
     if ((s = run_layernorm(x1, h, rows, C, d.ln2_gamma, d.ln2_beta, d.eps, st)) != RAG_OK) return s;
-    if ((s = run_gemm(blk, kFc1, rows, d.w_fc1, h, nullptr, m, st)) != RAG_OK) return s;
-    return run_gemm(blk, kFc2, rows, d.w_fc2, m, x1, y, st);
+    if ((s = run_gemm(h, d.w_fc1, d.b_fc1, nullptr, m, rows, Hd, C, rag::kGemmGelu, st)) != RAG_OK) return s;
+    return run_gemm(m, d.w_fc2, d.b_fc2, x1, y, rows, C, Hd, rag::kGemmResidual, st);
 }
 
 }  // namespace
@@ -308,11 +202,6 @@ extern "C" RAG_API rag_status rag_block_create(const rag_block_desc* desc, rag_b
     blk->d = *desc;
     blk->C = desc->H * RAG_HEAD_DIM;
     blk->hidden = blk->C * desc->mlp_ratio;
-    s = lt_status(hipblasLtCreate(&blk->lt), "hipblasLtCreate");
-    if (s != RAG_OK) {
-        delete blk;
-        return s;
-    }
     *out = blk;
     return RAG_OK;
 }
@@ -353,8 +242,5 @@ extern "C" RAG_API rag_status rag_block_forward_padded(rag_block* blk, const voi
 
 extern "C" RAG_API void rag_block_destroy(rag_block* blk)
 {
-    if (!blk) return;
-    for (auto& kv : blk->plans) destroy_plan(kv.second);
-    if (blk->lt) hipblasLtDestroy(blk->lt);
     delete blk;
 }

@@ -88,4 +88,11 @@ int launch_attn(const void* q, const void* k, const void* v, int64_t q_row_strid
                 int64_t o_row_stride, int32_t out_dtype, int layout, uint32_t flags,
                 void* stream);
 
+// ---- the encoder block's matrix products (gemm.hip) ----
+// D[M, N] = epi(X[M, K] W[N, K]^T + bias) (+ R): X, W, R, D bf16 row-major,
+// bias fp32; K a multiple of 64, N a multiple of 64; 16-byte aligned bases.
+enum { kGemmBias = 0, kGemmResidual = 1, kGemmGelu = 2 };
+int launch_gemm(const void* x, const void* w, const float* bias, const void* r, void* d, int32_t M,
+                int32_t N, int32_t K, int epi, void* stream);
+
 }  // namespace rag

@@ -309,10 +309,6 @@ rag_status validate_block_desc(const rag_block_desc* d)
         if (!ptrs[i]) return set_error(RAG_ERR_INVALID_ARG, "%s is NULL", names[i]);
         if (!aligned16(ptrs[i])) return set_error(RAG_ERR_ALIGNMENT, "%s must be 16-byte aligned", names[i]);
     }
-    if (d->workspace_bytes && !d->workspace)
-        return set_error(RAG_ERR_INVALID_ARG, "workspace is NULL but workspace_bytes > 0");
-    if (d->workspace && !aligned16(d->workspace))
-        return set_error(RAG_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
     return RAG_OK;
 }
 

@@ -267,7 +267,6 @@ def _block_desc(**kw):
     d.H, d.mlp_ratio, d.eps, d.scale = 6, 4, 1e-6, 0.125
     for i, name in enumerate(binding.Block.NAMES):
         setattr(d, name, A + 0x1000 * i)
-    d.workspace, d.workspace_bytes = A + 0x100000, 1 << 20
     for k, v in kw.items():
         setattr(d, k, v)
     return d
@@ -281,7 +280,7 @@ def _block_desc(**kw):
     (dict(scale=float("inf")), INVALID, "scale"),
     (dict(w_qkv=None), INVALID, "w_qkv"),
     (dict(b_fc2=A + 4), ALIGN, "b_fc2"),
-    (dict(workspace=None), INVALID, "workspace"),
+    (dict(w_fc1=A + 8), ALIGN, "w_fc1"),
 ])
 def test_block_create_rejects(lib, kwargs, status, needle):
     h = ctypes.c_void_p()
