@@ -409,6 +409,25 @@ RAG_API rag_status rag_block_create(const rag_block_desc* desc, rag_block** out)
 RAG_API rag_status rag_block_forward(rag_block* blk, const void* x, void* y, int32_t rows,
                                      const int32_t* cu_seqlens, int32_t B, int32_t max_seqlen,
                                      void* scratch, size_t scratch_bytes, void* stream);
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * forward as rag_block_forward, with the intermediates in a static device
+ * array of the library instead of a caller-provided scratch buffer.
+ *   - Limit: rows * (6C + mlp_ratio*C) * 2 bytes must fit its 128 MiB
+ *     (e.g. 17476 rows of DeiT-S, C = 384; 8738 rows of DeiT-B, C = 768);
+ *     larger calls return RAG_ERR_UNSUPPORTED and enqueue nothing.
+ *   - Nothing is allocated or freed by this call (no hipMalloc / hipFree, no
+ *     allocating library routine).  Each GPU the library runs on holds one
+ *     copy of the array until the process ends; its device address is looked
+ *     up once per device (rag_block_create does it for the current device).
+ *   - Every static call on one GPU shares that GPU's array: calls that overlap
+ *     on one GPU (two streams, two threads) race and give wrong results;
+ *     serialise them.  Nothing in the array must start at zero: each forward
+ *     writes every intermediate before reading it.
+ * Arguments, result and other errors as rag_block_forward. */
+RAG_API rag_status rag_block_forward_static(rag_block* blk, const void* x, void* y, int32_t rows,
+                                            const int32_t* cu_seqlens, int32_t B, int32_t max_seqlen,
+                                            void* stream);
 /* The same block on all B*N rows of the [B, N] layout with the padded
  * attention (keys with keep == 0 masked): the comparator of the packed pass. */
 RAG_API rag_status rag_block_forward_padded(rag_block* blk, const void* x, void* y,

@@ -33,7 +33,7 @@ EXPORTS = ("rag_pack", "rag_repack", "rag_attn", "rag_attn_tiled", "rag_unpack",
            "rag_pipeline_launch_fused", "rag_pipeline_destroy",
            "rag_measure_dispatch", "rag_measure_stages", "rag_last_error", "rag_status_string",
            "rag_version", "rag_block_scratch_bytes", "rag_block_create", "rag_block_forward",
-           "rag_block_forward_padded", "rag_block_destroy")
+           "rag_block_forward_padded", "rag_block_forward_static", "rag_block_destroy")
 
 _lib = None
 
@@ -109,6 +109,7 @@ def load(path: str = LIB_PATH):
     lib.rag_block_create.argtypes = [ctypes.POINTER(BlockDesc), ctypes.POINTER(vp)]
     lib.rag_block_forward.argtypes = [vp, vp, vp, i32, vp, i32, i32, vp, ctypes.c_size_t, vp]
     lib.rag_block_forward_padded.argtypes = [vp, vp, vp, vp, i32, i32, vp, ctypes.c_size_t, vp]
+    lib.rag_block_forward_static.argtypes = [vp, vp, vp, i32, vp, i32, i32, vp]
     lib.rag_block_destroy.argtypes = [vp]
     lib.rag_block_destroy.restype = None
     lib.rag_last_error.restype = ctypes.c_char_p
@@ -118,7 +119,8 @@ def load(path: str = LIB_PATH):
     for name in ("rag_pack", "rag_repack", "rag_attn", "rag_attn_tiled", "rag_unpack", "rag_attn_padded", "rag_attn_gathered",
                  "rag_pipeline_create", "rag_pipeline_launch", "rag_pipeline_launch_eager",
                  "rag_pipeline_launch_fused", "rag_measure_dispatch", "rag_measure_stages",
-                 "rag_block_create", "rag_block_forward", "rag_block_forward_padded"):
+                 "rag_block_create", "rag_block_forward", "rag_block_forward_padded",
+                 "rag_block_forward_static"):
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -497,6 +499,16 @@ class Block:
                                         cu_seqlens.data_ptr(), cu_seqlens.numel() - 1,
                                         int(max_seqlen), sc.data_ptr(), sc.numel(),
                                         _stream(stream)))
+
+    def forward_static(self, x: torch.Tensor, y: torch.Tensor, rows: int, cu_seqlens: torch.Tensor,
+                       max_seqlen: int, stream=None) -> None:
+        """forward() with the intermediates in the library's static device
+        array: the call allocates nothing (see rag_block_forward_static)."""
+        self._rows(x, y, rows)
+        _gpu(cu_seqlens, "cu_seqlens")
+        _check(load().rag_block_forward_static(self._h, x.data_ptr(), y.data_ptr(), int(rows),
+                                               cu_seqlens.data_ptr(), cu_seqlens.numel() - 1,
+                                               int(max_seqlen), _stream(stream)))
 
     def forward_padded(self, x: torch.Tensor, y: torch.Tensor, keep: torch.Tensor,
                        stream=None) -> None:

@@ -19,6 +19,7 @@
 // Every intermediate row is stored as bf16.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 #include <new>
 
@@ -159,10 +160,10 @@ size_t scratch_bytes(int64_t rows, int64_t C, int64_t hidden)
 }
 
 rag_status forward(rag_block* blk, const void* x, void* y, int32_t rows, const int32_t* cu, const uint8_t* keep,
-                   int32_t B, int32_t N, int32_t max_seqlen, void* scratch, int layout, hipStream_t st)
+                   int32_t B, int32_t N, int32_t max_seqlen, void* work, int layout, hipStream_t st)
 {
     const int C = blk->C;
-    char* base = static_cast<char*>(scratch);
+    char* base = static_cast<char*>(work);
     char* h = base;
     char* qkv = h + (size_t)rows * C * 2;
     char* a = qkv + (size_t)rows * 3 * C * 2;
@@ -191,6 +192,45 @@ extern "C" RAG_API size_t rag_block_scratch_bytes(int32_t rows, int32_t H, int32
     return scratch_bytes(rows, C, C * mlp_ratio);
 }
 
+namespace {
+
+// ---- the allocation-free forward (rag_block_forward_static) --------------
+//
+// Its intermediates live in this file-scope device array instead of a
+// caller-provided buffer: each GPU the library runs on holds one copy for the
+// life of the process, and every static call on that GPU shares it.  In host
+// code `scratch` names a host-side stand-in, never the device memory: the
+// device address is looked up once per device with hipGetSymbolAddress (with
+// that device current) and only that address is handed to the kernels.
+constexpr size_t kStaticScratchBytes = (size_t)128 << 20;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_dev[kMaxDevices];
+
+// The device address of `scratch` on the current device (looked up on the
+// first use on that device and kept).  Returns RAG_OK and sets *ptr, or an
+// error status.
+rag_status static_scratch(void** ptr)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return set_error(RAG_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return set_error(RAG_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+    void* p = g_scratch_dev[dev].load(std::memory_order_acquire);
+    if (!p) {
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return set_error(RAG_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        g_scratch_dev[dev].store(p, std::memory_order_release);  // the same value from any racing thread
+    }
+    *ptr = p;
+    return RAG_OK;
+}
+
+}  // namespace
+
 extern "C" RAG_API rag_status rag_block_create(const rag_block_desc* desc, rag_block** out)
 {
     if (!out) return set_error(RAG_ERR_INVALID_ARG, "out is NULL");
@@ -202,16 +242,24 @@ extern "C" RAG_API rag_status rag_block_create(const rag_block_desc* desc, rag_b
     blk->d = *desc;
     blk->C = desc->H * RAG_HEAD_DIM;
     blk->hidden = blk->C * desc->mlp_ratio;
+    // set-up of the allocation-free forward on the current device (a call on
+    // another device looks its own copy up on first use)
+    void* unused = nullptr;
+    s = static_scratch(&unused);
+    if (s != RAG_OK) {
+        delete blk;
+        return s;
+    }
     *out = blk;
     return RAG_OK;
 }
 
 extern "C" RAG_API rag_status rag_block_forward(rag_block* blk, const void* x, void* y, int32_t rows,
                                                 const int32_t* cu_seqlens, int32_t B, int32_t max_seqlen,
-                                                void* scratch, size_t scratch_bytes_given, void* stream)
+                                                void* work, size_t work_bytes, void* stream)
 {
     if (!blk) return set_error(RAG_ERR_INVALID_ARG, "block is NULL");
-    rag_status s = rag::validate_block_call(x, y, rows, blk->C, scratch, scratch_bytes_given,
+    rag_status s = rag::validate_block_call(x, y, rows, blk->C, work, work_bytes,
                                             scratch_bytes(rows, blk->C, blk->hidden));
     if (s != RAG_OK) return s;
     if (!cu_seqlens) return set_error(RAG_ERR_INVALID_ARG, "cu_seqlens is NULL");
@@ -219,24 +267,42 @@ extern "C" RAG_API rag_status rag_block_forward(rag_block* blk, const void* x, v
     if (max_seqlen < 1 || max_seqlen > 65535 * 64)
         return set_error(RAG_ERR_INVALID_ARG, "max_seqlen=%d out of range", max_seqlen);
     if (rows == 0) return RAG_OK;
-    return forward(blk, x, y, rows, cu_seqlens, nullptr, B, 0, max_seqlen, scratch, rag::kLayoutRagged,
+    return forward(blk, x, y, rows, cu_seqlens, nullptr, B, 0, max_seqlen, work, rag::kLayoutRagged,
                    static_cast<hipStream_t>(stream));
+}
+
+extern "C" RAG_API rag_status rag_block_forward_static(rag_block* blk, const void* x, void* y, int32_t rows,
+                                                       const int32_t* cu_seqlens, int32_t B, int32_t max_seqlen,
+                                                       void* stream)
+{
+    if (!blk) return set_error(RAG_ERR_INVALID_ARG, "block is NULL");
+    if (rows < 0) return set_error(RAG_ERR_INVALID_ARG, "rows=%d must be >= 0", rows);
+    const size_t need = scratch_bytes(rows, blk->C, blk->hidden);
+    if (need > kStaticScratchBytes)
+        return set_error(RAG_ERR_UNSUPPORTED,
+                         "rows=%d needs %zu bytes of intermediates; the static scratch holds %zu "
+                         "(at most %zu rows at C=%d)",
+                         rows, need, kStaticScratchBytes,
+                         kStaticScratchBytes / scratch_bytes(1, blk->C, blk->hidden), blk->C);
+    void* ptr = nullptr;
+    rag_status s = static_scratch(&ptr);
+    if (s != RAG_OK) return s;
+    return rag_block_forward(blk, x, y, rows, cu_seqlens, B, max_seqlen, ptr, kStaticScratchBytes, stream);
 }
 
 extern "C" RAG_API rag_status rag_block_forward_padded(rag_block* blk, const void* x, void* y,
                                                        const uint8_t* keep, int32_t B, int32_t N,
-                                                       void* scratch, size_t scratch_bytes_given,
-                                                       void* stream)
+                                                       void* work, size_t work_bytes, void* stream)
 {
     if (!blk) return set_error(RAG_ERR_INVALID_ARG, "block is NULL");
     if (!keep) return set_error(RAG_ERR_INVALID_ARG, "keep is NULL");
     if (B < 1 || N < 1 || B > RAG_MAX_B || N > RAG_MAX_N || (int64_t)B * N > INT32_MAX)
         return set_error(RAG_ERR_INVALID_ARG, "B=%d N=%d out of range", B, N);
     const int32_t rows = B * N;
-    rag_status s = rag::validate_block_call(x, y, rows, blk->C, scratch, scratch_bytes_given,
+    rag_status s = rag::validate_block_call(x, y, rows, blk->C, work, work_bytes,
                                             scratch_bytes(rows, blk->C, blk->hidden));
     if (s != RAG_OK) return s;
-    return forward(blk, x, y, rows, nullptr, keep, B, N, N, scratch, rag::kLayoutPadded,
+    return forward(blk, x, y, rows, nullptr, keep, B, N, N, work, rag::kLayoutPadded,
                    static_cast<hipStream_t>(stream));
 }
 

@@ -294,6 +294,7 @@ def test_block_calls_reject_without_a_block(lib):
     assert lib.rag_block_create(None, None) == INVALID
     assert lib.rag_block_forward(None, A, A, 10, A, 1, 10, A, 1 << 20, None) == INVALID
     assert lib.rag_block_forward_padded(None, A, A, A, 1, 10, A, 1 << 20, None) == INVALID
+    assert lib.rag_block_forward_static(None, A, A, 10, A, 1, 10, None) == INVALID
     lib.rag_block_destroy(None)  # a no-op
     assert lib.rag_block_scratch_bytes(-1, 6, 4) == 0
     assert lib.rag_block_scratch_bytes(10, 6, 4) == 10 * (6 * 384 + 4 * 384) * 2
