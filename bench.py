@@ -502,25 +502,61 @@ def timing_distributions(w_main, main_samples):
 
 
 def python_binding_floor(iters=1000):
-    """rag_attn at minimal work (B = 1, L = 1) called through the Python binding,
-    then a device synchronize: wall-clock p10/p50/p90, to set against the C++
-    round trip of the same call (the difference is the binding's overhead)."""
+    """rag_attn at minimal work (B = 1, L = 1) called from Python, then a
+    synchronize: wall-clock p10/p50/p90, to set against the C++ round trip of
+    the same call (launch + hipStreamSynchronize).  Three forms:
+      call_device_sync: the binding's rag_attn (arguments checked and converted
+        on every call) + torch.cuda.synchronize();
+      plan_stream_sync: a prepared binding.AttnPlan + a synchronize of torch's
+        current stream (the C++ figure's form);
+      plan_device_sync: the prepared plan + torch.cuda.synchronize()."""
     import torch
+    from ragged_attention_token_amd import binding
     from ragged_attention_token_amd import workloads as wl
 
     bf = Bufs(wl.custom(B=1, N=197, H=6, lengths=[1], seed=0, name="floor_l1"))
     bf.pack()
     torch.cuda.synchronize()
-    for _ in range(100):
-        bf.attn()
-        torch.cuda.synchronize()
-    xs = []
-    for _ in range(iters):
-        t0 = time.perf_counter()
-        bf.attn()
-        torch.cuda.synchronize()
-        xs.append((time.perf_counter() - t0) * 1e6)
-    return _pct(xs)
+    C, p = bf.w.C, bf.packed
+    plan = binding.AttnPlan(p[:, :C], p[:, C:2 * C], p[:, 2 * C:], bf.cu, bf.max_seqlen, bf.o_packed,
+                            H=bf.w.H, scale=bf.w.scale)
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name, call, sync in (("call_device_sync", bf.attn, torch.cuda.synchronize),
+                             ("plan_stream_sync", plan, stream.synchronize),
+                             ("plan_device_sync", plan, torch.cuda.synchronize)):
+        for _ in range(100):
+            call()
+            sync()
+        xs = []
+        for _ in range(iters):
+            t0 = time.perf_counter()
+            call()
+            sync()
+            xs.append((time.perf_counter() - t0) * 1e6)
+        out[name] = _pct(xs)
+    return out
+
+
+def serving_summary(sweep_res):
+    """The BS = 1-4 half of the metric: per sweep point with B <= 4, the round
+    trip (host launch call(s) + synchronize, p50 from C++) of every way to run
+    the pass, and the fastest of them."""
+    names = {"eager3": "pack+attn+unpack, three launches from one host call",
+             "graph": "the same pass as one hipGraphLaunch",
+             "fused": "the pass as one gathered launch",
+             "padded": "padded attention alone (comparator)"}
+    out = {"paths": names}
+    for key, rec in sweep_res.items():
+        B = int(key.split("_")[0][1:])
+        if B > 4:
+            continue
+        rt = {k: rec["roundtrip_us"][k] for k in names}
+        ragged = {k: v for k, v in rt.items() if k != "padded"}
+        best = min(ragged, key=ragged.get)
+        out[key] = {"roundtrip_us": rt, "fastest_ragged_path": best,
+                    "fastest_ragged_vs_padded": rt["padded"] / ragged[best]}
+    return out
 
 
 def copy_reference(w, steps):
@@ -741,6 +777,7 @@ def main():
     res["tile_list"] = tile_list_comparison(args.steps)
     if not args.no_sweep:
         res["sweep"] = sweep(args.steps)
+        res["serving_bs1_4"] = serving_summary(res["sweep"])
     if not args.no_cpu:
         print("timing the CPU oracle (<= %.0f s)" % args.cpu_seconds, file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

@@ -273,12 +273,20 @@ RAG_API rag_status rag_attn_gathered(const uint8_t* keep, int32_t B, int32_t N,
 /*
  * A whole pack -> attend -> unpack pass captured once into a HIP graph, so
  * that each later pass costs one host call ([abstract]: the per-call host
- * dispatch cost is what hides the pruning savings).
+ * dispatch cost is what hides the pruning savings).  The same pass can also
+ * be enqueued from one host call as direct launches (rag_pipeline_launch_eager:
+ * three; rag_pipeline_launch_fused: one), which on ROCm 7.2 is the lower-latency
+ * choice: one hipGraphLaunch costs more host time than three direct launches,
+ * whatever the graph holds (rag_measure_dispatch reports both, and a graph of
+ * one empty kernel beside them).
  *
  * The attention reads fused rows of the packed buffer: q at element 0, k at
  * element H*64, v at element 2*H*64 of each row (src rows are [3, H, 64]).
  * Buffers are fixed at creation; relaunching reads the current contents.
  */
+/* rag_pipeline_desc.flags: the captured graph holds the one-launch pass
+ * (rag_attn_gathered, src -> dst) instead of the three stages. */
+#define RAG_PIPELINE_FUSED 1u
 typedef struct rag_pipeline_desc {
     const uint8_t* keep;     /* [B, N] */
     int32_t B, N, H, head_dim;
@@ -298,14 +306,16 @@ typedef struct rag_pipeline_desc {
     void* dst;               /* [B*N] rows of H*64 out_dtype elements */
     int64_t dst_row_stride;  /* bytes */
     uint32_t unpack_flags;
+    uint32_t flags;          /* 0 or RAG_PIPELINE_FUSED */
 } rag_pipeline_desc;
 
 typedef struct rag_pipeline rag_pipeline;
 
-/* Check the descriptor, capture the three calls into a graph and instantiate
- * it.  Runs nothing on the device.  *out is NULL on error. */
+/* Check the descriptor, capture the pass (the three calls, or with
+ * RAG_PIPELINE_FUSED the one gathered launch) into a graph and instantiate it.
+ * Runs nothing on the device.  *out is NULL on error. */
 RAG_API rag_status rag_pipeline_create(const rag_pipeline_desc* desc, rag_pipeline** out);
-/* Enqueue one pass on `stream`: a single hipGraphLaunch. */
+/* Enqueue one pass on `stream`: a single hipGraphLaunch of the captured pass. */
 RAG_API rag_status rag_pipeline_launch(rag_pipeline* p, void* stream);
 /* Enqueue the same pass as three plain launches (no graph) on `stream`. */
 RAG_API rag_status rag_pipeline_launch_eager(rag_pipeline* p, void* stream);
@@ -330,9 +340,12 @@ RAG_API void rag_pipeline_destroy(rag_pipeline* p);
  *   [24..26] rag_attn_gathered: host enqueue only
  *   [27..29] an empty kernel taking one pointer argument: host enqueue only
  *            (beside [3..5], the runtime's cost of passing kernel arguments)
+ *   [30..32] a graph holding one empty kernel: hipGraphLaunch + sync
+ *   [33..35] the same: the hipGraphLaunch call alone (beside [3..5], the
+ *            runtime's cost of launching a graph rather than a kernel)
  * `out_us` must hold RAG_FLOOR_N doubles.  Runs work on `stream`.
  */
-#define RAG_FLOOR_N 30
+#define RAG_FLOOR_N 36
 RAG_API rag_status rag_measure_dispatch(rag_pipeline* p, int32_t warmup, int32_t iters,
                                         double* out_us, void* stream);
 

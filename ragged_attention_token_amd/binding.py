@@ -24,7 +24,8 @@ RAG_DTYPE_F32 = 0
 RAG_DTYPE_BF16 = 1
 RAG_UNPACK_ZERO_DROPPED = 1
 RAG_HEAD_DIM = 64
-RAG_FLOOR_N = 30
+RAG_PIPELINE_FUSED = 1
+RAG_FLOOR_N = 36
 RAG_STAGES_N = 7
 
 #: Every symbol include/rag.h declares.
@@ -58,7 +59,7 @@ class PipelineDesc(ctypes.Structure):
         ("max_seqlen_dev", ctypes.c_void_p),
         ("o_packed", ctypes.c_void_p), ("o_packed_row_stride", ctypes.c_int64),
         ("dst", ctypes.c_void_p), ("dst_row_stride", ctypes.c_int64),
-        ("unpack_flags", ctypes.c_uint32),
+        ("unpack_flags", ctypes.c_uint32), ("flags", ctypes.c_uint32),
     ]
 
 
@@ -135,9 +136,19 @@ def _check(status: int):
         raise RagError(status, last_error())
 
 
-def _stream(stream) -> int:
+try:  # the current stream's handle without building a Stream object
+    _raw_stream = torch._C._cuda_getCurrentRawStream
+except AttributeError:  # pragma: no cover
+    _raw_stream = None
+
+
+def _stream(stream, device: Optional[int] = None) -> int:
+    """hipStream_t of `stream` (a torch stream or a raw handle), or of torch's
+    current stream on `device` (default: the current device)."""
     if stream is None:
-        stream = torch.cuda.current_stream()
+        if _raw_stream is not None:
+            return _raw_stream(torch.cuda.current_device() if device is None else device)
+        stream = torch.cuda.current_stream(device)
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
@@ -166,8 +177,11 @@ def _row_bytes(t: torch.Tensor) -> int:
 def _inner_contiguous(t: torch.Tensor) -> bool:
     """Whether the axes after the first are laid out contiguously (read from the
     strides, without building a view)."""
+    shape, strides = t.shape, t.stride()
+    if len(shape) == 2:  # the common case, without the general loop
+        return strides[1] == 1 or shape[1] == 1
     expect = 1
-    for size, stride in zip(reversed(t.shape[1:]), reversed(t.stride()[1:])):
+    for size, stride in zip(reversed(shape[1:]), reversed(strides[1:])):
         if size != 1 and stride != expect:
             return False
         expect *= size
@@ -180,22 +194,31 @@ def _check_rows(t: torch.Tensor, name: str, min_row_bytes: int = 0) -> None:
     that many bytes from the start of every row, and the C ABI sees only a
     pointer and a stride, so the width is checked here: a narrower view (e.g.
     the last columns of a wider buffer) would let the kernels touch the
-    neighbouring columns or run past the end of the allocation."""
+    neighbouring columns or run past the end of the allocation.  (Shape and
+    strides are read once: this runs on every call.)"""
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch tensor on the GPU" % name)
-    if t.dim() < 2:
-        raise ValueError("%s must have a row axis and a column axis" % name)
-    if not _inner_contiguous(t):
-        raise ValueError("%s: elements within a row must be contiguous" % name)
-    if _row_bytes(t) < min_row_bytes:
+    shape = t.shape
+    if len(shape) == 2:
+        if t.stride(1) != 1 and shape[1] != 1:
+            raise ValueError("%s: elements within a row must be contiguous" % name)
+        row_bytes = shape[1] * t.element_size()
+    else:
+        if len(shape) < 2:
+            raise ValueError("%s must have a row axis and a column axis" % name)
+        if not _inner_contiguous(t):
+            raise ValueError("%s: elements within a row must be contiguous" % name)
+        row_bytes = _row_bytes(t)
+    if row_bytes < min_row_bytes:
         raise ValueError("%s rows hold %d bytes; the call reads or writes %d bytes of each row"
-                         % (name, _row_bytes(t), min_row_bytes))
+                         % (name, row_bytes, min_row_bytes))
 
 
-def _rows(t: torch.Tensor, name: str, min_row_bytes: int = 0):
+def _rows(t: torch.Tensor, name: str, min_row_bytes: int = 0, checked: bool = False):
     """(pointer, row stride in elements) of a row tensor on the GPU (checked as
-    in _check_rows)."""
-    _check_rows(t, name, min_row_bytes)
+    in _check_rows, unless the caller has just done so)."""
+    if not checked:
+        _check_rows(t, name, min_row_bytes)
     _gpu(t, name)
     return t.data_ptr(), t.stride(0)
 
@@ -208,7 +231,7 @@ def _qkvo(q, k, v, o, H, head_dim):
         _check_rows(t, name, int(H) * int(head_dim) * getattr(t, "element_size", lambda: 0)())
     out = []
     for t, name in named:
-        out.extend(_rows(t, name))
+        out.extend(_rows(t, name, checked=True))
     return out
 
 
@@ -224,8 +247,8 @@ def rag_pack(keep: torch.Tensor, src: torch.Tensor, packed: torch.Tensor, cu_seq
     rb = _row_bytes(src) if row_bytes is None else int(row_bytes)
     _check_rows(src, "src", rb)
     _check_rows(packed, "packed", rb)
-    sp, ss = _rows(src, "src")
-    pp, ps = _rows(packed, "packed")
+    sp, ss = _rows(src, "src", checked=True)
+    pp, ps = _rows(packed, "packed", checked=True)
     _gpu(keep, "keep")
     for t, name in ((cu_seqlens, "cu_seqlens"), (gather_idx, "gather_idx")):
         _gpu(t, name)
@@ -255,8 +278,8 @@ def rag_repack(keep_packed: torch.Tensor, cu_in: torch.Tensor, gather_in: torch.
     rb = _row_bytes(src) if row_bytes is None else int(row_bytes)
     _check_rows(src, "src", rb)
     _check_rows(dst, "dst", rb)
-    sp, ss = _rows(src, "src")
-    dp, ds = _rows(dst, "dst")
+    sp, ss = _rows(src, "src", checked=True)
+    dp, ds = _rows(dst, "dst", checked=True)
     _gpu(keep_packed, "keep_packed")
     for t, name in ((cu_in, "cu_in"), (gather_in, "gather_in"), (cu_out, "cu_out"),
                     (gather_out, "gather_out")):
@@ -302,6 +325,42 @@ def rag_attn_tiled(q, k, v, cu_seqlens, max_seqlen, o, H, scale, head_dim=RAG_HE
     rag_attn(q, k, v, cu_seqlens, max_seqlen, o, H, scale, head_dim, total_rows, stream, tiled=True)
 
 
+class AttnPlan:
+    """A prepared rag_attn call on fixed tensors: the arguments are checked and
+    turned into C values once, so that each call only looks up the current
+    stream and enters the C ABI (the per-call cost of a Python caller stays
+    near the C++ dispatch floor).  Arguments as rag_attn; the tensors are kept
+    alive here and must keep their storage."""
+
+    def __init__(self, q, k, v, cu_seqlens, max_seqlen, o, H, scale, head_dim=RAG_HEAD_DIM,
+                 total_rows=None, tiled=False):
+        qp, qs, kp, ks, vp, vs, op, os_ = _qkvo(q, k, v, o, H, head_dim)
+        _gpu(cu_seqlens, "cu_seqlens")
+        if cu_seqlens.dtype != torch.int32:
+            raise TypeError("cu_seqlens must be int32")
+        if not (q.dtype == k.dtype == v.dtype):
+            raise TypeError("q, k, v must share a dtype")
+        rows = min(q.shape[0], k.shape[0], v.shape[0], o.shape[0])
+        tr = rows if total_rows is None else int(total_rows)
+        if tr > rows:
+            raise ValueError("total_rows larger than the buffers")
+        lib = load()
+        self._fn = lib.rag_attn_tiled if tiled else lib.rag_attn
+        c = ctypes
+        self._args = (c.c_void_p(qp), c.c_void_p(kp), c.c_void_p(vp), c.c_int64(qs), c.c_int64(ks),
+                      c.c_int64(vs), c.c_int32(_dtype_code(q)), c.c_void_p(cu_seqlens.data_ptr()),
+                      c.c_int32(cu_seqlens.numel() - 1), c.c_int32(int(max_seqlen)), c.c_int32(tr),
+                      c.c_int32(int(H)), c.c_int32(int(head_dim)), c.c_float(float(scale)),
+                      c.c_void_p(op), c.c_int64(os_), c.c_int32(_dtype_code(o)))
+        self._dev = q.device.index
+        self._keep_alive = (q, k, v, cu_seqlens, o)
+
+    def __call__(self, stream=None) -> None:
+        status = self._fn(*self._args, _stream(stream, self._dev))
+        if status != RAG_OK:
+            raise RagError(status, last_error())
+
+
 def rag_unpack(packed: torch.Tensor, cu_seqlens: torch.Tensor, gather_idx: torch.Tensor,
                dst: torch.Tensor, N: int, flags: int = 0, row_bytes: Optional[int] = None,
                stream=None) -> None:
@@ -309,8 +368,8 @@ def rag_unpack(packed: torch.Tensor, cu_seqlens: torch.Tensor, gather_idx: torch
     rb = _row_bytes(dst) if row_bytes is None else int(row_bytes)
     _check_rows(packed, "packed", rb)
     _check_rows(dst, "dst", rb)
-    pp, ps = _rows(packed, "packed")
-    dp, ds = _rows(dst, "dst")
+    pp, ps = _rows(packed, "packed", checked=True)
+    dp, ds = _rows(dst, "dst", checked=True)
     for t, name in ((cu_seqlens, "cu_seqlens"), (gather_idx, "gather_idx")):
         _gpu(t, name)
         if t.dtype != torch.int32:
@@ -366,7 +425,8 @@ class Pipeline:
     and fixed for the pipeline's lifetime."""
 
     def __init__(self, keep, src, packed, cu_seqlens, gather_idx, o_packed, dst, H, scale,
-                 max_seqlen: int = 0, max_seqlen_dev=None, unpack_flags: int = 0):
+                 max_seqlen: int = 0, max_seqlen_dev=None, unpack_flags: int = 0,
+                 fused_graph: bool = False):
         B, N = keep.shape
         C = int(H) * RAG_HEAD_DIM
         # row widths the three kernels touch: fused q|k|v rows of src / packed,
@@ -397,26 +457,28 @@ class Pipeline:
         d.o_packed_row_stride = o_packed.stride(0) * o_packed.element_size()
         d.dst, d.dst_row_stride = dst.data_ptr(), dst.stride(0) * dst.element_size()
         d.unpack_flags = int(unpack_flags)
+        d.flags = RAG_PIPELINE_FUSED if fused_graph else 0
         self.desc = d
+        self._dev = keep.device.index
         handle = ctypes.c_void_p()
         _check(load().rag_pipeline_create(ctypes.byref(d), ctypes.byref(handle)))
         self._h = handle
 
     def launch(self, stream=None) -> None:
-        _check(load().rag_pipeline_launch(self._h, _stream(stream)))
+        _check(load().rag_pipeline_launch(self._h, _stream(stream, self._dev)))
 
     def launch_eager(self, stream=None) -> None:
-        _check(load().rag_pipeline_launch_eager(self._h, _stream(stream)))
+        _check(load().rag_pipeline_launch_eager(self._h, _stream(stream, self._dev)))
 
     def launch_fused(self, stream=None) -> None:
-        _check(load().rag_pipeline_launch_fused(self._h, _stream(stream)))
+        _check(load().rag_pipeline_launch_fused(self._h, _stream(stream, self._dev)))
 
     def measure_dispatch(self, warmup: int = 100, iters: int = 1000, stream=None) -> dict:
         out = (ctypes.c_double * RAG_FLOOR_N)()
         _check(load().rag_measure_dispatch(self._h, int(warmup), int(iters), out, _stream(stream)))
         keys = ["empty_roundtrip", "empty_enqueue", "attn_roundtrip", "attn_enqueue",
                 "eager3_roundtrip", "graph_roundtrip", "padded_roundtrip", "fused_roundtrip",
-                "fused_enqueue", "empty_arg_enqueue"]
+                "fused_enqueue", "empty_arg_enqueue", "graph1_roundtrip", "graph1_launch"]
         res = {}
         for i, k in enumerate(keys):
             res[k] = {"p10": out[3 * i], "p50": out[3 * i + 1], "p90": out[3 * i + 2]}

@@ -6,9 +6,12 @@
 // call costs more than the GPU work, so the dispatch floor is what must come
 // down): every entry point checks its arguments on the host, enqueues exactly
 // one kernel on the caller's stream and returns; nothing is read back, nothing
-// waits, nothing is allocated.  The pipeline captures the three launches once
-// into a HIP graph so that a whole pack -> attend -> unpack pass is one host
-// call.
+// waits, nothing is allocated.  The pipeline captures the pass once into a
+// HIP graph (the three launches, or the one gathered launch) so that a whole
+// pack -> attend -> unpack pass is one hipGraphLaunch; it also enqueues the
+// same pass from one host call as direct launches, which on ROCm 7.2 is the
+// faster of the two (rag_measure_dispatch times a graph of one empty kernel
+// beside them).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -217,7 +220,7 @@ extern "C" RAG_API rag_status rag_pipeline_create(const rag_pipeline_desc* desc,
         s = hip_status((int)hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal),
                        "begin capture");
         if (s == RAG_OK) {
-            rag_status es = enqueue_pass(p->d, cs);
+            rag_status es = (p->d.flags & RAG_PIPELINE_FUSED) ? enqueue_fused(p->d, cs) : enqueue_pass(p->d, cs);
             rag_status cs_end = hip_status((int)hipStreamEndCapture(cs, &p->graph), "end capture");
             s = es != RAG_OK ? es : cs_end;
         }
@@ -360,7 +363,28 @@ extern "C" RAG_API rag_status rag_measure_dispatch(rag_pipeline* p, int32_t warm
     };
     double unused_rt[3];
     if ((s = time_calls(empty_arg, st, warmup, iters, unused_rt, out_us + 27)) != RAG_OK) return s;
-    return RAG_OK;
+    // a graph of one empty kernel: what launching through a graph costs by itself
+    hipGraph_t g1 = nullptr;
+    hipGraphExec_t g1x = nullptr;
+    hipStream_t cs = nullptr;
+    s = hip_status((int)hipStreamCreateWithFlags(&cs, hipStreamNonBlocking), "capture stream");
+    if (s == RAG_OK) {
+        s = hip_status((int)hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal), "begin capture");
+        if (s == RAG_OK) {
+            hipLaunchKernelGGL(empty_kernel, dim3(1), dim3(64), 0, cs);
+            const rag_status ls = hip_status((int)hipGetLastError(), "empty kernel capture");
+            const rag_status es = hip_status((int)hipStreamEndCapture(cs, &g1), "end capture");
+            s = ls != RAG_OK ? ls : es;
+        }
+        if (s == RAG_OK)
+            s = hip_status((int)hipGraphInstantiate(&g1x, g1, nullptr, nullptr, 0), "graph instantiate");
+        (void)hipStreamDestroy(cs);
+    }
+    auto graph1 = [&]() { return hip_status((int)hipGraphLaunch(g1x, st), "hipGraphLaunch"); };
+    if (s == RAG_OK) s = time_calls(graph1, st, warmup, iters, out_us + 30, out_us + 33);
+    if (g1x) (void)hipGraphExecDestroy(g1x);
+    if (g1) (void)hipGraphDestroy(g1);
+    return s;
 }
 
 extern "C" RAG_API rag_status rag_measure_stages(rag_pipeline* p, int32_t iters, double* out_us,

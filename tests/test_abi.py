@@ -182,7 +182,8 @@ def test_pipeline_rejects(lib):
     d.dst, d.dst_row_stride = A, 768
     for field, value, status in (("head_dim", 80, UNSUPPORTED), ("max_seqlen", 500, INVALID),
                                  ("src_row_stride", 2000, INVALID), ("dst", A + 8, ALIGN),
-                                 ("unpack_flags", 4, UNSUPPORTED), ("in_dtype", 5, UNSUPPORTED)):
+                                 ("unpack_flags", 4, UNSUPPORTED), ("in_dtype", 5, UNSUPPORTED),
+                                 ("flags", 2, UNSUPPORTED)):
         saved = getattr(d, field)
         setattr(d, field, value)
         assert lib.rag_pipeline_create(ctypes.byref(d), ctypes.byref(h)) == status, field

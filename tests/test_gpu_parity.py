@@ -377,6 +377,61 @@ def test_gathered_zero_dropped_and_fused_pipeline():
     pipe.close()
 
 
+@pytest.mark.parametrize("flags", [0, binding.RAG_UNPACK_ZERO_DROPPED])
+def test_fused_graph_pipeline_replays_the_one_launch_pass(flags):
+    """A pipeline created with RAG_PIPELINE_FUSED captures the one-launch pass:
+    every replay writes dst exactly as the three-stage pass does (the same
+    kernel arithmetic), with unrelated eager work between the replays, and
+    leaves the packed buffers, offsets and gather index untouched."""
+    w = wl.custom(B=6, N=197, H=6, lengths=[0, 197, 1, 40, 64, 40], seed=19)
+    bufs = _pipeline_buffers(w, torch.bfloat16)
+    staged_pipe = _make_pipeline(w, bufs, flags=flags)
+    staged_pipe.launch_eager()
+    torch.cuda.synchronize()
+    staged = bufs["dst"].clone()
+    staged_pipe.close()
+    bufs = _pipeline_buffers(w, torch.bfloat16)
+    pipe = binding.Pipeline(bufs["keep"], bufs["src"], bufs["packed"], bufs["cu"], bufs["gather"],
+                            bufs["o_packed"], bufs["dst"], H=w.H, scale=w.scale, unpack_flags=flags,
+                            fused_graph=True)
+    for rep in range(3):
+        bufs["dst"].view(torch.uint8).fill_(SENTINEL_BYTE)
+        torch.cuda.synchronize()
+        pipe.launch()
+        torch.cuda.synchronize()
+        assert torch.equal(bufs["dst"].view(torch.uint8), staged.view(torch.uint8)), rep
+        for k in ("packed", "cu", "gather", "o_packed"):
+            assert (bufs[k].view(torch.uint8) == SENTINEL_BYTE).all(), (rep, k)
+        scratch = torch.randn(1 << 20, device="cuda").sum()  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        del scratch
+    res = pipe.measure_dispatch(warmup=3, iters=10)
+    assert res["graph1_launch"]["p50"] > 0 and res["graph1_roundtrip"]["p50"] > 0
+    pipe.close()
+
+
+def test_attn_plan_equals_the_call():
+    """binding.AttnPlan prepares a rag_attn call once; calling it gives the
+    call's output bit for bit (on torch's current stream and on another)."""
+    w = wl.deits(3, 500)
+    g = gpu_pack(w)
+    C = w.C
+    ref = gpu_attn(g["packed"], g["cu"], w, torch.float32)
+    o = sentinel_like((w.B * w.N, C), torch.float32)
+    p = g["packed"]
+    plan = binding.AttnPlan(p[:, :C], p[:, C:2 * C], p[:, 2 * C:], g["cu"], w.N, o, H=w.H, scale=w.scale)
+    plan()
+    torch.cuda.synchronize()
+    assert torch.equal(o[:w.T].view(torch.uint8), ref[:w.T].view(torch.uint8))
+    o.view(torch.uint8).fill_(SENTINEL_BYTE)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        plan()
+    side.synchronize()
+    assert torch.equal(o[:w.T].view(torch.uint8), ref[:w.T].view(torch.uint8))
+
+
 def test_lds_resident_and_tile_kernels_agree_bit_for_bit():
     """bf16 input takes the LDS-resident kernel when max_seqlen is small enough
     for the image's K and V to sit in LDS, and the 64-key tile kernel otherwise.
