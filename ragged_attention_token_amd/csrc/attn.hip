@@ -18,7 +18,7 @@
 //     keys with no further synchronisation (see the comment at the kernel);
 //   * attn_kernel (fp32 input, or longer sequences): one workgroup = one
 //     (head, image, q-tile of 64 rows), 4 wave64s of 16 query rows, K / V
-//     staged through LDS 64 keys at a time (K row-major, V transposed), the
+//     staged through LDS 64 keys at a time (row-major, as above), the
 //     next tile's loads in registers while the current tile computes.
 // Both:
 //   * all global traffic goes through buffer resources whose range ends at
@@ -57,8 +57,6 @@ constexpr int kD = 64;         // head dimension
 constexpr int kBM = 64;        // query rows per workgroup
 constexpr int kBN = 64;        // keys per LDS tile
 constexpr int kThreads = 256;  // 4 waves x 16 query rows
-constexpr int kKS = 72;        // LDS row stride of the K tile (bf16): 144 B
-constexpr int kVS = 68;        // LDS row stride of the V^T tile (bf16): 136 B
 
 // Where the rows of one image live.
 enum Layout : int {
@@ -97,8 +95,6 @@ __device__ __forceinline__ float row_max(float x)
     auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
-
-__device__ __forceinline__ uint32_t bits(__bf16 x) { return __builtin_bit_cast(uint16_t, x); }
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -449,6 +445,48 @@ __device__ void zero_dropped_head(const AttnParams& p, int64_t row0, int h)
     }
 }
 
+// ---- LDS operand layout shared by both kernels ------------------------------
+//
+// K and V rows are held in LDS as 128-byte rows (64 bf16) in natural row-major
+// order, with the eight 16-byte chunks of row r permuted by XOR with swz(r).
+// The permutation makes both operand reads conflict-free across 16
+// consecutive rows: the K reads (ds_read_b128, lane = row) and the V reads
+// with gfx950's transposing read ds_read_b64_tr_b16, which delivers V^T's MFMA
+// operand from row-major V.
+constexpr int kRowBytes = kD * 2;     // one head's bf16 row
+
+// Slot of chunk c of row r is c ^ swz(r); swz depends on r mod 16 only.
+__device__ __forceinline__ int swz(int row) { return (row ^ ((row >> 3) & 1)) & 7; }
+
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) short4_t lds_short4_t;
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Four bf16 of one LDS column: lane j of each 16-lane group receives element
+// (k, j) of the 4 x 16 block whose row segments the group's lanes address.
+__device__ __forceinline__ bf16x4 ld_tr4(const char* lds_addr)
+{
+    return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)lds_addr));
+}
+
+// Per-lane LDS offsets inside a 16-row block.
+//  K (A operand of S^T): row r16, chunks g and g + 4 of the row (the second
+//  is this one XOR 64).
+__device__ __forceinline__ uint32_t k_operand_offset(int r16, int g)
+{
+    return 128u * r16 + 16u * (uint32_t)(g ^ swz(r16));
+}
+//  V (A operand of O^T += V^T P^T, transposing read) for 16-column block db:
+//  lane i of group g addresses row 4g + i/4, columns 16 db + 4 (i % 4) .. + 3;
+//  it receives V[4g + k][16 db + i] for k = 0..3 -- keys 4g..4g+3 of d-row i,
+//  the k-slots that match the probabilities' layout (p_operand).
+__device__ __forceinline__ uint32_t v_operand_offset(int r16, int g, int db)
+{
+    const int vrow = 4 * g + (r16 >> 2);
+    return 128u * vrow + 16u * (uint32_t)((2 * db + ((r16 & 3) >> 1)) ^ swz(vrow)) + 8u * (r16 & 1);
+}
+
 template <bool IN_F32, bool OUT_F32, int LAYOUT, bool TILES>
 __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
 {
@@ -457,14 +495,13 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
     constexpr int NP = IN_F32 ? 2 : 1;  // bf16 planes: hi (and lo)
     constexpr int ES = IN_F32 ? 4 : 2;  // input element bytes
     constexpr int OES = OUT_F32 ? 4 : 2;
-    constexpr int K_PLANE = kBN * kKS;   // bf16 elements
-    constexpr int V_PLANE = kD * kVS;
-    constexpr int OUT_ROW = kD * OES + 16;                   // bytes, padded
-    constexpr int SMEM = 2 * (NP * K_PLANE + NP * V_PLANE);  // bytes
-    static_assert(4 * 16 * OUT_ROW <= SMEM, "output staging must fit the tile buffers");
+    constexpr int PLANE = kBN * kRowBytes;        // one bf16 plane of a 64-key K or V tile
+    constexpr int OUT_ROW = kD * OES + 16;        // bytes, padded
+    // K planes, then V planes; the output is staged in the same bytes afterwards
+    constexpr int SMEM = 2 * NP * PLANE > 4 * 16 * OUT_ROW ? 2 * NP * PLANE : 4 * 16 * OUT_ROW;
     __shared__ __attribute__((aligned(16))) char smem[SMEM];
-    __bf16* sK = reinterpret_cast<__bf16*>(smem);
-    __bf16* sVt = sK + NP * K_PLANE;
+    char* sK = smem;
+    char* sV = smem + NP * PLANE;
     __shared__ uint8_t sKeep[kBN];
     extern __shared__ int s_pos[];  // gathered: the image's kept positions by rank (N ints)
     __shared__ int s_wsum[16];  // keep ranking: up to 4 planes x 4 waves
@@ -547,33 +584,36 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
     online_init(st);
 
     // Registers carrying one K/V tile from global memory to LDS: this thread's
-    // two 16-byte K pieces and its V key pair (hi and, for fp32 input, lo).
+    // 16-byte chunk k_dg of key rows k_row0 and k_row1, of K and of V (hi and,
+    // for fp32 input, lo).  Eight consecutive lanes store one 128-byte LDS
+    // row, in the permuted chunk order of the operand layout.
     bf16x8 kh0, kl0, kh1, kl1, vh0, vl0, vh1, vl1;
-    const int k_key0 = tid >> 3, k_key1 = (tid + kThreads) >> 3, k_dg = tid & 7;
-    const int v_kp = tid >> 3, v_dg = tid & 7;
+    const int k_row0 = tid >> 3, k_row1 = (tid + kThreads) >> 3, k_dg = tid & 7;
+    const uint32_t so0 = 128u * k_row0 + 16u * (uint32_t)(k_dg ^ swz(k_row0));
+    const uint32_t so1 = 128u * k_row1 + 16u * (uint32_t)(k_dg ^ swz(k_row1));
     auto fetch = [&](int kt) {
-        load8<IN_F32>(rk, row_off(kt + k_key0, ksb) + 8 * k_dg * ES, kh0, kl0);
-        load8<IN_F32>(rk, row_off(kt + k_key1, ksb) + 8 * k_dg * ES, kh1, kl1);
-        load8<IN_F32>(rv, row_off(kt + 2 * v_kp, vsb) + 8 * v_dg * ES, vh0, vl0);
-        load8<IN_F32>(rv, row_off(kt + 2 * v_kp + 1, vsb) + 8 * v_dg * ES, vh1, vl1);
+        load8<IN_F32>(rk, row_off(kt + k_row0, ksb) + 8 * k_dg * ES, kh0, kl0);
+        load8<IN_F32>(rk, row_off(kt + k_row1, ksb) + 8 * k_dg * ES, kh1, kl1);
+        load8<IN_F32>(rv, row_off(kt + k_row0, vsb) + 8 * k_dg * ES, vh0, vl0);
+        load8<IN_F32>(rv, row_off(kt + k_row1, vsb) + 8 * k_dg * ES, vh1, vl1);
     };
     auto stash = [&]() {
-        // K row-major; V transposed with keys 2kp, 2kp+1 side by side (one
-        // 32-bit LDS store per (d, key pair))
-        *reinterpret_cast<bf16x8*>(&sK[k_key0 * kKS + 8 * k_dg]) = kh0;
-        *reinterpret_cast<bf16x8*>(&sK[k_key1 * kKS + 8 * k_dg]) = kh1;
+        *reinterpret_cast<bf16x8*>(sK + so0) = kh0;
+        *reinterpret_cast<bf16x8*>(sK + so1) = kh1;
+        *reinterpret_cast<bf16x8*>(sV + so0) = vh0;
+        *reinterpret_cast<bf16x8*>(sV + so1) = vh1;
         if constexpr (IN_F32) {
-            *reinterpret_cast<bf16x8*>(&sK[K_PLANE + k_key0 * kKS + 8 * k_dg]) = kl0;
-            *reinterpret_cast<bf16x8*>(&sK[K_PLANE + k_key1 * kKS + 8 * k_dg]) = kl1;
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int o = (8 * v_dg + i) * kVS + 2 * v_kp;
-            *reinterpret_cast<uint32_t*>(&sVt[o]) = bits(vh0[i]) | (bits(vh1[i]) << 16);
-            if constexpr (IN_F32)
-                *reinterpret_cast<uint32_t*>(&sVt[V_PLANE + o]) = bits(vl0[i]) | (bits(vl1[i]) << 16);
+            *reinterpret_cast<bf16x8*>(sK + PLANE + so0) = kl0;
+            *reinterpret_cast<bf16x8*>(sK + PLANE + so1) = kl1;
+            *reinterpret_cast<bf16x8*>(sV + PLANE + so0) = vl0;
+            *reinterpret_cast<bf16x8*>(sV + PLANE + so1) = vl1;
         }
     };
+    const uint32_t koff0 = k_operand_offset(r16, g);
+    const uint32_t koff1 = koff0 ^ 64u;
+    uint32_t voff[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) voff[db] = v_operand_offset(r16, g, db);
     fetch(0);
 
     // Stage the tile at key kt into LDS (the next one's loads go out meanwhile),
@@ -596,14 +636,14 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
             if (FULL || kb == 0 || 16 * kb < nk) {
-                const __bf16* kr = &sK[(kb * 16 + r16) * kKS + 8 * g];
-                const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kr);
-                const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kr + 32);
+                const char* kr = sK + 2048 * kb;
+                const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kr + koff0);
+                const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kr + koff1);
                 s[kb] = mfma(a0, qh0, f32x4{0.f, 0.f, 0.f, 0.f});
                 s[kb] = mfma(a1, qh1, s[kb]);
                 if constexpr (IN_F32) {
-                    const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(kr + K_PLANE);
-                    const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(kr + K_PLANE + 32);
+                    const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(kr + PLANE + koff0);
+                    const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(kr + PLANE + koff1);
                     s[kb] = mfma(b0, qh0, s[kb]);
                     s[kb] = mfma(b1, qh1, s[kb]);
                     s[kb] = mfma(a0, ql0, s[kb]);
@@ -622,15 +662,15 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
                 p_operand(s, cc, ph, pl, st);
 #pragma unroll
                 for (int db = 0; db < 4; ++db) {
-                    const int vo = (db * 16 + r16) * kVS + 32 * cc + 4 * g;
-                    const bf16x4 v0 = *reinterpret_cast<const bf16x4*>(&sVt[vo]);
-                    const bf16x4 v1 = *reinterpret_cast<const bf16x4*>(&sVt[vo + 16]);
+                    const char* vr = sV + 4096 * cc + voff[db];
+                    const bf16x4 v0 = ld_tr4(vr);
+                    const bf16x4 v1 = ld_tr4(vr + 2048);
                     const bf16x8 av = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
                     st.acc[db] = mfma(av, ph, st.acc[db]);
                     st.acc[db] = mfma(av, pl, st.acc[db]);
                     if constexpr (IN_F32) {
-                        const bf16x4 w0 = *reinterpret_cast<const bf16x4*>(&sVt[V_PLANE + vo]);
-                        const bf16x4 w1 = *reinterpret_cast<const bf16x4*>(&sVt[V_PLANE + vo + 16]);
+                        const bf16x4 w0 = ld_tr4(vr + PLANE);
+                        const bf16x4 w1 = ld_tr4(vr + PLANE + 2048);
                         const bf16x8 al = __builtin_shufflevector(w0, w1, 0, 1, 2, 3, 4, 5, 6, 7);
                         st.acc[db] = mfma(al, ph, st.acc[db]);
                     }
@@ -686,32 +726,11 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
 // further synchronisation, and waves without a block exit.  Compared with a
 // tile loop this removes the per-tile barriers and register staging, reads K
 // and V once per (image, head) and query split, and lets the last partial key
-// tile skip its empty 16-key blocks.
-//
-// LDS rows are 128 bytes (64 bf16) in natural row-major order, with the eight
-// 16-byte chunks of row r permuted by XOR with swz(r).  The permutation makes
-// both operand reads conflict-free across 16 consecutive rows: the K reads
-// (ds_read_b128, lane = row) and the V reads with gfx950's transposing read
-// ds_read_b64_tr_b16, which delivers V^T's MFMA operand from row-major V.
-constexpr int kRowBytes = kD * 2;     // one head's bf16 row
+// tile skip its empty 16-key blocks.  K and V rows use the LDS operand layout
+// above.
 constexpr int kLdsRowAlign = 32;      // K / V rows in LDS: a multiple of the P.V k-depth
 constexpr int kMaxWaves = 16;         // 16 query blocks: every block of kLdsMaxRows rows
 constexpr int kLdsMaxRows = 256;      // 64 KiB of K + V: two workgroups per CU
-
-// Slot of chunk c of row r is c ^ swz(r); swz depends on r mod 16 only.
-__device__ __forceinline__ int swz(int row) { return (row ^ ((row >> 3) & 1)) & 7; }
-
-typedef short short4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(3))) short4_t lds_short4_t;
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-
-// Four bf16 of one LDS column: lane j of each 16-lane group receives element
-// (k, j) of the 4 x 16 block whose row segments the group's lanes address.
-__device__ __forceinline__ bf16x4 ld_tr4(const char* lds_addr)
-{
-    return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)lds_addr));
-}
 
 // TL: 0 = grid of (head, image, query split); tile list of 1 = whole pairs,
 // 2 = 64-row query tiles.
@@ -823,19 +842,12 @@ __global__ __launch_bounds__(64 * kMaxWaves) void attn_lds_kernel(AttnParams p)
     __syncthreads();
     if (qb >= qhi) return;
 
-    // Per-lane LDS offsets inside a 16-row block.
-    //  K (A operand of S^T): row r16, chunks g and g + 4 of the row.
-    const uint32_t koff0 = 128u * r16 + 16u * (uint32_t)(g ^ swz(r16));
+    // per-lane LDS offsets of the K and V operands inside a 16-row block
+    const uint32_t koff0 = k_operand_offset(r16, g);
     const uint32_t koff1 = koff0 ^ 64u;
-    //  V (A operand of O^T += V^T P^T, transposing read): lane i of group g
-    //  addresses row 4g + i/4, columns 16 db + 4 (i % 4) .. + 3; it receives
-    //  V[4g + k][16 db + i] for k = 0..3 -- keys 4g..4g+3 of d-row i, the
-    //  k-slots that match the probabilities' layout below.
-    const int vrow = 4 * g + (r16 >> 2);
     uint32_t voff[4];
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
-        voff[db] = 128u * vrow + 16u * (uint32_t)((2 * db + ((r16 & 3) >> 1)) ^ swz(vrow)) + 8u * (r16 & 1);
+    for (int db = 0; db < 4; ++db) voff[db] = v_operand_offset(r16, g, db);
 
     const auto ro = make_rsrc(static_cast<char*>(p.o) + (row0 * p.os + hoff) * OES,
                               (uint32_t)(span - 1) * osb + kD * OES);
