@@ -365,6 +365,7 @@ def sweep(steps):
     and of a whole pass (three launches, and one graph launch), and the host
     round trip (launch + synchronize) of each at that point."""
     import torch
+    from ragged_attention_token_amd import binding
     from ragged_attention_token_amd import workloads as wl
 
     out = {}
@@ -385,6 +386,15 @@ def sweep(steps):
             fl = bf.pipe.measure_dispatch(warmup=20, iters=200)
             rec["roundtrip_us"] = {k: fl[k + "_roundtrip"]["p50"]
                                    for k in ("attn", "eager3", "graph", "padded", "fused")}
+            if B <= 4:
+                # the serving configuration of the pipeline object itself: created
+                # with the direct and fused flags, rag_pipeline_launch is one launch
+                dp = binding.Pipeline(bf.keep, bf.src, bf.packed, bf.cu, bf.gather, bf.o_packed,
+                                      bf.dst, H=w.H, scale=w.scale, max_seqlen=bf.max_seqlen,
+                                      fused_graph=True, direct=True)
+                rec["roundtrip_us"]["pipeline_direct_fused"] = \
+                    dp.measure_dispatch(warmup=20, iters=200)["graph_roundtrip"]["p50"]
+                dp.close()
             out["B%d_p%03d" % (B, p)] = rec
             print("sweep B=%d p=%03d: attn %.2f us, pipeline %.2f us" %
                   (B, p, rec["attn_us"], rec["pipeline_us"]), file=sys.stderr, flush=True)
@@ -545,6 +555,8 @@ def serving_summary(sweep_res):
     names = {"eager3": "pack+attn+unpack, three launches from one host call",
              "graph": "the same pass as one hipGraphLaunch",
              "fused": "the pass as one gathered launch",
+             "pipeline_direct_fused": "rag_pipeline_launch of a pipeline created with "
+                                      "RAG_PIPELINE_DIRECT | RAG_PIPELINE_FUSED (one launch)",
              "padded": "padded attention alone (comparator)"}
     out = {"paths": names}
     for key, rec in sweep_res.items():

@@ -25,6 +25,7 @@ RAG_DTYPE_BF16 = 1
 RAG_UNPACK_ZERO_DROPPED = 1
 RAG_HEAD_DIM = 64
 RAG_PIPELINE_FUSED = 1
+RAG_PIPELINE_DIRECT = 2
 RAG_FLOOR_N = 36
 RAG_STAGES_N = 7
 
@@ -426,7 +427,7 @@ class Pipeline:
 
     def __init__(self, keep, src, packed, cu_seqlens, gather_idx, o_packed, dst, H, scale,
                  max_seqlen: int = 0, max_seqlen_dev=None, unpack_flags: int = 0,
-                 fused_graph: bool = False):
+                 fused_graph: bool = False, direct: bool = False):
         B, N = keep.shape
         C = int(H) * RAG_HEAD_DIM
         # row widths the three kernels touch: fused q|k|v rows of src / packed,
@@ -457,7 +458,7 @@ class Pipeline:
         d.o_packed_row_stride = o_packed.stride(0) * o_packed.element_size()
         d.dst, d.dst_row_stride = dst.data_ptr(), dst.stride(0) * dst.element_size()
         d.unpack_flags = int(unpack_flags)
-        d.flags = RAG_PIPELINE_FUSED if fused_graph else 0
+        d.flags = (RAG_PIPELINE_FUSED if fused_graph else 0) | (RAG_PIPELINE_DIRECT if direct else 0)
         self.desc = d
         self._dev = keep.device.index
         handle = ctypes.c_void_p()

@@ -214,6 +214,10 @@ extern "C" RAG_API rag_status rag_pipeline_create(const rag_pipeline_desc* desc,
     rag_pipeline* p = new (std::nothrow) rag_pipeline;
     if (!p) return set_error(RAG_ERR_NO_MEMORY, "out of host memory");
     p->d = *desc;
+    if (p->d.flags & RAG_PIPELINE_DIRECT) {  // direct launches: nothing to capture
+        *out = p;
+        return RAG_OK;
+    }
     hipStream_t cs = nullptr;
     s = hip_status((int)hipStreamCreateWithFlags(&cs, hipStreamNonBlocking), "capture stream");
     if (s == RAG_OK) {
@@ -239,7 +243,10 @@ extern "C" RAG_API rag_status rag_pipeline_create(const rag_pipeline_desc* desc,
 
 extern "C" RAG_API rag_status rag_pipeline_launch(rag_pipeline* p, void* stream)
 {
-    if (!p || !p->exec) return set_error(RAG_ERR_INVALID_ARG, "pipeline is NULL");
+    if (!p) return set_error(RAG_ERR_INVALID_ARG, "pipeline is NULL");
+    if (p->d.flags & RAG_PIPELINE_DIRECT)
+        return (p->d.flags & RAG_PIPELINE_FUSED) ? enqueue_fused(p->d, stream) : enqueue_pass(p->d, stream);
+    if (!p->exec) return set_error(RAG_ERR_INVALID_ARG, "pipeline has no graph");
     return hip_status((int)hipGraphLaunch(p->exec, static_cast<hipStream_t>(stream)),
                       "hipGraphLaunch");
 }

@@ -246,7 +246,7 @@ rag_status validate_pipeline(const rag_pipeline_desc* d)
     if (d->H < 1) return set_error(RAG_ERR_INVALID_ARG, "H=%d must be >= 1", d->H);
     if (d->max_seqlen < 0 || d->max_seqlen > d->N)
         return set_error(RAG_ERR_INVALID_ARG, "max_seqlen=%d must lie in [0, N]", d->max_seqlen);
-    if (d->flags & ~RAG_PIPELINE_FUSED)
+    if (d->flags & ~(RAG_PIPELINE_FUSED | RAG_PIPELINE_DIRECT))
         return set_error(RAG_ERR_UNSUPPORTED, "unknown pipeline flags 0x%x", d->flags);
     const int64_t C = (int64_t)d->H * d->head_dim;
     const int64_t in_row = 3 * C * dtype_bytes(d->in_dtype);

@@ -183,12 +183,20 @@ def test_pipeline_rejects(lib):
     for field, value, status in (("head_dim", 80, UNSUPPORTED), ("max_seqlen", 500, INVALID),
                                  ("src_row_stride", 2000, INVALID), ("dst", A + 8, ALIGN),
                                  ("unpack_flags", 4, UNSUPPORTED), ("in_dtype", 5, UNSUPPORTED),
-                                 ("flags", 2, UNSUPPORTED)):
+                                 ("flags", 4, UNSUPPORTED)):
         saved = getattr(d, field)
         setattr(d, field, value)
         assert lib.rag_pipeline_create(ctypes.byref(d), ctypes.byref(h)) == status, field
         assert h.value is None
         setattr(d, field, saved)
+    # the direct forms capture nothing, so creating them runs no HIP call
+    for flags in (binding.RAG_PIPELINE_DIRECT, binding.RAG_PIPELINE_DIRECT | binding.RAG_PIPELINE_FUSED):
+        d.flags = flags
+        assert lib.rag_pipeline_create(ctypes.byref(d), ctypes.byref(h)) == OK, flags
+        assert h.value is not None
+        lib.rag_pipeline_destroy(h)
+        h = ctypes.c_void_p()
+    d.flags = 0
     assert lib.rag_pipeline_launch(None, None) == INVALID
     assert lib.rag_pipeline_launch_eager(None, None) == INVALID
     lib.rag_pipeline_destroy(None)  # a no-op

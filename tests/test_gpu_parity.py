@@ -410,6 +410,38 @@ def test_fused_graph_pipeline_replays_the_one_launch_pass(flags):
     pipe.close()
 
 
+@pytest.mark.parametrize("fused", [False, True])
+def test_direct_pipeline_launch_is_the_pass(fused):
+    """With RAG_PIPELINE_DIRECT no graph is captured and rag_pipeline_launch
+    enqueues the pass's direct launches: the three stages, or with
+    RAG_PIPELINE_FUSED the one gathered launch (which leaves the packed
+    buffers, offsets and gather index untouched).  Every launch writes dst as
+    the eager three-stage pass does, bit for bit."""
+    w = wl.custom(B=6, N=197, H=6, lengths=[0, 197, 1, 40, 64, 40], seed=23)
+    bufs = _pipeline_buffers(w, torch.bfloat16)
+    staged_pipe = _make_pipeline(w, bufs)
+    staged_pipe.launch_eager()
+    torch.cuda.synchronize()
+    staged = bufs["dst"].clone()
+    staged_pipe.close()
+    bufs = _pipeline_buffers(w, torch.bfloat16)
+    pipe = binding.Pipeline(bufs["keep"], bufs["src"], bufs["packed"], bufs["cu"], bufs["gather"],
+                            bufs["o_packed"], bufs["dst"], H=w.H, scale=w.scale,
+                            fused_graph=fused, direct=True)
+    for rep in range(3):
+        bufs["dst"].view(torch.uint8).fill_(SENTINEL_BYTE)
+        torch.cuda.synchronize()
+        pipe.launch()
+        torch.cuda.synchronize()
+        assert torch.equal(bufs["dst"].view(torch.uint8), staged.view(torch.uint8)), rep
+        if fused:
+            for k in ("packed", "cu", "gather", "o_packed"):
+                assert (bufs[k].view(torch.uint8) == SENTINEL_BYTE).all(), (rep, k)
+    res = pipe.measure_dispatch(warmup=3, iters=10)
+    assert res["graph_roundtrip"]["p50"] > 0
+    pipe.close()
+
+
 def test_attn_plan_equals_the_call():
     """binding.AttnPlan prepares a rag_attn call once; calling it gives the
     call's output bit for bit (on torch's current stream and on another)."""
