@@ -40,6 +40,7 @@
 //     operands).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "rag_device.h"
@@ -57,6 +58,15 @@ constexpr int kD = 64;         // head dimension
 constexpr int kBM = 64;        // query rows per workgroup
 constexpr int kBN = 64;        // keys per LDS tile
 constexpr int kThreads = 256;  // 4 waves x 16 query rows
+constexpr int64_t kGridRow = 1 << 20;
+// Tile kernel, grid launches: an XCD takes its (head, image) pairs kPairBlock
+// at a time, every q-tile of the block before the next block.  1 puts a
+// pair's q-tiles back to back (they then read the same K / V lines at the
+// same moment); all of the XCD's pairs at once is a q-tile-slowest order,
+// whose reuse distance lets Q and O streams evict the pairs' K / V from L2
+// (N = 577: 1.33x the algorithmic bytes fetched).  4 fetches the algorithmic
+// bytes and measured fastest of 1, 4, 16 and all.
+constexpr int kPairBlock = 4;  // workgroups per grid row of the tile kernel (multiple of 8)
 
 // Where the rows of one image live.
 enum Layout : int {
@@ -507,13 +517,28 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
     __shared__ int s_wsum[16];  // keep ranking: up to 4 planes x 4 waves
 
     // ---- which (head, image, query blocks): TILES, the tile list's item (four
-    // query blocks at most); otherwise a 3-D grid (head, image, q-tile of four
-    // blocks) with the q-tile slowest, so that the first q-tile of every
-    // (image, head) -- the only one most pruned sequences have -- is dispatched
-    // before any tile that will exit at once.
-    int h = blockIdx.x;
-    int b = blockIdx.y;
-    const int qt = blockIdx.z;
+    // query blocks at most); otherwise a grid of (pair, q-tile of four blocks)
+    // slots, pair = (head, image), laid out for the XCDs: workgroup i runs on
+    // XCD i % 8 as that XCD's (i / 8)-th; pairs are dealt round-robin to the
+    // XCDs and each XCD runs the q-tiles of kPairBlock of its pairs before the
+    // next kPairBlock, so every q-tile after a pair's first finds the pair's
+    // K and V in that XCD's L2 instead of fetching them again.  Slots past the
+    // last pair exit at once.
+    // (The grid is (X, Y) with X a multiple of 8, so that the linear id below
+    // is the dispatch order and id % 8 the XCD however large the launch.)
+    int h, b, qt;
+    if constexpr (!TILES) {
+        const int64_t id = blockIdx.x + (int64_t)gridDim.x * blockIdx.y;
+        const int xcd = (int)(id & 7);
+        const int64_t k = id >> 3;
+        const int64_t per_blk = (int64_t)kPairBlock * p.n_qtiles;
+        const int64_t blk = k / per_blk, r = k - blk * per_blk;
+        qt = (int)(r / kPairBlock);
+        const int64_t pair = xcd + 8 * (blk * kPairBlock + r % kPairBlock);
+        if (pair >= (int64_t)p.H * p.B) return;  // uniform over the workgroup
+        h = (int)(pair % p.H);
+        b = (int)(pair / p.H);
+    }
 
     int64_t row0;
     int L, qlo, qhi;
@@ -1002,7 +1027,12 @@ void launch_variant(const AttnParams& p, int layout, hipStream_t st)
         hipLaunchKernelGGL((attn_kernel<IN_F32, OUT_F32, kRagged, true>), grid, block, 0, st, p);
         return;
     }
-    const dim3 grid(p.H, p.B, p.n_qtiles), block(kThreads);
+    // one slot per (pair, q-tile), pairs rounded up to a multiple of the 8 XCDs,
+    // folded into rows of kGridRow slots
+    const int64_t per_xcd = ((int64_t)p.H * p.B + 7) / 8;
+    const int64_t slots = 8 * ((per_xcd + kPairBlock - 1) / kPairBlock * kPairBlock) * p.n_qtiles;
+    const dim3 grid((unsigned)std::min<int64_t>(slots, kGridRow),
+                    (unsigned)((slots + kGridRow - 1) / kGridRow)), block(kThreads);
     if (layout == kPadded)
         hipLaunchKernelGGL((attn_kernel<IN_F32, OUT_F32, kPadded, false>), grid, block, 0, st, p);
     else if (layout == kGathered)
