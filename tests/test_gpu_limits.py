@@ -116,3 +116,30 @@ def test_most_images():
     assert (gz[gather_ref].view(np.uint8) == as_numpy_rows(o32)[:T].view(np.uint8)).all()
     pz = _padded(w, torch.float32).cpu().numpy().astype(np.float64)
     assert np.abs(pz[gather_ref] - want).max() <= ATOL
+
+
+def test_tile_kernel_grid_over_several_rows():
+    """fp32 input takes the 64-key tile kernel, whose slots ((image, head) pair,
+    q-tile) are folded into grid rows of 2^20: B = 65535 images of H = 17 heads
+    give 1 114 095 pairs, more than one row.  Every row of the output matches
+    the oracle; the gathered and padded layouts (the same kernel) agree."""
+    rng = np.random.default_rng(33)
+    w = wl.custom(B=RAG_MAX_B, N=2, H=17, lengths=rng.integers(0, 3, size=RAG_MAX_B), dtype="f32",
+                  seed=33)
+    print("B", w.B, "H", w.H, "T", w.T, flush=True)
+    assert w.B * w.H > (1 << 20)
+    g = gpu_pack(w)
+    packed_ref, cu_ref, gather_ref = oracle.pack(w.keep, wl.rows(w))
+    o32 = gpu_attn(g["packed"], g["cu"], w, torch.float32, max_seqlen=2)
+    q, k, v = wl.split_qkv(packed_ref, w.C)
+    want = oracle.attn(q, k, v, cu_ref, w.H, w.d, w.scale)
+    T = w.T
+    out = o32.cpu().numpy()
+    err = np.abs(out[:T].astype(np.float64) - want).max()
+    print("max abs err", err, flush=True)
+    assert err <= ATOL
+    assert (out[T:].view(np.uint32) == np.uint32(SENTINEL_BYTE * 0x01010101)).all()
+    gz = as_numpy_rows(_gathered(w, torch.float32))
+    assert (gz[gather_ref].view(np.uint8) == as_numpy_rows(o32)[:T].view(np.uint8)).all()
+    pz = _padded(w, torch.float32).cpu().numpy().astype(np.float64)
+    assert np.abs(pz[gather_ref] - want).max() <= ATOL
