@@ -125,9 +125,11 @@ int main()
     EXPECT(validate_pipeline(&e), ALI, "dst");
     e = d; e.unpack_flags = 4;
     EXPECT(validate_pipeline(&e), UNS, "flags");
-    e = d; e.flags = 2;
+    e = d; e.flags = 4;
     EXPECT(validate_pipeline(&e), UNS, "pipeline flags");
     e = d; e.flags = RAG_PIPELINE_FUSED;
+    EXPECT(validate_pipeline(&e), OK, nullptr);
+    e = d; e.flags = RAG_PIPELINE_DIRECT | RAG_PIPELINE_FUSED;
     EXPECT(validate_pipeline(&e), OK, nullptr);
     // ---- encoder block
     rag_block_desc b;
