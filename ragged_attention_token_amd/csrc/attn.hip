@@ -87,6 +87,7 @@ struct AttnParams {
     int32_t lds_rows;        // LDS-resident kernel: K / V rows held, max_len rounded up to 32
     int32_t tl_kt;           // tile-list launch: key tiles of the longest image (else 0)
     float scale_log2;        // scale * log2(e)
+    int32_t natural_first;   // gathered layout: request K/V in natural order beside the keep bytes
 };
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c)
@@ -740,6 +741,72 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
     }
 }
 
+// ---- loads the compiler does not track ------------------------------------
+//
+// The gathered layout's speculative path issues its keep-byte loads and
+// LDS-writing K/V loads as inline assembly and waits for them with explicit
+// counts: the compiler's own waits would make the keep ranking wait for the
+// K/V loads (it cannot tell that LDS-writing loads and the ranking's LDS
+// words do not overlap).  Loads complete in issue order.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// The four words of the raw buffer resource over [base, base + bytes) that
+// make_rsrc builds.
+__device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes)
+{
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    return i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xFFFFu), (int)bytes, (int)dev::kRsrcWord3};
+}
+
+// One byte at offset off of the resource, zero-extended.  The result register
+// is written when the load completes: read it only after a wait_vm() that
+// covers the load and a vm_done() on it.
+__device__ __forceinline__ uint32_t ld_u8_untracked(i32x4 r, uint32_t off)
+{
+    uint32_t x;
+    asm volatile("buffer_load_ubyte %0, %1, %2, 0 offen" : "=v"(x) : "v"(off), "s"(r));
+    return x;
+}
+
+// Sixteen bytes per lane at offset voff of the resource into LDS at lds_addr
+// + 16 lane (lds_addr wave-uniform).  The LDS base goes in through M0 as an
+// input operand; the s_nop gives the M0 write the wait state the load needs.
+__device__ __forceinline__ void ld_lds16_untracked(i32x4 r, uint32_t lds_addr, uint32_t voff)
+{
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(r), "{m0}"(lds_addr));
+}
+
+// Waits until at most n (wave-uniform, even, >= 0) of this wave's
+// vector-memory operations are outstanding; an n above 14 waits for 14.
+__device__ __forceinline__ void wait_vm(int n)
+{
+    const int u = __builtin_amdgcn_readfirstlane(n);
+    asm volatile(
+        "s_cmp_lt_u32 %0, 2\n\ts_cbranch_scc1 0f\n\t"
+        "s_cmp_lt_u32 %0, 4\n\ts_cbranch_scc1 2f\n\t"
+        "s_cmp_lt_u32 %0, 6\n\ts_cbranch_scc1 4f\n\t"
+        "s_cmp_lt_u32 %0, 8\n\ts_cbranch_scc1 6f\n\t"
+        "s_cmp_lt_u32 %0, 10\n\ts_cbranch_scc1 8f\n\t"
+        "s_cmp_lt_u32 %0, 12\n\ts_cbranch_scc1 10f\n\t"
+        "s_cmp_lt_u32 %0, 14\n\ts_cbranch_scc1 12f\n\t"
+        "s_waitcnt vmcnt(14)\n\ts_branch 1f\n"
+        "12:\n\ts_waitcnt vmcnt(12)\n\ts_branch 1f\n"
+        "10:\n\ts_waitcnt vmcnt(10)\n\ts_branch 1f\n"
+        "8:\n\ts_waitcnt vmcnt(8)\n\ts_branch 1f\n"
+        "6:\n\ts_waitcnt vmcnt(6)\n\ts_branch 1f\n"
+        "4:\n\ts_waitcnt vmcnt(4)\n\ts_branch 1f\n"
+        "2:\n\ts_waitcnt vmcnt(2)\n\ts_branch 1f\n"
+        "0:\n\ts_waitcnt vmcnt(0)\n"
+        "1:"
+        :
+        : "s"(u)
+        : "memory", "scc");
+}
+
+// Marks x as produced after the preceding volatile statements (a wait_vm), so
+// that no read of it is scheduled before them.
+__device__ __forceinline__ void vm_done(uint32_t& x) { asm volatile("" : "+v"(x)); }
+
 // ---- LDS-resident kernel (bf16 input, sequences of up to kLdsMaxRows keys) --
 //
 // One workgroup = one (head, image, query split) with W = blockDim.x / 64
@@ -758,8 +825,9 @@ constexpr int kMaxWaves = 16;         // 16 query blocks: every block of kLdsMax
 constexpr int kLdsMaxRows = 256;      // 64 KiB of K + V: two workgroups per CU
 
 // TL: 0 = grid of (head, image, query split); tile list of 1 = whole pairs,
-// 2 = 64-row query tiles.
-template <bool OUT_F32, int LAYOUT, bool MULTI, int TL>
+// 2 = 64-row query tiles.  NAT (gathered layout, few pairs): K and V are
+// requested in natural order beside the keep bytes (see the gathered setup).
+template <bool OUT_F32, int LAYOUT, bool MULTI, int TL, bool NAT = false>
 __global__ __launch_bounds__(64 * kMaxWaves) void attn_lds_kernel(AttnParams p)
 {
     constexpr bool PADDED = LAYOUT == kPadded;
@@ -786,6 +854,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void attn_lds_kernel(AttnParams p)
 
     int64_t row0;
     int L, qlo = qs * nw, qhi;  // this workgroup's query blocks: qlo + wave (+ k * qstride) < qhi
+    bool natural = false;       // NAT: K, V and the wave's Q rows are already requested (every row kept)
+    bf16x8 qa0 = {}, qa1 = {};  // the wave's Q^T operand (see load_q)
     if constexpr (TILES) {
         Item it;
         if (!workgroup_item<TL == 1>(p, it)) return;  // uniform over the workgroup
@@ -802,8 +872,71 @@ __global__ __launch_bounds__(64 * kMaxWaves) void attn_lds_kernel(AttnParams p)
         for (int n = tid; n < nkeep; n += blockDim.x) s_keep[n] = n < p.N ? p.keep[row0 + n] : 0;
     } else if constexpr (GATHERED) {
         row0 = (int64_t)b * p.N;
-        L = p.N <= 4 * 64 * nw ? dev::rank_kept_planes<4>(p.keep + row0, p.N, s_pos, s_wsum, nw)
-                               : dev::rank_kept_waves(p.keep + row0, p.N, s_pos, s_wsum, nw);
+        // NAT (few pairs, and a bound max_seqlen >= N that admits an
+        // unpruned image; the host checks N <= 4 * 64 * waves): the image's K
+        // and V rows are requested in natural order beside its keep bytes,
+        // and kept if every row is kept, one memory round trip instead of the
+        // keep bytes' and then the gathered rows'.  Otherwise the gathered
+        // loads below overwrite them (loads complete in issue order).  With
+        // many pairs the extra traffic costs more than the round trip saves.
+        if constexpr (NAT) {
+            const int nt = 64 * nw;
+            const i32x4 rkeep = rsrc_words(p.keep + row0, (uint32_t)p.N);
+            uint32_t kb[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) kb[k] = ld_u8_untracked(rkeep, (uint32_t)(tid + k * nt));
+            const int64_t hoff0 = (int64_t)h * kD;
+            const uint32_t ksb0 = (uint32_t)(p.ks * 2), vsb0 = (uint32_t)(p.vs * 2);
+            const i32x4 rkw = rsrc_words(static_cast<const char*>(p.k) + (row0 * p.ks + hoff0) * 2,
+                                         (uint32_t)(p.N - 1) * ksb0 + kRowBytes);
+            const i32x4 rvw = rsrc_words(static_cast<const char*>(p.v) + (row0 * p.vs + hoff0) * 2,
+                                         (uint32_t)(p.N - 1) * vsb0 + kRowBytes);
+            const int nrb = ((p.N + kLdsRowAlign - 1) & ~(kLdsRowAlign - 1)) >> 3;
+            const int lr = lane >> 3, slot = lane & 7;
+            const uint32_t c16e = 16u * (uint32_t)(slot ^ swz(lr)), c16o = 16u * (uint32_t)(slot ^ swz(8 + lr));
+            int issued = 0;
+            for (int j = wave; j < nrb; j += nw) {
+                const uint32_t c16 = (j & 1) ? c16o : c16e;
+                const uint32_t row = (uint32_t)(8 * j + lr);
+                ld_lds16_untracked(rkw, (uint32_t)(uintptr_t)(sK + 1024 * j), row * ksb0 + c16);
+                ld_lds16_untracked(rvw, (uint32_t)(uintptr_t)(sV + 1024 * j), row * vsb0 + c16);
+                issued += 2;
+            }
+            // the wave's first query block, as load_q would read it with every
+            // row kept (rows past N read as zeros, as dropped rows do there)
+            if (qlo + wave < (p.N + 15) >> 4) {
+                const uint32_t qsb0 = (uint32_t)(p.qs * 2);
+                const auto rq0 = make_rsrc(static_cast<const char*>(p.q) + (row0 * p.qs + hoff0) * 2,
+                                           (uint32_t)(p.N - 1) * qsb0 + kRowBytes);
+                const uint32_t off = (uint32_t)(16 * (qlo + wave) + r16) * qsb0 + 16 * g;
+                qa0 = __builtin_bit_cast(bf16x8, ld16(rq0, off));
+                qa1 = __builtin_bit_cast(bf16x8, ld16(rq0, off + 64));
+                issued += 2;
+            }
+            wait_vm(issued);  // the keep bytes, issued first, have landed
+            bool dropped = false;  // a position < N of this thread is dropped
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                vm_done(kb[k]);
+                dropped = dropped || (tid + k * nt < p.N && kb[k] == 0u);
+            }
+            // every row kept: one barrier decides it, and no ranking is needed
+            // (the rows are in natural order); else rank as below
+            const bool wave_dropped = __ballot(dropped) != 0ull;  // (all lanes take part)
+            if (lane == 0) s_wsum[wave] = wave_dropped;
+            __syncthreads();
+            natural = true;
+            for (int w = 0; w < nw; ++w) natural = natural && s_wsum[w] == 0;
+            if (!natural) {
+                __syncthreads();  // every wave has read s_wsum before the ranking rewrites it
+                L = dev::rank_kept_planes_loaded<4>(kb, s_pos, s_wsum, nw);
+            } else {
+                L = p.N;
+            }
+        } else {
+            L = p.N <= 4 * 64 * nw ? dev::rank_kept_planes<4>(p.keep + row0, p.N, s_pos, s_wsum, nw)
+                                   : dev::rank_kept_waves(p.keep + row0, p.N, s_pos, s_wsum, nw);
+        }
         L = min(L, p.max_len);
         if (p.zero_dropped && qs == 0) zero_dropped_head<OUT_F32>(p, row0, h);
     } else {
@@ -826,8 +959,12 @@ __global__ __launch_bounds__(64 * kMaxWaves) void attn_lds_kernel(AttnParams p)
     const auto rv = make_rsrc(static_cast<const char*>(p.v) + (row0 * p.vs + hoff) * 2,
                               (uint32_t)(span - 1) * vsb + kRowBytes);
     auto row_off = [&](int r, uint32_t stride) -> uint32_t {
-        if constexpr (GATHERED) return r < L ? (uint32_t)s_pos[r] * stride : kDropOffset;
-        else return (uint32_t)r * stride;
+        if constexpr (GATHERED) {
+            if (NAT && natural) return r < L ? (uint32_t)r * stride : kDropOffset;  // rank r is row r
+            return r < L ? (uint32_t)s_pos[r] * stride : kDropOffset;
+        } else {
+            return (uint32_t)r * stride;
+        }
     };
 
     // ---- K, V -> LDS: one instruction moves 8 rows (1 KiB); lane l writes
@@ -836,7 +973,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void attn_lds_kernel(AttnParams p)
     // (the permutation repeats every 16 rows: one lane offset per row parity
     // of the 8-row block).  Rows past the sequence, up to the multiple of 32,
     // read as zeros.
-    {
+    if (!NAT || !natural) {
         const int nrb = ((L + kLdsRowAlign - 1) & ~(kLdsRowAlign - 1)) >> 3;
         const int lr = lane >> 3, slot = lane & 7;
         const uint32_t c16e = 16u * (uint32_t)(slot ^ swz(lr)), c16o = 16u * (uint32_t)(slot ^ swz(8 + lr));
@@ -856,13 +993,12 @@ __global__ __launch_bounds__(64 * kMaxWaves) void attn_lds_kernel(AttnParams p)
     // qs * W + wave + k * gridDim.z * W: one of them, or (MULTI) one or more.
     int qb = qlo + wave;
     const int qstride = gridDim.z * nw;
-    bf16x8 qa0, qa1;
     auto load_q = [&](int blk) {
         const uint32_t off = row_off(16 * blk + r16, qsb) + 16 * g;
         qa0 = __builtin_bit_cast(bf16x8, ld16(rq, off));
         qa1 = __builtin_bit_cast(bf16x8, ld16(rq, off + 64));
     };
-    if (qb < qhi) load_q(qb);
+    if (qb < qhi && !(NAT && natural)) load_q(qb);
     __builtin_amdgcn_s_waitcnt(0);  // every load of this wave has landed (LDS included)
     __syncthreads();
     if (qb >= qhi) return;
@@ -979,6 +1115,8 @@ void launch_lds_layout(const AttnParams& p, int layout, dim3 grid, dim3 block, s
 {
     if (layout == kPadded)
         hipLaunchKernelGGL((attn_lds_kernel<OUT_F32, kPadded, MULTI, 0>), grid, block, lds_bytes, st, p);
+    else if (layout == kGathered && !MULTI && p.natural_first && p.N <= 4 * (int)block.x)
+        hipLaunchKernelGGL((attn_lds_kernel<OUT_F32, kGathered, false, 0, true>), grid, block, lds_bytes, st, p);
     else if (layout == kGathered)
         hipLaunchKernelGGL((attn_lds_kernel<OUT_F32, kGathered, MULTI, 0>), grid, block, lds_bytes, st, p);
     else if (p.tl_kt == 0)
@@ -1071,6 +1209,7 @@ int launch_attn(const void* q, const void* k, const void* v, int64_t q_row_strid
     p.zero_dropped = (flags & RAG_UNPACK_ZERO_DROPPED) ? 1 : 0;
     p.lds_rows = 0;
     p.tl_kt = (layout == kRagged && (flags & kAttnTileList)) ? (p.max_len + 63) / 64 : 0;
+    p.natural_first = (layout == kGathered && max_seqlen >= N && (int64_t)B * H < 256) ? 1 : 0;
     p.scale_log2 = scale * 1.4426950408889634f;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool in_f32 = in_dtype == RAG_DTYPE_F32, out_f32 = out_dtype == RAG_DTYPE_F32;

@@ -84,21 +84,15 @@ __device__ __forceinline__ int rank_kept_preloaded(bool kept, int* pos, int* wsu
     return total;
 }
 
-// rank_kept_waves for rows of at most KMAX * 64 * nw positions, with every
-// keep byte requested before the first barrier (one memory round trip):
-// thread t of the workgroup covers positions t + k * 64 nw for k < KMAX, read
-// through a buffer resource over the row (positions past N read as zero).
-// Positions are ranked plane by plane (plane k = [k 64 nw, (k+1) 64 nw)),
-// which is ascending order.  wsum holds KMAX * nw ints.
+// rank_kept_waves for rows of at most KMAX * 64 * nw positions whose keep
+// bytes are already in registers: thread t of the workgroup holds kb[k], the
+// byte of position t + k * 64 nw (0 past N).  Positions are ranked plane by
+// plane (plane k = [k 64 nw, (k+1) 64 nw)), which is ascending order.  wsum
+// holds KMAX * nw ints.
 template <int KMAX>
-__device__ __forceinline__ int rank_kept_planes(const uint8_t* krow, int N, int* pos, int* wsum,
-                                                int nw)
+__device__ __forceinline__ int rank_kept_planes_loaded(const uint32_t (&kb)[KMAX], int* pos, int* wsum, int nw)
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nt = 64 * nw;
-    const auto rk = make_rsrc(krow, (uint32_t)N);
-    uint32_t kb[KMAX];
-#pragma unroll
-    for (int k = 0; k < KMAX; ++k) kb[k] = __builtin_amdgcn_raw_buffer_load_b8(rk, (uint32_t)(tid + k * nt), 0, 0);
     int below[KMAX];
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
@@ -121,6 +115,21 @@ __device__ __forceinline__ int rank_kept_planes(const uint8_t* krow, int N, int*
     }
     __syncthreads();
     return total;
+}
+
+// rank_kept_planes_loaded with every keep byte requested before the first
+// barrier (one memory round trip), read through a buffer resource over the
+// row (positions past N read as zero).
+template <int KMAX>
+__device__ __forceinline__ int rank_kept_planes(const uint8_t* krow, int N, int* pos, int* wsum,
+                                                int nw)
+{
+    const int tid = threadIdx.x, nt = 64 * nw;
+    const auto rk = make_rsrc(krow, (uint32_t)N);
+    uint32_t kb[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) kb[k] = __builtin_amdgcn_raw_buffer_load_b8(rk, (uint32_t)(tid + k * nt), 0, 0);
+    return rank_kept_planes_loaded<KMAX>(kb, pos, wsum, nw);
 }
 
 // rank_kept_waves for a 256-thread workgroup (wsum holds 4 ints).

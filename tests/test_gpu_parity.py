@@ -316,7 +316,7 @@ def _gathered(w, out_dtype, flags=0):
     return o
 
 
-@pytest.mark.parametrize("name", ["tiny", "deits_b4_p800", "deitb_ragged_b64", "empty_and_full",
+@pytest.mark.parametrize("name", ["tiny", "deits_b4_p800", "deitb_ragged_b64", "empty_and_full", "deits_b1_p000",
                                   "n1", "tile_edges", "n577_two", "f32_odd", "n5_golden_like"])
 def test_gathered_equals_three_stage_pipeline_and_oracle(name):
     w = FULL[name]()
@@ -334,6 +334,41 @@ def test_gathered_equals_three_stage_pipeline_and_oracle(name):
         assert (fz[gather_ref].view(np.uint8) == sz[:T].view(np.uint8)).all()
         dropped = np.setdiff1d(np.arange(w.B * w.N), gather_ref)
         assert (fz[dropped].view(np.uint8) == SENTINEL_BYTE).all()
+    got = as_numpy_rows(_gathered(w, torch.float32)).astype(np.float64)
+    for b, want in _oracle_attn_images(w, ref, range(w.B)).items():
+        s_, e_ = int(cu_ref[b]), int(cu_ref[b + 1])
+        assert np.abs(got[gather_ref[s_:e_]] - want).max() <= ATOL, b
+
+
+def test_gathered_unpruned_images_and_single_dropped_rows():
+    """Few (image, head) pairs with max_seqlen = N: the one-launch pass requests
+    K, V and Q in natural order beside the keep bytes and keeps them only when
+    every row of the image is kept.  Images with all rows kept, or one dropped
+    row at a position read by lane 0 of a wave (64, 128), by other lanes (1,
+    100) or at the end (196), or a kept prefix, must all equal the three-stage
+    result bit for bit and leave the dropped rows untouched."""
+    N, H = 197, 2
+    masks = [np.ones(N, np.uint8)]
+    for drop in (1, 64, 100, 128, 196):
+        m = np.ones(N, np.uint8)
+        m[drop] = 0
+        masks.append(m)
+    prefix = np.zeros(N, np.uint8)
+    prefix[:150] = 1
+    masks += [prefix, np.ones(N, np.uint8)]
+    B = len(masks)
+    w = wl.custom(B=B, N=N, H=H, lengths=[int(m.sum()) for m in masks], keep_kind="prefix", seed=24)
+    w.keep = np.stack(masks).astype(np.uint8)
+    print("case natural-order gathered B", B, "N", N, "H", H, flush=True)
+    ref = _oracle_pack(w)
+    _, cu_ref, gather_ref = ref
+    g = gpu_pack(w)
+    for out_dtype in (torch.float32, torch.bfloat16):
+        staged = as_numpy_rows(gpu_attn(g["packed"], g["cu"], w, out_dtype))
+        fused = as_numpy_rows(_gathered(w, out_dtype))
+        assert (fused[gather_ref].view(np.uint8) == staged[:w.T].view(np.uint8)).all()
+        dropped = np.setdiff1d(np.arange(w.B * w.N), gather_ref)
+        assert (fused[dropped].view(np.uint8) == SENTINEL_BYTE).all()
     got = as_numpy_rows(_gathered(w, torch.float32)).astype(np.float64)
     for b, want in _oracle_attn_images(w, ref, range(w.B)).items():
         s_, e_ = int(cu_ref[b]), int(cu_ref[b + 1])
