@@ -1129,6 +1129,19 @@ void launch_lds_layout(const AttnParams& p, int layout, dim3 grid, dim3 block, s
                            dim3(tile_list_grid(p.B, p.H, p.tl_kt, false)), block, lds_bytes, st, p);
 }
 
+// Compute units of the current device (cached per device; 0 if the query fails).
+int device_cus()
+{
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+    if (dev < 64 && cached[dev] > 0) return cached[dev];
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (dev < 64) cached[dev] = n;
+    return n;
+}
+
 template <bool OUT_F32>
 void launch_lds_variant(AttnParams p, int layout, size_t lds_bytes, hipStream_t st)
 {
@@ -1139,15 +1152,24 @@ void launch_lds_variant(AttnParams p, int layout, size_t lds_bytes, hipStream_t 
     // gridDim.z workgroups of at most 4 waves, one block each, so that more CUs
     // share the work.  A tile-list launch (p.tl_kt > 0, ragged layout) keeps
     // these workgroup shapes, its items being the whole pairs, or the 64-row
-    // query tiles (4 blocks on 4 waves) with few pairs.
+    // query tiles (4 blocks on 4 waves) with few pairs.  Ragged launches with
+    // fewer than four pairs per CU split images of more than 8 blocks in two
+    // workgroups of one block per wave: the last long images then end sooner
+    // (DeiT-B with ragged lengths in [20, 197]: 5% less time; more splits or
+    // the gathered and padded layouts, which rank or mask the keep row in
+    // every workgroup, measured slower).
     const int nqb = (p.max_len + 15) / 16;
-    const bool many = (int64_t)p.B * p.H >= 256;
+    const int64_t npairs = (int64_t)p.B * p.H;
+    const bool many = npairs >= 256;
+    const bool halves = layout == kRagged && p.tl_kt == 0 && many && nqb > 8 && npairs < 4 * (int64_t)device_cus();
     int waves;
-    if (many)  // one block per wave up to 8, else two
+    if (halves)
+        waves = (nqb + 1) / 2;
+    else if (many)  // one block per wave up to 8, else two
         waves = nqb <= 8 ? nqb : (nqb + 1) / 2;
     else
         waves = min(nqb, 4);
-    const int splits = many ? 1 : (nqb + waves - 1) / waves;
+    const int splits = halves ? 2 : many ? 1 : (nqb + waves - 1) / waves;
     p.lds_rows = (p.max_len + kLdsRowAlign - 1) & ~(kLdsRowAlign - 1);
     if (p.tl_kt > 0 && !many) waves = 4;
     const dim3 grid(p.H, p.B, splits), block(64 * waves);
