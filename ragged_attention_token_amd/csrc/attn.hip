@@ -747,7 +747,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
 // LDS-writing K/V loads as inline assembly and waits for them with explicit
 // counts: the compiler's own waits would make the keep ranking wait for the
 // K/V loads (it cannot tell that LDS-writing loads and the ranking's LDS
-// words do not overlap).  Loads complete in issue order.
+// words do not overlap).  A wave's loads complete in issue order, which the
+// count-based wait for the keep bytes (issued first) relies on.
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // The four words of the raw buffer resource over [base, base + bytes) that
@@ -877,8 +878,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void attn_lds_kernel(AttnParams p)
         // and V rows are requested in natural order beside its keep bytes,
         // and kept if every row is kept, one memory round trip instead of the
         // keep bytes' and then the gathered rows'.  Otherwise the gathered
-        // loads below overwrite them (loads complete in issue order).  With
-        // many pairs the extra traffic costs more than the round trip saves.
+        // loads below overwrite them.  With many pairs the extra traffic
+        // costs more than the round trip saves.
         if constexpr (NAT) {
             const int nt = 64 * nw;
             const i32x4 rkeep = rsrc_words(p.keep + row0, (uint32_t)p.N);
@@ -974,6 +975,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void attn_lds_kernel(AttnParams p)
     // of the 8-row block).  Rows past the sequence, up to the multiple of 32,
     // read as zeros.
     if (!NAT || !natural) {
+        // (NAT: the natural-order loads into the same LDS rows have landed
+        // first; by now they have, so the wait costs nothing)
+        if constexpr (NAT) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         const int nrb = ((L + kLdsRowAlign - 1) & ~(kLdsRowAlign - 1)) >> 3;
         const int lr = lane >> 3, slot = lane & 7;
         const uint32_t c16e = 16u * (uint32_t)(slot ^ swz(lr)), c16o = 16u * (uint32_t)(slot ^ swz(8 + lr));
