@@ -498,6 +498,73 @@ __device__ __forceinline__ uint32_t v_operand_offset(int r16, int g, int db)
     return 128u * vrow + 16u * (uint32_t)((2 * db + ((r16 & 3) >> 1)) ^ swz(vrow)) + 8u * (r16 & 1);
 }
 
+// ---- loads the compiler does not track ------------------------------------
+//
+// The tile kernel's K/V loads into LDS and the gathered layout's speculative
+// loads are inline assembly, waited for with explicit counts: the compiler
+// cannot tell that LDS-writing loads and the LDS words read meanwhile (the
+// current K/V tile, the keep ranking's words) do not overlap, and its own
+// waits would serialise them.  A wave's loads complete in issue order, which
+// the count-based wait for the keep bytes (issued first) relies on.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// The four words of the raw buffer resource over [base, base + bytes) that
+// make_rsrc builds.
+__device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes)
+{
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    return i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xFFFFu), (int)bytes, (int)dev::kRsrcWord3};
+}
+
+// One byte at offset off of the resource, zero-extended.  The result register
+// is written when the load completes: read it only after a wait_vm() that
+// covers the load and a vm_done() on it.
+__device__ __forceinline__ uint32_t ld_u8_untracked(i32x4 r, uint32_t off)
+{
+    uint32_t x;
+    asm volatile("buffer_load_ubyte %0, %1, %2, 0 offen" : "=v"(x) : "v"(off), "s"(r));
+    return x;
+}
+
+// Sixteen bytes per lane at offset voff of the resource into LDS at lds_addr
+// + 16 lane (lds_addr wave-uniform).  The LDS base goes in through M0 as an
+// input operand; the s_nop gives the M0 write the wait state the load needs.
+__device__ __forceinline__ void ld_lds16_untracked(i32x4 r, uint32_t lds_addr, uint32_t voff)
+{
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(r), "{m0}"(lds_addr));
+}
+
+// Waits until at most n (wave-uniform, even, >= 0) of this wave's
+// vector-memory operations are outstanding; an n above 14 waits for 14.
+__device__ __forceinline__ void wait_vm(int n)
+{
+    const int u = __builtin_amdgcn_readfirstlane(n);
+    asm volatile(
+        "s_cmp_lt_u32 %0, 2\n\ts_cbranch_scc1 0f\n\t"
+        "s_cmp_lt_u32 %0, 4\n\ts_cbranch_scc1 2f\n\t"
+        "s_cmp_lt_u32 %0, 6\n\ts_cbranch_scc1 4f\n\t"
+        "s_cmp_lt_u32 %0, 8\n\ts_cbranch_scc1 6f\n\t"
+        "s_cmp_lt_u32 %0, 10\n\ts_cbranch_scc1 8f\n\t"
+        "s_cmp_lt_u32 %0, 12\n\ts_cbranch_scc1 10f\n\t"
+        "s_cmp_lt_u32 %0, 14\n\ts_cbranch_scc1 12f\n\t"
+        "s_waitcnt vmcnt(14)\n\ts_branch 1f\n"
+        "12:\n\ts_waitcnt vmcnt(12)\n\ts_branch 1f\n"
+        "10:\n\ts_waitcnt vmcnt(10)\n\ts_branch 1f\n"
+        "8:\n\ts_waitcnt vmcnt(8)\n\ts_branch 1f\n"
+        "6:\n\ts_waitcnt vmcnt(6)\n\ts_branch 1f\n"
+        "4:\n\ts_waitcnt vmcnt(4)\n\ts_branch 1f\n"
+        "2:\n\ts_waitcnt vmcnt(2)\n\ts_branch 1f\n"
+        "0:\n\ts_waitcnt vmcnt(0)\n"
+        "1:"
+        :
+        : "s"(u)
+        : "memory", "scc");
+}
+
+// Marks x as produced after the preceding volatile statements (a wait_vm), so
+// that no read of it is scheduled before them.
+__device__ __forceinline__ void vm_done(uint32_t& x) { asm volatile("" : "+v"(x)); }
+
 template <bool IN_F32, bool OUT_F32, int LAYOUT, bool TILES>
 __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
 {
@@ -508,12 +575,15 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
     constexpr int OES = OUT_F32 ? 4 : 2;
     constexpr int PLANE = kBN * kRowBytes;        // one bf16 plane of a 64-key K or V tile
     constexpr int OUT_ROW = kD * OES + 16;        // bytes, padded
-    // K planes, then V planes; the output is staged in the same bytes afterwards
-    constexpr int SMEM = 2 * NP * PLANE > 4 * 16 * OUT_ROW ? 2 * NP * PLANE : 4 * 16 * OUT_ROW;
+    // fp32 input: K planes, then V planes, staged through registers; bf16
+    // input: two K/V tile buffers filled by LDS-writing loads.  The output is
+    // staged in the same bytes afterwards.
+    constexpr int KV_BYTES = IN_F32 ? 2 * NP * PLANE : 4 * PLANE;
+    constexpr int SMEM = KV_BYTES > 4 * 16 * OUT_ROW ? KV_BYTES : 4 * 16 * OUT_ROW;
     __shared__ __attribute__((aligned(16))) char smem[SMEM];
     char* sK = smem;
     char* sV = smem + NP * PLANE;
-    __shared__ uint8_t sKeep[kBN];
+    __shared__ uint8_t sKeep[2][kBN];  // padded: keep bytes of the tile in each buffer
     extern __shared__ int s_pos[];  // gathered: the image's kept positions by rank (N ints)
     __shared__ int s_wsum[16];  // keep ranking: up to 4 planes x 4 waves
 
@@ -605,64 +675,34 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
         load8<IN_F32>(rq, off, qh0, ql0);
         load8<IN_F32>(rq, off + 32 * ES, qh1, ql1);
     }
+    if constexpr (!IN_F32) {
+        // (a use of Q before the untracked K/V loads go out, so that the
+        // compiler's wait for Q covers Q alone, not the first K/V tiles)
+        asm volatile("" : "+v"(qh0), "+v"(qh1));
+    }
     const float c = fold_scale(p.scale_log2, qh0, qh1, ql0, ql1);
     Online st;
     online_init(st);
 
-    // Registers carrying one K/V tile from global memory to LDS: this thread's
-    // 16-byte chunk k_dg of key rows k_row0 and k_row1, of K and of V (hi and,
-    // for fp32 input, lo).  Eight consecutive lanes store one 128-byte LDS
-    // row, in the permuted chunk order of the operand layout.
-    bf16x8 kh0, kl0, kh1, kl1, vh0, vl0, vh1, vl1;
-    const int k_row0 = tid >> 3, k_row1 = (tid + kThreads) >> 3, k_dg = tid & 7;
-    const uint32_t so0 = 128u * k_row0 + 16u * (uint32_t)(k_dg ^ swz(k_row0));
-    const uint32_t so1 = 128u * k_row1 + 16u * (uint32_t)(k_dg ^ swz(k_row1));
-    auto fetch = [&](int kt) {
-        load8<IN_F32>(rk, row_off(kt + k_row0, ksb) + 8 * k_dg * ES, kh0, kl0);
-        load8<IN_F32>(rk, row_off(kt + k_row1, ksb) + 8 * k_dg * ES, kh1, kl1);
-        load8<IN_F32>(rv, row_off(kt + k_row0, vsb) + 8 * k_dg * ES, vh0, vl0);
-        load8<IN_F32>(rv, row_off(kt + k_row1, vsb) + 8 * k_dg * ES, vh1, vl1);
-    };
-    auto stash = [&]() {
-        *reinterpret_cast<bf16x8*>(sK + so0) = kh0;
-        *reinterpret_cast<bf16x8*>(sK + so1) = kh1;
-        *reinterpret_cast<bf16x8*>(sV + so0) = vh0;
-        *reinterpret_cast<bf16x8*>(sV + so1) = vh1;
-        if constexpr (IN_F32) {
-            *reinterpret_cast<bf16x8*>(sK + PLANE + so0) = kl0;
-            *reinterpret_cast<bf16x8*>(sK + PLANE + so1) = kl1;
-            *reinterpret_cast<bf16x8*>(sV + PLANE + so0) = vl0;
-            *reinterpret_cast<bf16x8*>(sV + PLANE + so1) = vl1;
-        }
-    };
     const uint32_t koff0 = k_operand_offset(r16, g);
     const uint32_t koff1 = koff0 ^ 64u;
     uint32_t voff[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db) voff[db] = v_operand_offset(r16, g, db);
-    fetch(0);
 
-    // Stage the tile at key kt into LDS (the next one's loads go out meanwhile),
-    // then compute it; FULL: all 64 keys present (no key-range masking).  The
-    // full tiles run in one loop and the partial last tile after it.
-    auto tile = [&](auto full_tag, const int kt) {
+    // One 64-key tile at key kt from K / V rows at kbase / vbase in LDS (the
+    // operand layout above; fp32 input: the lo planes PLANE bytes after) and
+    // keep_tile (padded); FULL: all 64 keys present (no key-range masking).
+    auto compute = [&](auto full_tag, const int kt, const char* kbase, const char* vbase,
+                       const uint8_t* keep_tile) {
         constexpr bool FULL = decltype(full_tag)::value;
         const int nk = min(kBN, L - kt);
-        if (kt > 0) __syncthreads();  // the previous tile is no longer read
-        stash();
-        if (kt + kBN < L) fetch(kt + kBN);  // in flight while this tile is computed
-        if constexpr (PADDED) {
-            if (tid < kBN) sKeep[tid] = (tid < nk) ? p.keep[row0 + kt + tid] : 0;
-        }
-        __syncthreads();
-        if (!wave_active) return;
-
         // ---- S^T = K Q^T: block kb holds keys kt+16kb+4g+i (i<4), query r16
         f32x4 s[4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
             if (FULL || kb == 0 || 16 * kb < nk) {
-                const char* kr = sK + 2048 * kb;
+                const char* kr = kbase + 2048 * kb;
                 const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kr + koff0);
                 const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kr + koff1);
                 s[kb] = mfma(a0, qh0, f32x4{0.f, 0.f, 0.f, 0.f});
@@ -679,7 +719,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
                 s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};  // absent keys, masked below
             }
         }
-        online_probs<FULL, PADDED>(s, nk, sKeep, g, c, kt == 0, st);
+        online_probs<FULL, PADDED>(s, nk, keep_tile, g, c, kt == 0, st);
         // ---- O^T += V^T P^T, 32 keys per MFMA ----------------------------
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
@@ -688,7 +728,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
                 p_operand(s, cc, ph, pl, st);
 #pragma unroll
                 for (int db = 0; db < 4; ++db) {
-                    const char* vr = sV + 4096 * cc + voff[db];
+                    const char* vr = vbase + 4096 * cc + voff[db];
                     const bf16x4 v0 = ld_tr4(vr);
                     const bf16x4 v1 = ld_tr4(vr + 2048);
                     const bf16x8 av = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -704,9 +744,109 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
             }
         }
     };
-    int kt = 0;
-    for (; kt + kBN <= L; kt += kBN) tile(std::true_type{}, kt);
-    if (kt < L) tile(std::false_type{}, kt);
+
+    if constexpr (IN_F32) {
+        // Registers carrying one K/V tile from global memory to LDS: this
+        // thread's 16-byte chunk k_dg of key rows k_row0 and k_row1, of K and
+        // of V (hi and lo).  Eight consecutive lanes store one 128-byte LDS
+        // row, in the permuted chunk order of the operand layout.
+        bf16x8 kh0, kl0, kh1, kl1, vh0, vl0, vh1, vl1;
+        const int k_row0 = tid >> 3, k_row1 = (tid + kThreads) >> 3, k_dg = tid & 7;
+        const uint32_t so0 = 128u * k_row0 + 16u * (uint32_t)(k_dg ^ swz(k_row0));
+        const uint32_t so1 = 128u * k_row1 + 16u * (uint32_t)(k_dg ^ swz(k_row1));
+        auto fetch = [&](int kt) {
+            load8<IN_F32>(rk, row_off(kt + k_row0, ksb) + 8 * k_dg * ES, kh0, kl0);
+            load8<IN_F32>(rk, row_off(kt + k_row1, ksb) + 8 * k_dg * ES, kh1, kl1);
+            load8<IN_F32>(rv, row_off(kt + k_row0, vsb) + 8 * k_dg * ES, vh0, vl0);
+            load8<IN_F32>(rv, row_off(kt + k_row1, vsb) + 8 * k_dg * ES, vh1, vl1);
+        };
+        auto stash = [&]() {
+            *reinterpret_cast<bf16x8*>(sK + so0) = kh0;
+            *reinterpret_cast<bf16x8*>(sK + so1) = kh1;
+            *reinterpret_cast<bf16x8*>(sV + so0) = vh0;
+            *reinterpret_cast<bf16x8*>(sV + so1) = vh1;
+            *reinterpret_cast<bf16x8*>(sK + PLANE + so0) = kl0;
+            *reinterpret_cast<bf16x8*>(sK + PLANE + so1) = kl1;
+            *reinterpret_cast<bf16x8*>(sV + PLANE + so0) = vl0;
+            *reinterpret_cast<bf16x8*>(sV + PLANE + so1) = vl1;
+        };
+        fetch(0);
+        // Stage the tile at key kt into LDS (the next one's loads go out
+        // meanwhile), then compute it.  The full tiles run in one loop and the
+        // partial last tile after it.
+        auto tile = [&](auto full_tag, const int kt) {
+            const int nk = min(kBN, L - kt);
+            if (kt > 0) __syncthreads();  // the previous tile is no longer read
+            stash();
+            if (kt + kBN < L) fetch(kt + kBN);  // in flight while this tile is computed
+            if constexpr (PADDED) {
+                if (tid < kBN) sKeep[0][tid] = (tid < nk) ? p.keep[row0 + kt + tid] : 0;
+            }
+            __syncthreads();
+            if (wave_active) compute(full_tag, kt, sK, sV, sKeep[0]);
+        };
+        int kt = 0;
+        for (; kt + kBN <= L; kt += kBN) tile(std::true_type{}, kt);
+        if (kt < L) tile(std::false_type{}, kt);
+    } else {
+        // bf16 input: K and V tiles go straight into LDS by LDS-writing loads
+        // (no registers, no LDS store instructions), into two tile buffers:
+        // tile t + 1 is requested into one while tile t is computed from the
+        // other, and one barrier per tile separates them.  The loads are
+        // untracked (see above) and waited for explicitly before the barrier.
+        // Wave w moves 8-row blocks w and w + 4 of K and of V (1 KiB each);
+        // lane l writes slot l & 7 of row l >> 3 of its block.
+        const int lr = lane >> 3, slot = lane & 7;
+        const uint32_t c16e = 16u * (uint32_t)(slot ^ swz(lr)), c16o = 16u * (uint32_t)(slot ^ swz(8 + lr));
+        const i32x4 rkw = rsrc_words(static_cast<const char*>(p.k) + (row0 * p.ks + hoff) * ES,
+                                     (uint32_t)(span - 1) * ksb + kD * ES);
+        const i32x4 rvw = rsrc_words(static_cast<const char*>(p.v) + (row0 * p.vs + hoff) * ES,
+                                     (uint32_t)(span - 1) * vsb + kD * ES);
+        const uint32_t lds0 = (uint32_t)(uintptr_t)smem;  // (the low half of a flat LDS pointer)
+        auto request = [&](int kt, int buf) {
+            const uint32_t base = lds0 + (uint32_t)(buf * 2 * PLANE);
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                const int j = wave + 4 * jj;
+                const int row = kt + 8 * j + lr;
+                const uint32_t c16 = (j & 1) ? c16o : c16e;
+                ld_lds16_untracked(rkw, base + 1024u * (uint32_t)j, row_off(row, ksb) + c16);
+                ld_lds16_untracked(rvw, base + PLANE + 1024u * (uint32_t)j, row_off(row, vsb) + c16);
+            }
+        };
+        // padded: key kt + tid's keep byte (tid < 64; 0 past the sequence)
+        auto keep_byte = [&](int kt) -> uint8_t {
+            return (tid < kBN && kt + tid < L) ? p.keep[row0 + kt + tid] : (uint8_t)0;
+        };
+        const int nt = (L + kBN - 1) / kBN;
+        uint8_t kbyte = 0;
+        if constexpr (PADDED) kbyte = keep_byte(0);
+        request(0, 0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if constexpr (PADDED) {
+            if (tid < kBN) sKeep[0][tid] = kbyte;
+        }
+        __syncthreads();
+        auto step = [&](auto full_tag, int t) {
+            const int kt = t * kBN, buf = t & 1;
+            if (t + 1 < nt) {
+                if constexpr (PADDED) kbyte = keep_byte(kt + kBN);
+                request(kt + kBN, buf ^ 1);
+            }
+            if (wave_active) {
+                const char* kbase = smem + buf * 2 * PLANE;
+                compute(full_tag, kt, kbase, kbase + PLANE, sKeep[buf]);
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the next tile has landed
+            if constexpr (PADDED) {
+                if (t + 1 < nt && tid < kBN) sKeep[buf ^ 1][tid] = kbyte;
+            }
+            __syncthreads();  // ... and every wave is done with this one
+        };
+        int t = 0;
+        for (; (t + 1) * kBN <= L; ++t) step(std::true_type{}, t);
+        if (t * kBN < L) step(std::false_type{}, t);
+    }
 
     // ---- epilogue: O = acc / l, staged through LDS for row-contiguous stores --
     __syncthreads();  // every wave is done with the K / V tiles
@@ -740,73 +880,6 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
         __builtin_amdgcn_raw_buffer_store_b128(val, ro, row_off(qrow + wave * 16 + r, osb) + 16 * cix, 0, 0);
     }
 }
-
-// ---- loads the compiler does not track ------------------------------------
-//
-// The gathered layout's speculative path issues its keep-byte loads and
-// LDS-writing K/V loads as inline assembly and waits for them with explicit
-// counts: the compiler's own waits would make the keep ranking wait for the
-// K/V loads (it cannot tell that LDS-writing loads and the ranking's LDS
-// words do not overlap).  A wave's loads complete in issue order, which the
-// count-based wait for the keep bytes (issued first) relies on.
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// The four words of the raw buffer resource over [base, base + bytes) that
-// make_rsrc builds.
-__device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes)
-{
-    const uint64_t a = (uint64_t)(uintptr_t)base;
-    return i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xFFFFu), (int)bytes, (int)dev::kRsrcWord3};
-}
-
-// One byte at offset off of the resource, zero-extended.  The result register
-// is written when the load completes: read it only after a wait_vm() that
-// covers the load and a vm_done() on it.
-__device__ __forceinline__ uint32_t ld_u8_untracked(i32x4 r, uint32_t off)
-{
-    uint32_t x;
-    asm volatile("buffer_load_ubyte %0, %1, %2, 0 offen" : "=v"(x) : "v"(off), "s"(r));
-    return x;
-}
-
-// Sixteen bytes per lane at offset voff of the resource into LDS at lds_addr
-// + 16 lane (lds_addr wave-uniform).  The LDS base goes in through M0 as an
-// input operand; the s_nop gives the M0 write the wait state the load needs.
-__device__ __forceinline__ void ld_lds16_untracked(i32x4 r, uint32_t lds_addr, uint32_t voff)
-{
-    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(r), "{m0}"(lds_addr));
-}
-
-// Waits until at most n (wave-uniform, even, >= 0) of this wave's
-// vector-memory operations are outstanding; an n above 14 waits for 14.
-__device__ __forceinline__ void wait_vm(int n)
-{
-    const int u = __builtin_amdgcn_readfirstlane(n);
-    asm volatile(
-        "s_cmp_lt_u32 %0, 2\n\ts_cbranch_scc1 0f\n\t"
-        "s_cmp_lt_u32 %0, 4\n\ts_cbranch_scc1 2f\n\t"
-        "s_cmp_lt_u32 %0, 6\n\ts_cbranch_scc1 4f\n\t"
-        "s_cmp_lt_u32 %0, 8\n\ts_cbranch_scc1 6f\n\t"
-        "s_cmp_lt_u32 %0, 10\n\ts_cbranch_scc1 8f\n\t"
-        "s_cmp_lt_u32 %0, 12\n\ts_cbranch_scc1 10f\n\t"
-        "s_cmp_lt_u32 %0, 14\n\ts_cbranch_scc1 12f\n\t"
-        "s_waitcnt vmcnt(14)\n\ts_branch 1f\n"
-        "12:\n\ts_waitcnt vmcnt(12)\n\ts_branch 1f\n"
-        "10:\n\ts_waitcnt vmcnt(10)\n\ts_branch 1f\n"
-        "8:\n\ts_waitcnt vmcnt(8)\n\ts_branch 1f\n"
-        "6:\n\ts_waitcnt vmcnt(6)\n\ts_branch 1f\n"
-        "4:\n\ts_waitcnt vmcnt(4)\n\ts_branch 1f\n"
-        "2:\n\ts_waitcnt vmcnt(2)\n\ts_branch 1f\n"
-        "0:\n\ts_waitcnt vmcnt(0)\n"
-        "1:"
-        :
-        : "s"(u)
-        : "memory", "scc");
-}
-
-// Marks x as produced after the preceding volatile statements (a wait_vm), so
-// that no read of it is scheduled before them.
-__device__ __forceinline__ void vm_done(uint32_t& x) { asm volatile("" : "+v"(x)); }
 
 // ---- LDS-resident kernel (bf16 input, sequences of up to kLdsMaxRows keys) --
 //
