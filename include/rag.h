@@ -180,7 +180,9 @@ RAG_API rag_status rag_repack(const uint8_t* keep_packed, const int32_t* cu_in,
  * P.V product.  Deterministic (no atomics).  Max abs error vs exact fp64
  * attention on the same inputs: <= 2e-3 for F32 output (measured well below).
  * Pointers must be 16-byte aligned and row strides multiples of 16 bytes;
- * max_seqlen times the widest row stride must stay below 2^31 bytes.
+ * max_seqlen times the widest row stride must stay below 2^31 bytes, and B*H
+ * must not exceed 2^31 - 1 (RAG_ERR_UNSUPPORTED otherwise; also for
+ * rag_attn_padded and rag_attn_gathered).
  */
 RAG_API rag_status rag_attn(const void* q, const void* k, const void* v, int64_t q_row_stride,
                             int64_t k_row_stride, int64_t v_row_stride, rag_dtype in_dtype,

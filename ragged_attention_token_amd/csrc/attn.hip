@@ -58,7 +58,6 @@ constexpr int kD = 64;         // head dimension
 constexpr int kBM = 64;        // query rows per workgroup
 constexpr int kBN = 64;        // keys per LDS tile
 constexpr int kThreads = 256;  // 4 waves x 16 query rows
-constexpr int64_t kGridRow = 1 << 20;
 // Tile kernel, grid launches: an XCD takes its (head, image) pairs kPairBlock
 // at a time, every q-tile of the block before the next block.  1 puts a
 // pair's q-tiles back to back (they then read the same K / V lines at the
@@ -66,7 +65,8 @@ constexpr int64_t kGridRow = 1 << 20;
 // whose reuse distance lets Q and O streams evict the pairs' K / V from L2
 // (N = 577: 1.33x the algorithmic bytes fetched).  4 fetches the algorithmic
 // bytes and measured fastest of 1, 4, 16 and all.
-constexpr int kPairBlock = 4;  // workgroups per grid row of the tile kernel (multiple of 8)
+constexpr int kPairBlock = 4;  // a power of two
+constexpr int kMaxGridY = 65535;
 
 // Where the rows of one image live.
 enum Layout : int {
@@ -88,7 +88,21 @@ struct AttnParams {
     int32_t tl_kt;           // tile-list launch: key tiles of the longest image (else 0)
     float scale_log2;        // scale * log2(e)
     int32_t natural_first;   // gathered layout: request K/V in natural order beside the keep bytes
+    uint32_t h_magic;        // floor(2^32 / H) + 1 (H >= 2): pair / H by a multiply-high
 };
+
+// (pair / H, pair % H) for pair < 2^32: the multiply-high by h_magic
+// over-estimates the quotient by at most one, corrected once.
+__device__ __forceinline__ void split_pair(uint32_t pair, int H, uint32_t h_magic, int& h, int& b)
+{
+    uint32_t q = pair;
+    if (H > 1) {
+        q = __umulhi(pair, h_magic);
+        q -= (q * (uint32_t)H > pair) ? 1u : 0u;
+    }
+    b = (int)q;
+    h = (int)(pair - q * (uint32_t)H);
+}
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c)
 {
@@ -595,20 +609,18 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
     // next kPairBlock, so every q-tile after a pair's first finds the pair's
     // K and V in that XCD's L2 instead of fetching them again.  Slots past the
     // last pair exit at once.
-    // (The grid is (X, Y) with X a multiple of 8, so that the linear id below
-    // is the dispatch order and id % 8 the XCD however large the launch.)
+    // The grid is (8 * kPairBlock * q-tiles, blocks of pairs), the second
+    // folded into (Y, Z) beyond kMaxGridY: x = XCD + 8 * (pair in the block +
+    // kPairBlock * q-tile), so the dispatch order is the linear id and x % 8
+    // the XCD, and the decode is shifts and masks.
     int h, b, qt;
     if constexpr (!TILES) {
-        const int64_t id = blockIdx.x + (int64_t)gridDim.x * blockIdx.y;
-        const int xcd = (int)(id & 7);
-        const int64_t k = id >> 3;
-        const int64_t per_blk = (int64_t)kPairBlock * p.n_qtiles;
-        const int64_t blk = k / per_blk, r = k - blk * per_blk;
-        qt = (int)(r / kPairBlock);
-        const int64_t pair = xcd + 8 * (blk * kPairBlock + r % kPairBlock);
-        if (pair >= (int64_t)p.H * p.B) return;  // uniform over the workgroup
-        h = (int)(pair % p.H);
-        b = (int)(pair / p.H);
+        const uint32_t x = blockIdx.x;
+        const uint32_t blk = blockIdx.y + gridDim.y * blockIdx.z;
+        qt = (int)(x / (8u * kPairBlock));
+        const uint32_t pair = (x & 7u) + 8u * (blk * kPairBlock + ((x >> 3) & (kPairBlock - 1)));
+        if (pair >= (uint32_t)p.H * (uint32_t)p.B) return;  // uniform over the workgroup
+        split_pair(pair, p.H, p.h_magic, h, b);
     }
 
     int64_t row0;
@@ -675,12 +687,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
         load8<IN_F32>(rq, off, qh0, ql0);
         load8<IN_F32>(rq, off + 32 * ES, qh1, ql1);
     }
-    if constexpr (!IN_F32) {
-        // (a use of Q before the untracked K/V loads go out, so that the
-        // compiler's wait for Q covers Q alone, not the first K/V tiles)
-        asm volatile("" : "+v"(qh0), "+v"(qh1));
-    }
-    const float c = fold_scale(p.scale_log2, qh0, qh1, ql0, ql1);
+    // (bf16 input: formed once the first K/V tile has landed, below)
+    float c = 0.f;
+    if constexpr (IN_F32) c = fold_scale(p.scale_log2, qh0, qh1, ql0, ql1);
     Online st;
     online_init(st);
 
@@ -823,6 +832,11 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
         if constexpr (PADDED) kbyte = keep_byte(0);
         request(0, 0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // Q, requested before tile 0, has landed with it: a use of Q here puts
+        // the compiler's own wait for it where it costs nothing (at the first
+        // score product it would also wait for the next tile's loads).
+        asm volatile("" : "+v"(qh0), "+v"(qh1));
+        c = fold_scale(p.scale_log2, qh0, qh1, ql0, ql1);
         if constexpr (PADDED) {
             if (tid < kBN) sKeep[0][tid] = kbyte;
         }
@@ -1264,12 +1278,11 @@ void launch_variant(const AttnParams& p, int layout, hipStream_t st)
         hipLaunchKernelGGL((attn_kernel<IN_F32, OUT_F32, kRagged, true>), grid, block, 0, st, p);
         return;
     }
-    // one slot per (pair, q-tile), pairs rounded up to a multiple of the 8 XCDs,
-    // folded into rows of kGridRow slots
-    const int64_t per_xcd = ((int64_t)p.H * p.B + 7) / 8;
-    const int64_t slots = 8 * ((per_xcd + kPairBlock - 1) / kPairBlock * kPairBlock) * p.n_qtiles;
-    const dim3 grid((unsigned)std::min<int64_t>(slots, kGridRow),
-                    (unsigned)((slots + kGridRow - 1) / kGridRow)), block(kThreads);
+    // one slot per (pair, q-tile); blocks of 8 * kPairBlock pairs
+    const int64_t nblk = ((int64_t)p.H * p.B + 8 * kPairBlock - 1) / (8 * kPairBlock);
+    const int64_t gy = std::min<int64_t>(nblk, kMaxGridY);
+    const dim3 grid((unsigned)(8 * kPairBlock * p.n_qtiles), (unsigned)gy,
+                    (unsigned)((nblk + gy - 1) / gy)), block(kThreads);
     if (layout == kPadded)
         hipLaunchKernelGGL((attn_kernel<IN_F32, OUT_F32, kPadded, false>), grid, block, 0, st, p);
     else if (layout == kGathered)
@@ -1310,6 +1323,7 @@ int launch_attn(const void* q, const void* k, const void* v, int64_t q_row_strid
     p.tl_kt = (layout == kRagged && (flags & kAttnTileList)) ? (p.max_len + 63) / 64 : 0;
     p.natural_first = (layout == kGathered && max_seqlen >= N && (int64_t)B * H < 256) ? 1 : 0;
     p.scale_log2 = scale * 1.4426950408889634f;
+    p.h_magic = H > 1 ? (uint32_t)((1ull << 32) / (uint64_t)H + 1ull) : 0u;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool in_f32 = in_dtype == RAG_DTYPE_F32, out_f32 = out_dtype == RAG_DTYPE_F32;
     const size_t lds_bytes = lds_kernel_bytes(p, in_f32, layout);

@@ -132,9 +132,9 @@ rag_status validate_unpack(const void* packed, int64_t packed_row_stride, int32_
 }
 
 static rag_status check_attn_common(const void* q, const void* k, const void* v, int64_t qs,
-                                    int64_t ks, int64_t vs, int32_t in_dtype, int32_t H,
-                                    int32_t head_dim, float scale, const void* o, int64_t os,
-                                    int32_t out_dtype)
+                                    int64_t ks, int64_t vs, int32_t in_dtype, int32_t B,
+                                    int32_t H, int32_t head_dim, float scale, const void* o,
+                                    int64_t os, int32_t out_dtype)
 {
     if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
         return set_error(RAG_ERR_UNSUPPORTED, "dtype must be RAG_DTYPE_F32 or RAG_DTYPE_BF16");
@@ -142,6 +142,10 @@ static rag_status check_attn_common(const void* q, const void* k, const void* v,
         return set_error(RAG_ERR_UNSUPPORTED, "head_dim=%d; only %d is built", head_dim,
                          RAG_HEAD_DIM);
     if (H < 1) return set_error(RAG_ERR_INVALID_ARG, "H=%d must be >= 1", H);
+    // (the kernels number the (head, image) pairs with 32-bit integers)
+    if ((int64_t)B * H > INT32_MAX)
+        return set_error(RAG_ERR_UNSUPPORTED, "B*H=%lld (head, image) pairs exceed 2^31-1",
+                         (long long)B * H);
     if (!std::isfinite(scale)) return set_error(RAG_ERR_INVALID_ARG, "scale must be finite");
     const int64_t C = (int64_t)H * head_dim;
     const void* ptrs[4] = {q, k, v, o};
@@ -187,7 +191,7 @@ rag_status validate_attn(const void* q, const void* k, const void* v, int64_t q_
     if (total_rows < 0) return set_error(RAG_ERR_INVALID_ARG, "total_rows=%d must be >= 0", total_rows);
     if (!cu_seqlens) return set_error(RAG_ERR_INVALID_ARG, "cu_seqlens is NULL");
     rag_status s = check_attn_common(q, k, v, q_row_stride, k_row_stride, v_row_stride, in_dtype,
-                                     H, head_dim, scale, o, o_row_stride, out_dtype);
+                                     B, H, head_dim, scale, o, o_row_stride, out_dtype);
     if (s != RAG_OK) return s;
     return check_span(max_seqlen, q_row_stride, k_row_stride, v_row_stride, in_dtype, o_row_stride,
                       out_dtype);
@@ -214,7 +218,7 @@ rag_status validate_attn_padded(const void* q, const void* k, const void* v,
     rag_status s = check_batch(B, N);
     if (s != RAG_OK) return s;
     if (!keep) return set_error(RAG_ERR_INVALID_ARG, "keep is NULL");
-    s = check_attn_common(q, k, v, q_row_stride, k_row_stride, v_row_stride, in_dtype, H, head_dim,
+    s = check_attn_common(q, k, v, q_row_stride, k_row_stride, v_row_stride, in_dtype, B, H, head_dim,
                           scale, o, o_row_stride, out_dtype);
     if (s != RAG_OK) return s;
     return check_span(N, q_row_stride, k_row_stride, v_row_stride, in_dtype, o_row_stride,

@@ -144,6 +144,23 @@ def test_attn_rejects(lib, kwargs, status, needle):
         assert needle in binding.last_error()
 
 
+def test_attn_rejects_more_pairs_than_32_bit_ids(lib):
+    """The kernels number (head, image) pairs with 32-bit integers: B*H above
+    2^31 - 1 is refused before any launch."""
+    H = 32769  # 65535 * 32769 = 2^31 + 32768
+    w = H * 64
+    kw = dict(B=65535, H=H, maxlen=1, tr=65535, qs=3 * w, ks=3 * w, vs=3 * w, os_=w)
+    assert attn(lib, **kw) == UNSUPPORTED
+    assert "B*H" in binding.last_error()
+    # one head fewer is below the limit: the check after it (the scale) decides
+    assert attn(lib, **dict(kw, H=H - 1, qs=3 * (w - 64), ks=3 * (w - 64), vs=3 * (w - 64),
+                            os_=w - 64, scale=float("inf"))) == INVALID
+    assert "scale" in binding.last_error()
+    assert lib.rag_attn_padded(A, A, A, 3 * w, 3 * w, 3 * w, BF16, A, 65535, 1, H, 64, 0.125, A,
+                               w, F32, None) == UNSUPPORTED
+    assert "B*H" in binding.last_error()
+
+
 @pytest.mark.parametrize("kwargs,needle", [(dict(B=1025, tr=1025 * 197), "B=1025"),
                                            (dict(H=65, os_=65 * 64, qs=3 * 65 * 64, ks=3 * 65 * 64,
                                                  vs=3 * 65 * 64), "H=65"),
