@@ -120,9 +120,10 @@ def test_most_images():
 
 def test_tile_kernel_grid_over_several_rows():
     """fp32 input takes the 64-key tile kernel, whose slots ((image, head) pair,
-    q-tile) are folded into grid rows of 2^20: B = 65535 images of H = 17 heads
-    give 1 114 095 pairs, more than one row.  Every row of the output matches
-    the oracle; the gathered and padded layouts (the same kernel) agree."""
+    q-tile) form a grid of (32 * q-tiles, blocks of 32 pairs): B = 65535 images
+    of H = 17 heads give 1 114 095 pairs in 34 816 blocks.  Every row of the
+    output matches the oracle; the gathered and padded layouts (the same
+    kernel) agree."""
     rng = np.random.default_rng(33)
     w = wl.custom(B=RAG_MAX_B, N=2, H=17, lengths=rng.integers(0, 3, size=RAG_MAX_B), dtype="f32",
                   seed=33)
@@ -143,3 +144,27 @@ def test_tile_kernel_grid_over_several_rows():
     assert (gz[gather_ref].view(np.uint8) == as_numpy_rows(o32)[:T].view(np.uint8)).all()
     pz = _padded(w, torch.float32).cpu().numpy().astype(np.float64)
     assert np.abs(pz[gather_ref] - want).max() <= ATOL
+
+
+def test_tile_kernel_pair_blocks_folded_into_z():
+    """bf16 input with max_seqlen = 257 takes the 64-key tile kernel (5 q-tiles
+    per pair).  B = 65535 images of H = 33 heads give 2 162 655 pairs, 67 584
+    blocks of 32: more than the 65 535 grid rows, so the blocks continue in a
+    second z layer, and the images at the end of the batch are served from it.
+    Every row of the output matches the oracle; rows past the packed ones are
+    untouched."""
+    rng = np.random.default_rng(34)
+    w = wl.custom(B=RAG_MAX_B, N=2, H=33, lengths=rng.integers(0, 3, size=RAG_MAX_B), seed=34)
+    print("B", w.B, "H", w.H, "T", w.T, flush=True)
+    assert (w.B * w.H + 31) // 32 > 65535
+    g = gpu_pack(w)
+    packed_ref, cu_ref, gather_ref = oracle.pack(w.keep, wl.rows(w))
+    o32 = gpu_attn(g["packed"], g["cu"], w, torch.float32, max_seqlen=257)
+    q, k, v = wl.split_qkv(packed_ref, w.C)
+    want = oracle.attn(q, k, v, cu_ref, w.H, w.d, w.scale)
+    T = w.T
+    out = o32.cpu().numpy()
+    err = np.abs(out[:T].astype(np.float64) - want).max()
+    print("max abs err", err, flush=True)
+    assert err <= ATOL
+    assert (out[T:].view(np.uint32) == np.uint32(SENTINEL_BYTE * 0x01010101)).all()
