@@ -20,7 +20,10 @@
 //   * both operands are K-contiguous, so both MFMA operands come from LDS rows
 //     with one 16-byte read per lane; the product is computed transposed,
 //     D^T = W X^T, so that a lane's four accumulator values are four
-//     consecutive output columns of one row (one 8-byte store);
+//     consecutive output columns of one row;
+//   * the epilogue stages each wave's 64 x 64 fp32 block in LDS and writes
+//     rows back 16 bytes per lane, 128 contiguous bytes per 8 lanes (the
+//     accumulator layout would store 16 rows x 32 bytes per instruction);
 //   * workgroup tile 128 (m) x 128 (n), four wave64s in a 2 x 2 arrangement,
 //     each owning 64 x 64 outputs (4 x 4 blocks of v_mfma_f32_16x16x32_bf16,
 //     fp32 accumulators in VGPRs);
@@ -48,7 +51,6 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 using dev::kDropOffset;
 using dev::ld16;
 using dev::make_rsrc;
@@ -190,35 +192,61 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p)
         __syncthreads();
     }
 
-    // ---- epilogue: acc[nb][mb][i] = D[m0 + 64 wm + 16 mb + r16][n0 + 64 wn + 16 nb + 4 g + i]
+    // ---- epilogue: acc[nb][mb][i] = D[m0 + 64 wm + 16 mb + r16][n0 + 64 wn + 16 nb + 4 g + i].
+    // Each wave stages its 64 x 64 fp32 block in LDS (free after the loop's
+    // last barrier; 16 KiB per wave) and writes it back row-contiguously: a
+    // lane takes 8 consecutive columns of one row (16 output bytes), 8 lanes a
+    // whole 128-byte row segment, where the accumulator layout would give 16
+    // rows x 32 bytes per store.  Rows are 256 bytes (16 chunks of 16 bytes);
+    // chunk c of row r sits at chunk c ^ (r & 15), so that both the accumulator
+    // writes (16 rows, one chunk each) and the row reads (two rows of 8 chunk
+    // pairs per 16 lanes) hit distinct banks.  The arithmetic is the same
+    // as element by element: (acc + bias), GELU, + residual, one rounding.
+    const int n0w = n0 + 64 * wn;  // the wave's first column
+    if (n0w >= p.N) return;        // (N is a multiple of 64: a wave's columns are all in or all out)
+    char* so = lds + wave * (64 * 256);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+            const int row = 16 * mb + r16, chunk = 4 * nb + g;
+            *reinterpret_cast<f32x4*>(so + row * 256 + 16 * (chunk ^ r16)) = acc[nb][mb];
+        }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+    __builtin_amdgcn_wave_barrier();
     const int mrows = min(kBM, p.M - m0);
     const auto rd = make_rsrc(p.d + (int64_t)m0 * p.N, (uint32_t)mrows * (uint32_t)p.N * 2u);
     const auto rr = make_rsrc(p.r ? p.r + (int64_t)m0 * p.N : p.d, p.r ? (uint32_t)mrows * (uint32_t)p.N * 2u : 0u);
+    const int cl = lane & 7;  // the lane's 8 columns: 8 cl .. 8 cl + 7 of the wave's 64
+    const f32x4 bias0 = *reinterpret_cast<const f32x4*>(p.bias + n0w + 8 * cl);
+    const f32x4 bias1 = *reinterpret_cast<const f32x4*>(p.bias + n0w + 8 * cl + 4);
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-        const int n = n0 + 64 * wn + 16 * nb + 4 * g;
-        const bool ncol = n < p.N;
-        const f32x4 bias = ncol ? *reinterpret_cast<const f32x4*>(p.bias + n) : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 8; ++j) {
+        const int row = 8 * j + (lane >> 3);  // row within the wave's block
+        const char* src = so + row * 256;
+        const f32x4 a0 = *reinterpret_cast<const f32x4*>(src + 16 * ((2 * cl) ^ (row & 15)));
+        const f32x4 a1 = *reinterpret_cast<const f32x4*>(src + 16 * ((2 * cl + 1) ^ (row & 15)));
+        const int m = 64 * wm + row;  // row within the tile
+        const uint32_t off = ((uint32_t)m * (uint32_t)p.N + (uint32_t)(n0w + 8 * cl)) * 2u;
+        float v[8];
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-            const int m = 64 * wm + 16 * mb + r16;  // row within the tile
-            const uint32_t off = ncol ? ((uint32_t)m * (uint32_t)p.N + (uint32_t)n) * 2u : kDropOffset;
-            f32x4 v = acc[nb][mb] + bias;
-            if constexpr (EPI == kGemmGelu) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) v[i] = gelu_exact(v[i]);
-            }
-            if constexpr (EPI == kGemmResidual) {
-                const u32x2 rv = __builtin_amdgcn_raw_buffer_load_b64(rr, off, 0, 0);
-                const bf16x4 r4 = __builtin_bit_cast(bf16x4, rv);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) v[i] += static_cast<float>(r4[i]);
-            }
-            bf16x4 o;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) o[i] = static_cast<__bf16>(v[i]);
-            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o), rd, off, 0, 0);
+        for (int i = 0; i < 4; ++i) {
+            v[i] = a0[i] + bias0[i];
+            v[4 + i] = a1[i] + bias1[i];
         }
+        if constexpr (EPI == kGemmGelu) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = gelu_exact(v[i]);
+        }
+        if constexpr (EPI == kGemmResidual) {
+            const bf16x8 r8 = __builtin_bit_cast(bf16x8, ld16(rr, off));
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] += static_cast<float>(r8[i]);
+        }
+        bf16x8 o;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = static_cast<__bf16>(v[i]);
+        dev::st16(__builtin_bit_cast(u32x4, o), rd, off);
     }
 }
 
