@@ -85,6 +85,7 @@ struct AttnParams {
     const uint8_t* keep;     // padded and gathered
     int32_t B, N, H, total_rows, max_len, n_qtiles, zero_dropped;
     int32_t lds_rows;        // LDS-resident kernel: K / V rows held, max_len rounded up to 32
+    int32_t out_stage;       // LDS-resident kernel: byte offset of the per-wave output slots (0: none)
     int32_t tl_kt;           // tile-list launch: key tiles of the longest image (else 0)
     float scale_log2;        // scale * log2(e)
     int32_t natural_first;   // gathered layout: request K/V in natural order beside the keep bytes
@@ -911,11 +912,14 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
 constexpr int kLdsRowAlign = 32;      // K / V rows in LDS: a multiple of the P.V k-depth
 constexpr int kMaxWaves = 16;         // 16 query blocks: every block of kLdsMaxRows rows
 constexpr int kLdsMaxRows = 256;      // 64 KiB of K + V: two workgroups per CU
+constexpr size_t kLdsStageMax = 80 * 1024;  // K + V + keep data + output slots: two workgroups per CU
 
 // TL: 0 = grid of (head, image, query split); tile list of 1 = whole pairs,
 // 2 = 64-row query tiles.  NAT (gathered layout, few pairs): K and V are
 // requested in natural order beside the keep bytes (see the gathered setup).
-template <bool OUT_F32, int LAYOUT, bool MULTI, int TL, bool NAT = false>
+// STAGE (few pairs): the output goes out through per-wave LDS slots at byte
+// p.out_stage as whole-row 16-byte chunks (see the epilogue).
+template <bool OUT_F32, int LAYOUT, bool MULTI, int TL, bool NAT = false, bool STAGE = false>
 __global__ __launch_bounds__(64 * kMaxWaves) void attn_lds_kernel(AttnParams p)
 {
     constexpr bool PADDED = LAYOUT == kPadded;
@@ -1165,18 +1169,52 @@ __global__ __launch_bounds__(64 * kMaxWaves) void attn_lds_kernel(AttnParams p)
 
         // ---- epilogue: O = acc / l; lane holds O[16 qb + r16][16 db + 4g + i] ----
         const float inv = online_inv(st);
-        const uint32_t orow = row_off(16 * qb + r16, osb);
+        if constexpr (STAGE) {
+            // The block's 16 output rows go through the wave's own LDS slot
+            // and out as 16-byte chunks, 128 contiguous bytes per 8 lanes (the
+            // accumulator layout alone stores 16 rows x 32 or 64 bytes per
+            // instruction).  Chunk c of slot row r sits at c ^ (r mod NCH) so
+            // that both the accumulator writes and the row reads spread over
+            // the banks.  The slot is rewritten only after this wave's reads
+            // of it (its next block), which LDS orders within a wave.
+            constexpr int RB = kD * OES;  // bytes per output row: 128 (bf16) or 256 (fp32)
+            constexpr int NCH = RB / 16;  // 16-byte chunks per row
+            char* so = lds + p.out_stage + wave * 16 * RB;
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
-            const f32x4 r = st.acc[db] * inv;
-            const uint32_t off = orow + (uint32_t)(16 * db + 4 * g) * OES;
-            if constexpr (OUT_F32) {
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, r), ro, off, 0, 0);
-            } else {
-                bf16x4 o4;
+            for (int db = 0; db < 4; ++db) {
+                const f32x4 r = st.acc[db] * inv;
+                if constexpr (OUT_F32) {
+                    *reinterpret_cast<f32x4*>(so + r16 * RB + 16 * ((4 * db + g) ^ (r16 & (NCH - 1)))) = r;
+                } else {
+                    bf16x4 o4;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) o4[i] = static_cast<__bf16>(r[i]);
-                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o4), ro, off, 0, 0);
+                    for (int i = 0; i < 4; ++i) o4[i] = static_cast<__bf16>(r[i]);
+                    *reinterpret_cast<bf16x4*>(so + r16 * RB + 16 * ((2 * db + (g >> 1)) ^ (r16 & (NCH - 1))) +
+                                               8 * (g & 1)) = o4;
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's slot writes are done
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int k = 0; k < 16 * NCH / 64; ++k) {
+                const int row = lane / NCH + k * (64 / NCH), ch = lane % NCH;
+                const u32x4 val = *reinterpret_cast<const u32x4*>(so + row * RB + 16 * (ch ^ (row & (NCH - 1))));
+                __builtin_amdgcn_raw_buffer_store_b128(val, ro, row_off(16 * qb + row, osb) + 16u * (uint32_t)ch, 0, 0);
+            }
+        } else {
+            const uint32_t orow = row_off(16 * qb + r16, osb);
+#pragma unroll
+            for (int db = 0; db < 4; ++db) {
+                const f32x4 r = st.acc[db] * inv;
+                const uint32_t off = orow + (uint32_t)(16 * db + 4 * g) * OES;
+                if constexpr (OUT_F32) {
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, r), ro, off, 0, 0);
+                } else {
+                    bf16x4 o4;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) o4[i] = static_cast<__bf16>(r[i]);
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o4), ro, off, 0, 0);
+                }
             }
         }
         if constexpr (!MULTI) break;  // (single-block launches: one block per wave)
@@ -1200,23 +1238,23 @@ size_t lds_kernel_bytes(const AttnParams& p, bool in_f32, int layout)
     return bytes <= 64 * 1024 ? bytes : 0;
 }
 
-template <bool OUT_F32, bool MULTI>
+template <bool OUT_F32, bool MULTI, bool STAGE = false>
 void launch_lds_layout(const AttnParams& p, int layout, dim3 grid, dim3 block, size_t lds_bytes,
                        hipStream_t st)
 {
     if (layout == kPadded)
-        hipLaunchKernelGGL((attn_lds_kernel<OUT_F32, kPadded, MULTI, 0>), grid, block, lds_bytes, st, p);
+        hipLaunchKernelGGL((attn_lds_kernel<OUT_F32, kPadded, MULTI, 0, false, STAGE>), grid, block, lds_bytes, st, p);
     else if (layout == kGathered && !MULTI && p.natural_first && p.N <= 4 * (int)block.x)
-        hipLaunchKernelGGL((attn_lds_kernel<OUT_F32, kGathered, false, 0, true>), grid, block, lds_bytes, st, p);
+        hipLaunchKernelGGL((attn_lds_kernel<OUT_F32, kGathered, false, 0, true, STAGE>), grid, block, lds_bytes, st, p);
     else if (layout == kGathered)
-        hipLaunchKernelGGL((attn_lds_kernel<OUT_F32, kGathered, MULTI, 0>), grid, block, lds_bytes, st, p);
+        hipLaunchKernelGGL((attn_lds_kernel<OUT_F32, kGathered, MULTI, 0, false, STAGE>), grid, block, lds_bytes, st, p);
     else if (p.tl_kt == 0)
-        hipLaunchKernelGGL((attn_lds_kernel<OUT_F32, kRagged, MULTI, 0>), grid, block, lds_bytes, st, p);
-    else if (grid.z == 1)  // tile list, many pairs: whole (image, head) pairs
-        hipLaunchKernelGGL((attn_lds_kernel<OUT_F32, kRagged, MULTI, 1>),
+        hipLaunchKernelGGL((attn_lds_kernel<OUT_F32, kRagged, MULTI, 0, false, STAGE>), grid, block, lds_bytes, st, p);
+    else if (grid.z == 1)  // tile list, many pairs (or few with one query split): whole (image, head) pairs
+        hipLaunchKernelGGL((attn_lds_kernel<OUT_F32, kRagged, MULTI, 1, false, STAGE>),
                            dim3(tile_list_grid(p.B, p.H, p.tl_kt, true)), block, lds_bytes, st, p);
     else  // tile list, few pairs: the query splits are 64-row query tiles
-        hipLaunchKernelGGL((attn_lds_kernel<OUT_F32, kRagged, false, 2>),
+        hipLaunchKernelGGL((attn_lds_kernel<OUT_F32, kRagged, false, 2, false, STAGE>),
                            dim3(tile_list_grid(p.B, p.H, p.tl_kt, false)), block, lds_bytes, st, p);
 }
 
@@ -1263,11 +1301,23 @@ void launch_lds_variant(AttnParams p, int layout, size_t lds_bytes, hipStream_t 
     const int splits = halves ? 2 : many ? 1 : (nqb + waves - 1) / waves;
     p.lds_rows = (p.max_len + kLdsRowAlign - 1) & ~(kLdsRowAlign - 1);
     if (p.tl_kt > 0 && !many) waves = 4;
+    // With few pairs (the latency-bound small batches, whose last stores end
+    // the launch) the output goes through per-wave LDS slots (16 rows each)
+    // after K, V and the layout's keep data: B = 1-4 attention and the
+    // one-launch pass 4-5% sooner.  With many pairs the extra LDS traffic
+    // cost more than the whole-row stores saved (the headline batch 1.5%
+    // slower, the unpruned one-launch pass 17%).
+    const size_t base = (lds_bytes + 15) & ~(size_t)15;
+    const size_t staged = base + (size_t)waves * 16 * kD * (OUT_F32 ? 4 : 2);
     const dim3 grid(p.H, p.B, splits), block(64 * waves);
-    if (waves * splits >= nqb)
+    if (!many && staged <= kLdsStageMax) {  // (few pairs: one block per wave)
+        p.out_stage = (int32_t)base;
+        launch_lds_layout<OUT_F32, false, true>(p, layout, grid, block, staged, st);
+    } else if (waves * splits >= nqb) {
         launch_lds_layout<OUT_F32, false>(p, layout, grid, block, lds_bytes, st);
-    else
+    } else {
         launch_lds_layout<OUT_F32, true>(p, layout, grid, block, lds_bytes, st);
+    }
 }
 
 template <bool IN_F32, bool OUT_F32>
@@ -1320,6 +1370,7 @@ int launch_attn(const void* q, const void* k, const void* v, int64_t q_row_strid
     p.n_qtiles = (p.max_len + kBM - 1) / kBM;
     p.zero_dropped = (flags & RAG_UNPACK_ZERO_DROPPED) ? 1 : 0;
     p.lds_rows = 0;
+    p.out_stage = 0;
     p.tl_kt = (layout == kRagged && (flags & kAttnTileList)) ? (p.max_len + 63) / 64 : 0;
     p.natural_first = (layout == kGathered && max_seqlen >= N && (int64_t)B * H < 256) ? 1 : 0;
     p.scale_log2 = scale * 1.4426950408889634f;
