@@ -516,6 +516,40 @@ def test_lds_resident_and_tile_kernels_agree_bit_for_bit():
     _check_attn(w, ref, o32, o16, range(w.B))
 
 
+def test_few_pairs_at_the_longest_lds_resident_length():
+    """Few (image, head) pairs at 256 keys, the LDS-resident kernel's longest
+    sequences, where its output leaves through per-wave LDS slots beside 64 KiB
+    of K and V: 72 KiB in all with bf16 output, exactly the 80 KiB limit with
+    fp32 output (ragged layout); past it for the padded layout's fp32 output,
+    which keeps the direct stores.  Every form equals the 64-key tile kernel or
+    the three-stage result bit for bit, and the oracle."""
+    w = wl.custom(B=3, N=256, H=2, lengths=[256, 255, 1], seed=41)
+    ref = _oracle_pack(w)
+    gather_ref = ref[2]
+    g = gpu_pack(w)
+    for out_dtype in (torch.float32, torch.bfloat16):
+        lds = gpu_attn(g["packed"], g["cu"], w, out_dtype, max_seqlen=256)
+        tile = gpu_attn(g["packed"], g["cu"], w, out_dtype, max_seqlen=257)
+        assert torch.equal(lds[:w.T].view(torch.uint8), tile[:w.T].view(torch.uint8)), out_dtype
+        fused = as_numpy_rows(_gathered(w, out_dtype))
+        assert (fused[gather_ref].view(np.uint8) == as_numpy_rows(lds)[:w.T].view(np.uint8)).all(), out_dtype
+    o32 = gpu_attn(g["packed"], g["cu"], w, torch.float32, max_seqlen=256)
+    o16 = gpu_attn(g["packed"], g["cu"], w, torch.bfloat16, max_seqlen=256)
+    _check_attn(w, ref, o32, o16, range(w.B))
+    C = w.C
+    q, k, v = wl.split_qkv(wl.rows(w), C)
+    want = oracle.attn_padded(q, k, v, w.keep, w.H, w.d, w.scale)
+    src = g["src"]
+    for out_dtype in (torch.float32, torch.bfloat16):
+        o = sentinel_like((w.B * w.N, C), out_dtype)
+        binding.rag_attn_padded(src[:, :C], src[:, C:2 * C], src[:, 2 * C:], g["keep"], o, H=w.H,
+                                scale=w.scale)
+        torch.cuda.synchronize()
+        got = o.float().cpu().numpy().astype(np.float64)
+        bound = ATOL + (np.abs(want) * 2.0 ** -8 if out_dtype == torch.bfloat16 else 0.0)
+        assert (np.abs(got - want) <= bound).all(), out_dtype
+
+
 def _truncate_keep(keep: np.ndarray, m: int) -> np.ndarray:
     """The first m kept positions of every image (what a max_seqlen of m keeps)."""
     out = np.zeros_like(keep)
