@@ -515,21 +515,16 @@ __device__ __forceinline__ uint32_t v_operand_offset(int r16, int g, int db)
 
 // ---- loads the compiler does not track ------------------------------------
 //
-// The tile kernel's K/V loads into LDS and the gathered layout's speculative
-// loads are inline assembly, waited for with explicit counts: the compiler
-// cannot tell that LDS-writing loads and the LDS words read meanwhile (the
-// current K/V tile, the keep ranking's words) do not overlap, and its own
-// waits would serialise them.  A wave's loads complete in issue order, which
-// the count-based wait for the keep bytes (issued first) relies on.
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// The four words of the raw buffer resource over [base, base + bytes) that
-// make_rsrc builds.
-__device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes)
-{
-    const uint64_t a = (uint64_t)(uintptr_t)base;
-    return i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xFFFFu), (int)bytes, (int)dev::kRsrcWord3};
-}
+// The tile kernel's K/V loads into LDS (dev::ld_lds16_untracked) and the
+// gathered layout's speculative loads are inline assembly, waited for with
+// explicit counts: the compiler cannot tell that LDS-writing loads and the
+// LDS words read meanwhile (the current K/V tile, the keep ranking's words) do
+// not overlap, and its own waits would serialise them.  A wave's loads
+// complete in issue order, which the count-based wait for the keep bytes
+// (issued first) relies on.
+using dev::i32x4;
+using dev::ld_lds16_untracked;
+using dev::rsrc_words;
 
 // One byte at offset off of the resource, zero-extended.  The result register
 // is written when the load completes: read it only after a wait_vm() that
@@ -539,14 +534,6 @@ __device__ __forceinline__ uint32_t ld_u8_untracked(i32x4 r, uint32_t off)
     uint32_t x;
     asm volatile("buffer_load_ubyte %0, %1, %2, 0 offen" : "=v"(x) : "v"(off), "s"(r));
     return x;
-}
-
-// Sixteen bytes per lane at offset voff of the resource into LDS at lds_addr
-// + 16 lane (lds_addr wave-uniform).  The LDS base goes in through M0 as an
-// input operand; the s_nop gives the M0 write the wait state the load needs.
-__device__ __forceinline__ void ld_lds16_untracked(i32x4 r, uint32_t lds_addr, uint32_t voff)
-{
-    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(r), "{m0}"(lds_addr));
 }
 
 // Waits until at most n (wave-uniform, even, >= 0) of this wave's

@@ -28,9 +28,9 @@
 //     each owning 64 x 64 outputs (4 x 4 blocks of v_mfma_f32_16x16x32_bf16,
 //     fp32 accumulators in VGPRs);
 //   * k advances 64 at a time through two LDS buffers: while k-tile kt is
-//     multiplied from one, k-tile kt + 1 (already in registers) is written to
-//     the other and k-tile kt + 2 is requested from memory (eight 16-byte
-//     buffer loads per lane); one barrier per k-tile.  LDS rows are 128 bytes
+//     multiplied from one, k-tile kt + 1 is requested into the other by buffer
+//     loads that write LDS (eight 16-byte loads per lane, no registers and no
+//     LDS store instructions); one wait and one barrier per k-tile.  LDS rows are 128 bytes
 //     (64 bf16) with the eight 16-byte chunks of row r permuted by XOR with
 //     swz(r), so that 16 lanes reading chunk c of 16 consecutive rows hit
 //     distinct banks;
@@ -51,7 +51,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-using dev::kDropOffset;
+using dev::i32x4;
 using dev::ld16;
 using dev::make_rsrc;
 using dev::u32x4;
@@ -127,31 +127,29 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p)
     const uint32_t rowb = (uint32_t)p.K * 2u;  // bytes per operand row
 
     // operand rows of this tile; rows past M (or N) read as zero
-    const auto rx = make_rsrc(p.x + (int64_t)m0 * p.K, (uint32_t)min(kBM, p.M - m0) * rowb);
-    const auto rw = make_rsrc(p.w + (int64_t)n0 * p.K, (uint32_t)min(kBN, p.N - n0) * rowb);
+    const i32x4 rx = dev::rsrc_words(p.x + (int64_t)m0 * p.K, (uint32_t)min(kBM, p.M - m0) * rowb);
+    const i32x4 rw = dev::rsrc_words(p.w + (int64_t)n0 * p.K, (uint32_t)min(kBN, p.N - n0) * rowb);
 
     // Staging: load j (0..7) of thread tid moves LDS bytes [16 (tid + 256 j), +16)
     // of the k-tile: LDS row tid / 8 + 32 j (W rows 0..127 for j < 4, then X
     // rows), slot tid % 8, which holds global chunk slot ^ swz(row) of that row
-    // (swz depends on the row mod 16, the same for every j).
+    // (swz depends on the row mod 16, the same for every j).  The loads write
+    // LDS themselves (no registers, no LDS store instructions): wave w's load j
+    // fills the 1 KiB at 16 (64 w + 256 j), 16 bytes per lane.
     uint32_t goff[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int row = (tid >> 3) + 32 * j;
         goff[j] = (uint32_t)row * rowb + 16u * (uint32_t)((tid & 7) ^ swz(row));
     }
-    u32x4 stage[kLoads];
-    auto fetch = [&](int kt) {
+    const uint32_t lds0 = (uint32_t)(uintptr_t)lds;  // (the low half of a flat LDS pointer)
+    auto request = [&](int kt, int buf) {
         const uint32_t kb = (uint32_t)kt * (kBK * 2);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) stage[j] = ld16(rw, goff[j] + kb);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) stage[4 + j] = ld16(rx, goff[j] + kb);
-    };
-    auto stash = [&](int buf) {
-#pragma unroll
-        for (int j = 0; j < kLoads; ++j)
-            *reinterpret_cast<u32x4*>(lds + buf * kTileBytes + 16 * (tid + kThreads * j)) = stage[j];
+        for (int j = 0; j < kLoads; ++j) {
+            const uint32_t base = lds0 + (uint32_t)(buf * kTileBytes) + 16u * (uint32_t)(64 * wave + kThreads * j);
+            dev::ld_lds16_untracked(j < 4 ? rw : rx, base, goff[j & 3] + kb);
+        }
     };
 
     // wave (wn, wm) owns W rows 64 wn .. and X rows 64 wm .. of the tile
@@ -164,11 +162,13 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p)
         for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int nk = p.K / kBK;
-    fetch(0);
-    stash(0);
-    if (nk > 1) fetch(1);
+    request(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
+        // k-tile kt + 1 goes to the other buffer, last read before the previous
+        // barrier, while tile kt is multiplied
+        if (kt + 1 < nk) request(kt + 1, (kt + 1) & 1);
         const char* st = lds + (kt & 1) * kTileBytes;
         const char* sW = st + 128 * (64 * wn + r16);
         const char* sX = st + kBN * 128 + 128 * (64 * wm + r16);
@@ -186,10 +186,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p)
 #pragma unroll
                 for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = mfma(a[nb], b[mb], acc[nb][mb]);
         }
-        // the other buffer was last read in iteration kt - 1, before its barrier
-        if (kt + 1 < nk) stash((kt + 1) & 1);
-        if (kt + 2 < nk) fetch(kt + 2);
-        __syncthreads();
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // tile kt + 1 has landed
+        __syncthreads();  // ... and every wave is done with tile kt
     }
 
     // ---- epilogue: acc[nb][mb][i] = D[m0 + 64 wm + 16 mb + r16][n0 + 64 wn + 16 nb + 4 g + i].

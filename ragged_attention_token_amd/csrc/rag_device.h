@@ -22,6 +22,28 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
 }
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// The four words of the raw buffer resource over [base, base + bytes) that
+// make_rsrc builds, for loads written in inline assembly.
+__device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes)
+{
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    return i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xFFFFu), (int)bytes, (int)kRsrcWord3};
+}
+
+// Sixteen bytes per lane at offset voff of the resource, written to LDS at
+// lds_addr + 16 lane (lds_addr wave-uniform), by a buffer load that writes LDS
+// (no registers).  The compiler does not track it: it cannot tell that such a
+// load and the LDS words read meanwhile (another buffer) do not overlap, and
+// its own waits would serialise them; every use waits with an explicit
+// s_waitcnt vmcnt.  The LDS base goes in through M0 as an input operand; the
+// s_nop gives the M0 write the wait state the load needs.
+__device__ __forceinline__ void ld_lds16_untracked(i32x4 r, uint32_t lds_addr, uint32_t voff)
+{
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(r), "{m0}"(lds_addr));
+}
+
 __device__ __forceinline__ u32x4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
