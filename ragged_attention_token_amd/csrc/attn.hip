@@ -1188,20 +1188,42 @@ __global__ __launch_bounds__(64 * kMaxWaves) void attn_lds_kernel(AttnParams p)
                 const u32x4 val = *reinterpret_cast<const u32x4*>(so + row * RB + 16 * (ch ^ (row & (NCH - 1))));
                 __builtin_amdgcn_raw_buffer_store_b128(val, ro, row_off(16 * qb + row, osb) + 16u * (uint32_t)ch, 0, 0);
             }
-        } else {
-            const uint32_t orow = row_off(16 * qb + r16, osb);
+        } else if constexpr (!OUT_F32) {
+            // bf16: lane (r16, g) holds columns 16 db + 4g .. + 3 of its row.  One
+            // v_permlane16_swap per register pair exchanges between lanes l and
+            // l ^ 16 (groups g and g ^ 1) so that an even-g lane ends with
+            // columns 16 db + 4g .. + 7 of db = 0 and 2, an odd-g lane those of
+            // db = 1 and 3 (from 16 db + 4 (g - 1)): two 16-byte stores per lane,
+            // each instruction writing 64 contiguous bytes of 16 rows.
+            uint32_t w[4][2];
 #pragma unroll
             for (int db = 0; db < 4; ++db) {
                 const f32x4 r = st.acc[db] * inv;
-                const uint32_t off = orow + (uint32_t)(16 * db + 4 * g) * OES;
-                if constexpr (OUT_F32) {
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, r), ro, off, 0, 0);
-                } else {
-                    bf16x4 o4;
+                bf16x4 o4;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) o4[i] = static_cast<__bf16>(r[i]);
-                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o4), ro, off, 0, 0);
-                }
+                for (int i = 0; i < 4; ++i) o4[i] = static_cast<__bf16>(r[i]);
+                const u32x2 u = __builtin_bit_cast(u32x2, o4);
+                w[db][0] = u[0];
+                w[db][1] = u[1];
+            }
+            u32x4 ch[2];
+#pragma unroll
+            for (int pr = 0; pr < 2; ++pr) {
+                const auto s0 = __builtin_amdgcn_permlane16_swap(w[2 * pr][0], w[2 * pr + 1][0], false, false);
+                const auto s1 = __builtin_amdgcn_permlane16_swap(w[2 * pr][1], w[2 * pr + 1][1], false, false);
+                ch[pr] = u32x4{s0[0], s1[0], s0[1], s1[1]};
+            }
+            const uint32_t orow = row_off(16 * qb + r16, osb);
+            const uint32_t col = 16u * (uint32_t)(g & 1) + 4u * (uint32_t)(g & 2);
+            __builtin_amdgcn_raw_buffer_store_b128(ch[0], ro, orow + col * 2u, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(ch[1], ro, orow + (32u + col) * 2u, 0, 0);
+        } else {
+            const uint32_t orow = row_off(16 * qb + r16, osb);  // fp32: 16 bytes per lane already
+#pragma unroll
+            for (int db = 0; db < 4; ++db) {
+                const f32x4 r = st.acc[db] * inv;
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, r), ro,
+                                                       orow + (uint32_t)(16 * db + 4 * g) * OES, 0, 0);
             }
         }
         if constexpr (!MULTI) break;  // (single-block launches: one block per wave)
