@@ -10,6 +10,9 @@ the input and output dtypes and a max_seqlen bound, then checks on the GPU:
   * rag_attn_gathered bit for bit equal to the packed result at the kept rows;
   * rag_attn_padded within 2e-3 of the oracle on the kept rows;
   * rag_repack with a random second-stage keep mask against oracle.repack.
+A second draw takes more (image, head) pairs (B up to 96, H up to 12) at lengths
+around the LDS-resident limit, so both sides of the attention's few/many-pairs
+switch are exercised.
 max_seqlen is either the longest image (every row attended) or a bound below
 it (images truncated to their first max_seqlen rows, which the oracle is given
 the same way: its input is the truncated batch).
@@ -27,6 +30,7 @@ pytestmark = pytest.mark.gpu
 
 ATOL = 2e-3
 CASES = 24
+MANY_CASES = 8
 
 
 def _draw(seed):
@@ -49,6 +53,29 @@ def _draw(seed):
     return w, out_dtype, bound
 
 
+def _draw_many(seed):
+    """More (image, head) pairs: B 8-96, H 1-12, lengths near the LDS-resident limit of
+    256 rows and the 64-row tile, so that both sides of the few/many-pairs switch (256
+    pairs) and of the per-wave output slots' LDS limit are drawn."""
+    rng = np.random.default_rng(5000 + seed)
+    N = int(rng.choice([16, 63, 64, 127, 128, 129, 192, 197, 255, 256, 257, 320]))
+    B = int(rng.integers(8, 97))
+    H = int(rng.integers(1, 13))
+    kind = rng.integers(0, 3)
+    if kind == 0:
+        lengths = rng.integers(0, N + 1, size=B)
+    elif kind == 1:
+        lengths = np.full(B, N)
+    else:
+        lengths = np.clip(rng.normal(0.5 * N, 0.1 * N, size=B).astype(int), 0, N)
+    dtype = "f32" if rng.random() < 0.2 else "bf16"
+    out_dtype = torch.float32 if rng.random() < 0.5 else torch.bfloat16
+    w = wl.custom(B=B, N=N, H=H, lengths=lengths, dtype=dtype, seed=6000 + seed)
+    mx = int(w.lengths.max()) if w.T else 1
+    bound = mx if rng.random() < 0.8 else max(1, int(rng.integers(1, mx + 1)))
+    return w, out_dtype, bound
+
+
 def _attn(packed, cu, w, out_dtype, bound, tiled=False):
     C = w.C
     o = sentinel_like((packed.shape[0], C), out_dtype)
@@ -62,6 +89,12 @@ def _attn(packed, cu, w, out_dtype, bound, tiled=False):
 def test_random_case(seed):
     w, out_dtype, bound = _draw(seed)
     _check_case(w, out_dtype, bound, seed)
+
+
+@pytest.mark.parametrize("seed", range(MANY_CASES))
+def test_random_case_many_pairs(seed):
+    w, out_dtype, bound = _draw_many(seed)
+    _check_case(w, out_dtype, bound, 10000 + seed)
 
 
 def test_every_image_empty():
