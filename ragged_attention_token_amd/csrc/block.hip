@@ -36,12 +36,35 @@ using rag::dev::u32x4;
 
 constexpr int kLnRowsPerWave = 2;
 
+// Sum over the wave of one value per lane, as a butterfly over lane distances
+// 32, 16, 8, 4, 2, 1: each step adds the value of the lane whose index differs
+// in that bit (own + partner; the adds are commutative, so both lanes of a
+// pair hold the same bits).  Distances 32 and 16 take the gfx950 permlane
+// swaps; 8 is a rotation by 8 within each 16-lane row; 4 is a rotation by 4,
+// which reads lane i^4's value because lanes i and i^8 already agree; 2 and 1
+// are quad permutations.  No LDS round trips.
+__device__ __forceinline__ float wave_sum(float x)
+{
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));  // row_ror:8
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false));  // row_ror:4
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));   // quad 2,3,0,1
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));   // quad 1,0,3,2
+    return x;
+}
+
 // LayerNorm over rows of C bf16 values (C a multiple of 8, at most 2048):
 // y = (x - mean) / sqrt(var + eps) * gamma + beta, mean and (biased) variance
-// in fp32 over the row, y rounded to bf16.  Each wave normalises
-// kLnRowsPerWave rows, 4 waves per workgroup; a lane holds NCH 16-byte chunks
-// of each row (NCH = ceil(C / 512)), and every row's loads are issued before
-// the first reduction.
+// in fp32 over the row (two passes: the mean, then the squared deviations),
+// y rounded to bf16.  Each wave normalises kLnRowsPerWave rows, 4 waves per
+// workgroup; a lane holds NCH 16-byte chunks of each row (NCH = ceil(C / 512)).
+// The wave index is made uniform so that the row addresses are scalar: every
+// row's loads and the lane's gamma and beta are in flight together before the
+// first reduction.  Chunks past the row read zeros, and their stores fall
+// outside the row's buffer resource, which drops them.
 template <int NCH>
 __global__ __launch_bounds__(256) void layernorm_kernel(const __bf16* x, __bf16* y, int rows, int C,
                                                         const float* gamma, const float* beta,
@@ -49,7 +72,8 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const __bf16* x, __bf16*
 {
     constexpr int R = kLnRowsPerWave;
     const int lane = threadIdx.x & 63;
-    const int row0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * R;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int row0 = (blockIdx.x * 4 + wave) * R;
     if (row0 >= rows) return;
     const int nchunk = C / 8;
     float v[R][NCH][8];
@@ -60,11 +84,21 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const __bf16* x, __bf16*
                                             row0 + r < rows ? (uint32_t)C * 2u : 0u);
 #pragma unroll
         for (int j = 0; j < NCH; ++j) {
-            const int ch = lane + 64 * j;
-            const bf16x8 w = __builtin_bit_cast(bf16x8, rag::dev::ld16(rx, 16u * (uint32_t)ch));
+            const bf16x8 w = __builtin_bit_cast(bf16x8, rag::dev::ld16(rx, 16u * (uint32_t)(lane + 64 * j)));
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[r][j][e] = ch < nchunk ? static_cast<float>(w[e]) : 0.f;
+            for (int e = 0; e < 8; ++e) v[r][j][e] = static_cast<float>(w[e]);
         }
+    }
+    const auto rg = rag::dev::make_rsrc(gamma, (uint32_t)C * 4u);
+    const auto rb = rag::dev::make_rsrc(beta, (uint32_t)C * 4u);
+    f32x4 ga[NCH], gb[NCH], ba[NCH], bb[NCH];
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+        const uint32_t off = 32u * (uint32_t)(lane + 64 * j);
+        ga[j] = __builtin_bit_cast(f32x4, rag::dev::ld16(rg, off));
+        gb[j] = __builtin_bit_cast(f32x4, rag::dev::ld16(rg, off + 16u));
+        ba[j] = __builtin_bit_cast(f32x4, rag::dev::ld16(rb, off));
+        bb[j] = __builtin_bit_cast(f32x4, rag::dev::ld16(rb, off + 16u));
     }
     float mean[R], rstd[R];
 #pragma unroll
@@ -74,9 +108,7 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const __bf16* x, __bf16*
         for (int j = 0; j < NCH; ++j)
 #pragma unroll
             for (int e = 0; e < 8; ++e) sum += v[r][j][e];
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
-        mean[r] = sum / (float)C;
+        mean[r] = wave_sum(sum) / (float)C;
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -90,28 +122,21 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const __bf16* x, __bf16*
                 sq += in ? d * d : 0.f;
             }
         }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) sq += __shfl_xor(sq, off);
-        rstd[r] = 1.f / sqrtf(sq / (float)C + eps);
+        rstd[r] = 1.f / sqrtf(wave_sum(sq) / (float)C + eps);
     }
 #pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-        const int ch = lane + 64 * j;
-        if (ch >= nchunk) continue;
-        const auto* g4 = reinterpret_cast<const f32x4*>(gamma + 8 * ch);
-        const auto* b4 = reinterpret_cast<const f32x4*>(beta + 8 * ch);
-        const f32x4 ga = g4[0], gb = g4[1], ba = b4[0], bb = b4[1];
+    for (int r = 0; r < R; ++r) {
+        if (row0 + r >= rows) continue;
+        const auto ry = rag::dev::make_rsrc(y + (int64_t)(row0 + r) * C, (uint32_t)C * 2u);
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            if (row0 + r >= rows) continue;
+        for (int j = 0; j < NCH; ++j) {
             bf16x8 o;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float gm = e < 4 ? ga[e] : gb[e - 4], bt = e < 4 ? ba[e] : bb[e - 4];
+                const float gm = e < 4 ? ga[j][e] : gb[j][e - 4], bt = e < 4 ? ba[j][e] : bb[j][e - 4];
                 o[e] = static_cast<__bf16>((v[r][j][e] - mean[r]) * rstd[r] * gm + bt);
             }
-            const auto ry = rag::dev::make_rsrc(y + (int64_t)(row0 + r) * C, (uint32_t)C * 2u);
-            rag::dev::st16(__builtin_bit_cast(u32x4, o), ry, 16u * (uint32_t)ch);
+            rag::dev::st16(__builtin_bit_cast(u32x4, o), ry, 16u * (uint32_t)(lane + 64 * j));
         }
     }
 }
