@@ -280,6 +280,12 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(PackParams p)
         pf = prefix_begin(p.keep, img_row0);
         L = dev::rank_kept(p.keep + img_row0, n_in, s_pos, s_red);
     }
+    // L and the offset below come out of workgroup reductions through LDS, so
+    // they are equal in every lane, but the compiler cannot tell: read from
+    // lane 0 they are scalars, and the destination's buffer resource built
+    // from them stays in scalar registers (otherwise every row store runs in
+    // a loop over the distinct resources of the wave's lanes).
+    L = __builtin_amdgcn_readfirstlane(L);
     if (L == 0 && sl > 0) return;  // uniform; slice 0 still writes cu
 
     // this slice: vectors [c0, c0 + w) of every row.  Lane tid starts at
@@ -318,7 +324,7 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(PackParams p)
     u32x4 x[kPackUnroll];
     load_batch(r, col, x);
 
-    const int offset = prefix_count(pf, p.keep, img_row0, s_red);
+    const int offset = __builtin_amdgcn_readfirstlane(prefix_count(pf, p.keep, img_row0, s_red));
     if (sl == 0) {
         if (tid == 0) {
             p.cu[b + 1] = offset + L;
