@@ -338,21 +338,38 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(PackParams p)
     if (L == 0) return;
     const auto rd = make_rsrc(p.packed + (int64_t)offset * p.packed_stride, (uint32_t)L * pstride);
     const int total = L * w;
-    for (int vb = 0;; vb += kPackUnroll * kThreads) {  // vb: the batch's first vector (uniform)
-        const bool more = vb + kPackUnroll * kThreads < total;
+    // A step requests the next batch into `nxt` and then stores the batch in
+    // `cur`, with no branch between the two, so the compiler's waits before
+    // the stores cover only `cur`'s loads.  The two register sets alternate
+    // between steps (no copy of one into the other), and the last batch is
+    // stored on its own.
+    constexpr int kB = kPackUnroll * kThreads;
+    auto store = [&](const u32x4 (&cur)[kPackUnroll]) {
+#pragma unroll
+        for (int j = 0; j < kPackUnroll; ++j) {
+            st16(cur[j], rd, r < L ? (uint32_t)r * pstride + 16u * (uint32_t)(c0 + col) : kDropOffset);
+            advance(r, col);
+        }
+    };
+    auto step = [&](const u32x4 (&cur)[kPackUnroll], u32x4 (&nxt)[kPackUnroll]) {
         int rn = r, cn = col;
 #pragma unroll
         for (int j = 0; j < kPackUnroll; ++j) advance(rn, cn);  // next batch's cursor
-        u32x4 y[kPackUnroll];
-        if (more) load_batch(rn, cn, y);
-#pragma unroll
-        for (int j = 0; j < kPackUnroll; ++j) {
-            st16(x[j], rd, r < L ? (uint32_t)r * pstride + 16u * (uint32_t)(c0 + col) : kDropOffset);
-            advance(r, col);
+        load_batch(rn, cn, nxt);
+        store(cur);
+    };
+    u32x4 y[kPackUnroll];
+    for (int vb = 0;; vb += 2 * kB) {  // vb: the first vector of the batch in x (uniform)
+        if (vb + kB >= total) {
+            store(x);
+            break;
         }
-        if (!more) break;
-#pragma unroll
-        for (int j = 0; j < kPackUnroll; ++j) x[j] = y[j];
+        step(x, y);
+        if (vb + 2 * kB >= total) {
+            store(y);
+            break;
+        }
+        step(y, x);
     }
 }
 
