@@ -645,7 +645,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
     if (qlo >= qhi) return;
     const int qrow = 16 * qlo;  // first query row of the workgroup
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loops and addresses
     const int r16 = lane & 15, g = lane >> 4;
     const bool wave_active = qlo + wave < qhi;
     const int64_t hoff = (int64_t)h * kD;
@@ -920,7 +921,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void attn_lds_kernel(AttnParams p)
     int h = blockIdx.x, b = blockIdx.y;
     const int qs = blockIdx.z;
     const int nw = blockDim.x >> 6;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loops and addresses
     const int r16 = lane & 15, g = lane >> 4;
 
     // LDS: K rows [0, R), V rows [0, R), then the gathered layout's kept
