@@ -435,12 +435,13 @@ __device__ __forceinline__ bool workgroup_item(const AttnParams& p, Item& it)
         }
     }
     __syncthreads();
-    it.b = s_item[0];
-    it.h = s_item[1];
-    it.q0 = s_item[2];
-    it.q1 = s_item[3];
-    it.L = s_item[4];
-    it.row0 = s_item[5];
+    // equal in every lane; read from lane 0 they are scalars for the compiler
+    it.b = __builtin_amdgcn_readfirstlane(s_item[0]);
+    it.h = __builtin_amdgcn_readfirstlane(s_item[1]);
+    it.q0 = __builtin_amdgcn_readfirstlane(s_item[2]);
+    it.q1 = __builtin_amdgcn_readfirstlane(s_item[3]);
+    it.L = __builtin_amdgcn_readfirstlane(s_item[4]);
+    it.row0 = __builtin_amdgcn_readfirstlane(s_item[5]);
     return it.b >= 0;
 }
 
@@ -630,7 +631,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p)
         row0 = (int64_t)b * p.N;
         L = p.N <= 4 * kThreads ? dev::rank_kept_planes<4>(p.keep + row0, p.N, s_pos, s_wsum, 4)
                                 : dev::rank_kept(p.keep + row0, p.N, s_pos, s_wsum);
-        L = min(L, p.max_len);
+        L = min(__builtin_amdgcn_readfirstlane(L), p.max_len);  // (a workgroup reduction: uniform)
         if (p.zero_dropped && qt == 0) zero_dropped_head<OUT_F32>(p, row0, h);
     } else {
         const int s = min(max(p.cu[b], 0), p.total_rows);
@@ -1008,6 +1009,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void attn_lds_kernel(AttnParams p)
             __syncthreads();
             natural = true;
             for (int w = 0; w < nw; ++w) natural = natural && s_wsum[w] == 0;
+            natural = __builtin_amdgcn_readfirstlane((int)natural) != 0;  // uniform (read from LDS)
             if (!natural) {
                 __syncthreads();  // every wave has read s_wsum before the ranking rewrites it
                 L = dev::rank_kept_planes_loaded<4>(kb, s_pos, s_wsum, nw);
@@ -1018,7 +1020,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void attn_lds_kernel(AttnParams p)
             L = p.N <= 4 * 64 * nw ? dev::rank_kept_planes<4>(p.keep + row0, p.N, s_pos, s_wsum, nw)
                                    : dev::rank_kept_waves(p.keep + row0, p.N, s_pos, s_wsum, nw);
         }
-        L = min(L, p.max_len);
+        L = min(__builtin_amdgcn_readfirstlane(L), p.max_len);  // (a workgroup reduction: uniform)
         if (p.zero_dropped && qs == 0) zero_dropped_head<OUT_F32>(p, row0, h);
     } else {
         const int s = min(max(p.cu[b], 0), p.total_rows);

@@ -122,7 +122,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p)
     if (t >= p.tiles) return;  // uniform over the workgroup
     const int tm = t / p.tiles_n;
     const int m0 = tm * kBM, n0 = (t - tm * p.tiles_n) * kBN;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar LDS bases and branches
     const int r16 = lane & 15, g = lane >> 4;
     const uint32_t rowb = (uint32_t)p.K * 2u;  // bytes per operand row
 
