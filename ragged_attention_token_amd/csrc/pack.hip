@@ -43,7 +43,7 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kUnroll = 4;                           // unpack: 16-byte vectors per lane per batch
 constexpr int kBatch = kThreads * kUnroll;           // vectors per workgroup per batch
-constexpr int kPackUnroll = 8;                       // pack: 16-byte vectors per lane per batch
+constexpr int kPackUnroll = 4;                       // pack: 16-byte vectors per lane per batch
 constexpr int kPrefixLoads = 8;                      // keep-mask words per lane per round
 constexpr int kPackTargetGroups = 768;               // workgroups a pack launch aims for
 using dev::kDropOffset;
